@@ -1,0 +1,102 @@
+/*
+ * bonsai.h -- C ABI of the binary / ternary g128 weight-only matmul library (libbonsai.so).
+ *
+ * The method ("1-bit Bonsai 27B" model card, section "Weight representation: Binary g128"):
+ * every weight is a single sign bit, 0 standing for -scale and 1 for +scale, and each run of
+ * 128 consecutive weights along K shares one FP16 scale.  The model card's CUDA quick-start
+ * and its highlights describe the matmul running straight on the packed signs, unpacking them
+ * inside the kernel and applying the group scales there, with no dense FP16 weight copy.  The
+ * ternary companion ("Ternary Bonsai 27B" article, ternary-format and limitations sections)
+ * uses {-1, 0, +1} x the same FP16 group scale, stored today in 2 bits per weight.
+ *
+ * LAYOUT (normative; the pages fix no bit order, this is the library's reading)
+ *   Binary  wbits  : uint32 [N][K/32], row-major.  The sign of W[n][k] is bit (k % 32) of
+ *                    wbits[n][k / 32]; bit = 1 -> +s, bit = 0 -> -s.  In little-endian memory
+ *                    byte b of a row holds k = 8b .. 8b+7, least significant bit first.
+ *   Ternary wcodes : uint32 [N][K/16], row-major.  W[n][k] is the 2-bit field of
+ *                    wcodes[n][k / 16] whose low bit is bit 2*(k % 16); field value
+ *                    0 -> 0, 1 -> +1, 3 -> -1; the value 2 is reserved (never produced by the
+ *                    packer, rejected by the unpacker; GPU results on it are unspecified).
+ *   Scales         : IEEE binary16 bit patterns, uint16 [N][K/128], row-major;
+ *                    W[n][k] uses scales[n][k / 128].  Any value is taken literally.
+ *   x              : IEEE binary16, [M][K] row-major.      y : float32, [M][N] row-major.
+ *   Every entry point computes  y[m][n] = sum_k W[n][k] * x[m][k]  (y = x W^T),
+ *   accumulating in float32.  K must be a multiple of 128.
+ *
+ * CONVENTIONS
+ *   Ownership : the caller allocates and owns every buffer; for the GPU entry points they are
+ *               device memory.  The library allocates nothing, frees nothing and never
+ *               synchronises in these calls; it keeps no state between calls.
+ *   Streams   : GPU work is enqueued on `hip_stream` (a hipStream_t; NULL = default stream).
+ *               BONSAI_OK means "validated and enqueued"; faults during execution surface at
+ *               the caller's next synchronisation.
+ *   Errors    : arguments are checked on the host before anything is enqueued; on any error
+ *               nothing is enqueued and the status says why.  No C++ exception crosses the ABI.
+ *   Aliasing  : y must not overlap the inputs.  Device pointers must be 16-byte aligned.
+ *   Empty     : M == 0 or N == 0 is a no-op (BONSAI_OK).  K == 0 writes y = 0.
+ *   Threads   : every entry point is reentrant and thread-safe.
+ *   Results   : float32 sums in a kernel-defined order; they match the exact product within
+ *               1e-3 * sum_k |W[n][k] x[m][k]| + 1e-6, are bitwise reproducible run to run for
+ *               a given shape, and are exact whenever every partial sum is exactly
+ *               representable in float32 (e.g. small integer x and power-of-two scales).
+ */
+#ifndef BONSAI_H
+#define BONSAI_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    BONSAI_OK = 0,
+    BONSAI_ERR_NULL = 1,    /* a required pointer is NULL                                   */
+    BONSAI_ERR_SHAPE = 2,   /* M, N or K negative or out of range, or K % 128 != 0           */
+    BONSAI_ERR_ALIGN = 3,   /* a device pointer is not 16-byte aligned                       */
+    BONSAI_ERR_VALUE = 4,   /* pack input outside {-1,+1} (binary) or {-1,0,+1} (ternary)    */
+    BONSAI_ERR_CODE = 5,    /* unpack met the reserved ternary field value 2                 */
+    BONSAI_ERR_DEVICE = 6   /* the HIP runtime refused the launch                            */
+} bonsai_status;
+
+/* Largest K the GPU entry points accept (a multiple of 128). */
+#define BONSAI_MAX_K 131072
+/* Largest M of the GEMV entry points (M and N of every GPU entry point are at most 2^30). */
+#define BONSAI_GEMV_MAX_M 8
+
+/* Binary decode GEMV: y[M][N] = x[M][K] * W^T for 1 <= M <= 8 (M == 0: no-op).
+ * The bandwidth-bound decode step (model card, cross-platform throughput: tg128 is the
+ * memory-bound phase).  wbits, scales, x, y: device pointers laid out as above. */
+bonsai_status bonsai_q1_gemv(const uint32_t *wbits, const uint16_t *scales, const uint16_t *x,
+                             float *y, int64_t M, int64_t N, int64_t K, void *hip_stream);
+
+/* Binary prefill GEMM: y[M][N] = x[M][K] * W^T for any M >= 0 (tuned for M = 512, the pp512
+ * prompt length of the model card's throughput table, its compute-bound phase). */
+bonsai_status bonsai_q1_gemm(const uint32_t *wbits, const uint16_t *scales, const uint16_t *x,
+                             float *y, int64_t M, int64_t N, int64_t K, void *hip_stream);
+
+/* Ternary decode GEMV on 2-bit codes: y[M][N] = x[M][K] * W^T for 1 <= M <= 8. */
+bonsai_status bonsai_q2t_gemv(const uint32_t *wcodes, const uint16_t *scales, const uint16_t *x,
+                              float *y, int64_t M, int64_t N, int64_t K, void *hip_stream);
+
+/* Host-side executable layout spec: pure functions on host memory, no device, no allocation.
+ * signs/trits are int8 [N][K] row-major; K must be a multiple of 32 (binary) or 16 (ternary).
+ * pack rejects values outside the alphabet with BONSAI_ERR_VALUE (output then unspecified);
+ * unpack of ternary rejects field value 2 with BONSAI_ERR_CODE. */
+bonsai_status bonsai_q1_pack(const int8_t *signs, int64_t N, int64_t K, uint32_t *wbits);
+bonsai_status bonsai_q1_unpack(const uint32_t *wbits, int64_t N, int64_t K, int8_t *signs);
+bonsai_status bonsai_q2t_pack(const int8_t *trits, int64_t N, int64_t K, uint32_t *wcodes);
+bonsai_status bonsai_q2t_unpack(const uint32_t *wcodes, int64_t N, int64_t K, int8_t *trits);
+
+/* Name of the HIP runtime error behind the most recent BONSAI_ERR_DEVICE returned on the
+ * calling thread ("none" if there was none).  Static string; never NULL. */
+const char *bonsai_last_device_error(void);
+
+/* Static, NUL-terminated description of a status value. */
+const char *bonsai_status_str(bonsai_status s);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* BONSAI_H */

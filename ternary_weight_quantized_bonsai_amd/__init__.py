@@ -1,0 +1,164 @@
+"""Python binding of libbonsai (binary / ternary g128 weight-only matmul on MI355X).
+
+Argument marshalling only: every step of the computation runs in the gfx950 kernels of
+``_lib/libbonsai.so``, reached through its C ABI (``include/bonsai.h``).  PyTorch supplies
+device memory and the current HIP stream; nothing here computes a result on the host.
+If the shared library has not been built, importing this package raises ImportError.
+"""
+from __future__ import annotations
+
+import ctypes
+from pathlib import Path
+
+import numpy as np
+
+_PKG = Path(__file__).resolve().parent
+LIB_PATH = _PKG / "_lib" / "libbonsai.so"
+
+OK, ERR_NULL, ERR_SHAPE, ERR_ALIGN, ERR_VALUE, ERR_CODE, ERR_DEVICE = range(7)
+MAX_K = 131072
+GEMV_MAX_M = 8
+
+# PyTorch ships its own HIP runtime, loaded under the name libamdhip64.so.  Importing torch
+# first makes libbonsai's libamdhip64.so.7 dependency resolve to that same runtime (same
+# SONAME), so the process holds one HIP runtime and torch's streams and memory are valid here.
+import torch  # noqa: E402,F401
+
+if not LIB_PATH.exists():
+    raise ImportError(f"{LIB_PATH} is missing: build it with "
+                      "`python -c 'import __graft_entry__ as g; g.build()'` (hipcc, gfx950)")
+
+_lib = ctypes.CDLL(str(LIB_PATH))
+_c_i64 = ctypes.c_int64
+_vp = ctypes.c_void_p
+for _name in ("bonsai_q1_gemv", "bonsai_q1_gemm", "bonsai_q2t_gemv"):
+    _f = getattr(_lib, _name)
+    _f.argtypes = [_vp, _vp, _vp, _vp, _c_i64, _c_i64, _c_i64, _vp]
+    _f.restype = ctypes.c_int
+for _name in ("bonsai_q1_pack", "bonsai_q1_unpack", "bonsai_q2t_pack", "bonsai_q2t_unpack"):
+    _f = getattr(_lib, _name)
+    _f.argtypes = [_vp, _c_i64, _c_i64, _vp]
+    _f.restype = ctypes.c_int
+_lib.bonsai_last_device_error.argtypes = []
+_lib.bonsai_last_device_error.restype = ctypes.c_char_p
+_lib.bonsai_status_str.argtypes = [ctypes.c_int]
+_lib.bonsai_status_str.restype = ctypes.c_char_p
+
+
+class BonsaiError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        detail = f" [{_lib.bonsai_last_device_error().decode()}]" if status == ERR_DEVICE else ""
+        super().__init__(f"{fn}: {status_str(status)} (status {status}){detail}")
+        self.status = status
+
+
+def status_str(status: int) -> str:
+    return _lib.bonsai_status_str(int(status)).decode()
+
+
+def raw():
+    """The ctypes handle of libbonsai.so (argtypes set), for callers passing raw pointers."""
+    return _lib
+
+
+def _check(fn: str, status: int):
+    if status != OK:
+        raise BonsaiError(fn, status)
+
+
+# ---------------------------------------------------------------------------------------
+# GPU entry points (torch tensors in device memory)
+# ---------------------------------------------------------------------------------------
+def _dev_args(words, scales, x, out, n_word_div: int):
+    import torch
+
+    for name, t, ok in (("words", words, (torch.int32, torch.uint32)),
+                        ("scales", scales, (torch.float16, torch.int16, torch.uint16)),
+                        ("x", x, (torch.float16, torch.int16, torch.uint16))):
+        if t.dtype not in ok:
+            raise TypeError(f"{name}: dtype {t.dtype} not in {ok}")
+        if not t.is_cuda or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous device tensor")
+    if words.dim() != 2 or scales.dim() != 2 or x.dim() != 2:
+        raise ValueError("words [N, K/w], scales [N, K/128] and x [M, K] must be 2-D")
+    M, K = x.shape
+    N = words.shape[0]
+    if words.shape[1] * n_word_div != K or tuple(scales.shape) != (N, K // 128):
+        raise ValueError(f"inconsistent shapes words {tuple(words.shape)}, scales "
+                         f"{tuple(scales.shape)}, x {tuple(x.shape)}")
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.float32, device=x.device)
+    elif out.dtype != torch.float32 or tuple(out.shape) != (M, N) or not out.is_contiguous():
+        raise ValueError("out must be a contiguous float32 [M, N] tensor")
+    stream = torch.cuda.current_stream(x.device).cuda_stream
+    return M, N, K, out, stream
+
+
+def _call(fn: str, words, scales, x, out, div):
+    M, N, K, out, stream = _dev_args(words, scales, x, out, div)
+    _check(fn, getattr(_lib, fn)(words.data_ptr(), scales.data_ptr(), x.data_ptr(), out.data_ptr(),
+                                 M, N, K, stream))
+    return out
+
+
+def q1_gemv(wbits, scales, x, out=None):
+    """y[M, N] = x[M, K] W^T for binary g128 weights, 1 <= M <= 8 (bonsai_q1_gemv)."""
+    return _call("bonsai_q1_gemv", wbits, scales, x, out, 32)
+
+
+def q1_gemm(wbits, scales, x, out=None):
+    """y[M, N] = x[M, K] W^T for binary g128 weights, any M (bonsai_q1_gemm)."""
+    return _call("bonsai_q1_gemm", wbits, scales, x, out, 32)
+
+
+def q2t_gemv(wcodes, scales, x, out=None):
+    """y[M, N] = x[M, K] W^T for ternary g128 weights on 2-bit codes, 1 <= M <= 8."""
+    return _call("bonsai_q2t_gemv", wcodes, scales, x, out, 16)
+
+
+# ---------------------------------------------------------------------------------------
+# Host layout functions (numpy arrays in host memory)
+# ---------------------------------------------------------------------------------------
+def _host(a, dtype):
+    a = np.ascontiguousarray(a)
+    if a.dtype != dtype:
+        raise TypeError(f"expected {np.dtype(dtype)}, got {a.dtype}")
+    return a
+
+
+def q1_pack(signs: np.ndarray) -> np.ndarray:
+    """int8 signs [N, K] in {-1, +1} -> uint32 words [N, K/32] (bonsai_q1_pack)."""
+    s = _host(signs, np.int8)
+    N, K = s.shape
+    out = np.empty((N, K // 32 if K % 32 == 0 else 0), dtype=np.uint32)
+    _check("bonsai_q1_pack", _lib.bonsai_q1_pack(s.ctypes.data, N, K, out.ctypes.data))
+    return out
+
+
+def q1_unpack(wbits: np.ndarray, K: int) -> np.ndarray:
+    w = _host(wbits, np.uint32)
+    N = w.shape[0]
+    out = np.empty((N, K), dtype=np.int8)
+    if w.shape[1] * 32 != K:
+        raise ValueError("wbits must be [N, K/32]")
+    _check("bonsai_q1_unpack", _lib.bonsai_q1_unpack(w.ctypes.data, N, K, out.ctypes.data))
+    return out
+
+
+def q2t_pack(trits: np.ndarray) -> np.ndarray:
+    """int8 trits [N, K] in {-1, 0, +1} -> uint32 words [N, K/16] (bonsai_q2t_pack)."""
+    t = _host(trits, np.int8)
+    N, K = t.shape
+    out = np.empty((N, K // 16 if K % 16 == 0 else 0), dtype=np.uint32)
+    _check("bonsai_q2t_pack", _lib.bonsai_q2t_pack(t.ctypes.data, N, K, out.ctypes.data))
+    return out
+
+
+def q2t_unpack(wcodes: np.ndarray, K: int) -> np.ndarray:
+    w = _host(wcodes, np.uint32)
+    N = w.shape[0]
+    out = np.empty((N, K), dtype=np.int8)
+    if w.shape[1] * 16 != K:
+        raise ValueError("wcodes must be [N, K/16]")
+    _check("bonsai_q2t_unpack", _lib.bonsai_q2t_unpack(w.ctypes.data, N, K, out.ctypes.data))
+    return out

@@ -1,0 +1,168 @@
+// capi.hip -- the C ABI of libbonsai: host-side validation, launches, and the host
+// pack/unpack functions that make the storage layout executable.  Declarations and the
+// normative layout are in include/bonsai.h.
+#include <limits.h>
+
+#include "../../include/bonsai.h"
+#include "launch.h"
+
+namespace bonsai {
+namespace {
+
+__global__ void fill_zero_kernel(float *y, int64_t count)
+{
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < count; i += stride) y[i] = 0.f;
+}
+
+thread_local const char *g_last_device_error = "none";
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Shared argument checks of the GPU entry points.  max_m < 0: no upper bound on M.
+bonsai_status check_gpu_args(const void *w, const void *s, const void *x, const float *y,
+                             int64_t M, int64_t N, int64_t K, int64_t max_m)
+{
+    if (M < 0 || N < 0 || K < 0 || (max_m >= 0 && M > max_m)) return BONSAI_ERR_SHAPE;
+    if (K % 128 != 0 || K > BONSAI_MAX_K || N > (1 << 30) || M > (1 << 30)) return BONSAI_ERR_SHAPE;
+    if (M == 0 || N == 0) return BONSAI_OK;
+    if (!y) return BONSAI_ERR_NULL;
+    if (K == 0) return aligned16(y) ? BONSAI_OK : BONSAI_ERR_ALIGN;
+    if (!w || !s || !x) return BONSAI_ERR_NULL;
+    if (!aligned16(w) || !aligned16(s) || !aligned16(x) || !aligned16(y)) return BONSAI_ERR_ALIGN;
+    return BONSAI_OK;
+}
+
+template <typename Launch>
+bonsai_status run(const void *w, const void *s, const void *x, float *y, int64_t M, int64_t N,
+                  int64_t K, int64_t max_m, void *stream, Launch launch)
+{
+    const bonsai_status st = check_gpu_args(w, s, x, y, M, N, K, max_m);
+    if (st != BONSAI_OK || M == 0 || N == 0) return st;
+    hipStream_t hs = static_cast<hipStream_t>(stream);
+    const hipError_t e = K == 0 ? launch_fill_zero(y, M * N, hs)
+                                : launch((int)M, (int)N, (int)K, hs);
+    if (e == hipSuccess) return BONSAI_OK;
+    g_last_device_error = hipGetErrorName(e);
+    return BONSAI_ERR_DEVICE;
+}
+
+}  // namespace
+
+hipError_t launch_fill_zero(float *y, int64_t count, hipStream_t stream)
+{
+    const int64_t blocks = (count + 255) / 256;
+    void *args[] = {&y, &count};
+    return hipLaunchKernel(reinterpret_cast<const void *>(&fill_zero_kernel),
+                           dim3((unsigned)(blocks < 4096 ? blocks : 4096)), dim3(256), args, 0, stream);
+}
+
+}  // namespace bonsai
+
+using namespace bonsai;
+
+extern "C" {
+
+bonsai_status bonsai_q1_gemv(const uint32_t *wbits, const uint16_t *scales, const uint16_t *x,
+                             float *y, int64_t M, int64_t N, int64_t K, void *hip_stream)
+{
+    return run(wbits, scales, x, y, M, N, K, BONSAI_GEMV_MAX_M, hip_stream,
+               [&](int m, int n, int k, hipStream_t st) { return launch_q1_gemv(wbits, scales, x, y, m, n, k, st); });
+}
+
+bonsai_status bonsai_q1_gemm(const uint32_t *wbits, const uint16_t *scales, const uint16_t *x,
+                             float *y, int64_t M, int64_t N, int64_t K, void *hip_stream)
+{
+    return run(wbits, scales, x, y, M, N, K, -1, hip_stream,
+               [&](int m, int n, int k, hipStream_t st) { return launch_q1_gemm(wbits, scales, x, y, m, n, k, st); });
+}
+
+bonsai_status bonsai_q2t_gemv(const uint32_t *wcodes, const uint16_t *scales, const uint16_t *x,
+                              float *y, int64_t M, int64_t N, int64_t K, void *hip_stream)
+{
+    return run(wcodes, scales, x, y, M, N, K, BONSAI_GEMV_MAX_M, hip_stream,
+               [&](int m, int n, int k, hipStream_t st) { return launch_q2t_gemv(wcodes, scales, x, y, m, n, k, st); });
+}
+
+bonsai_status bonsai_q1_pack(const int8_t *signs, int64_t N, int64_t K, uint32_t *wbits)
+{
+    if (N < 0 || K < 0 || K % 32 != 0) return BONSAI_ERR_SHAPE;
+    if (N == 0 || K == 0) return BONSAI_OK;
+    if (!signs || !wbits) return BONSAI_ERR_NULL;
+    for (int64_t n = 0; n < N; ++n)
+        for (int64_t w = 0; w < K / 32; ++w) {
+            uint32_t word = 0;
+            for (int j = 0; j < 32; ++j) {
+                const int8_t v = signs[n * K + 32 * w + j];
+                if (v != 1 && v != -1) return BONSAI_ERR_VALUE;
+                word |= (uint32_t)(v > 0) << j;
+            }
+            wbits[n * (K / 32) + w] = word;
+        }
+    return BONSAI_OK;
+}
+
+bonsai_status bonsai_q1_unpack(const uint32_t *wbits, int64_t N, int64_t K, int8_t *signs)
+{
+    if (N < 0 || K < 0 || K % 32 != 0) return BONSAI_ERR_SHAPE;
+    if (N == 0 || K == 0) return BONSAI_OK;
+    if (!signs || !wbits) return BONSAI_ERR_NULL;
+    for (int64_t n = 0; n < N; ++n)
+        for (int64_t k = 0; k < K; ++k)
+            signs[n * K + k] = ((wbits[n * (K / 32) + k / 32] >> (k % 32)) & 1u) ? 1 : -1;
+    return BONSAI_OK;
+}
+
+bonsai_status bonsai_q2t_pack(const int8_t *trits, int64_t N, int64_t K, uint32_t *wcodes)
+{
+    if (N < 0 || K < 0 || K % 16 != 0) return BONSAI_ERR_SHAPE;
+    if (N == 0 || K == 0) return BONSAI_OK;
+    if (!trits || !wcodes) return BONSAI_ERR_NULL;
+    for (int64_t n = 0; n < N; ++n)
+        for (int64_t w = 0; w < K / 16; ++w) {
+            uint32_t word = 0;
+            for (int j = 0; j < 16; ++j) {
+                const int8_t v = trits[n * K + 16 * w + j];
+                uint32_t code;
+                if (v == 0) code = 0u;
+                else if (v == 1) code = 1u;
+                else if (v == -1) code = 3u;
+                else return BONSAI_ERR_VALUE;
+                word |= code << (2 * j);
+            }
+            wcodes[n * (K / 16) + w] = word;
+        }
+    return BONSAI_OK;
+}
+
+bonsai_status bonsai_q2t_unpack(const uint32_t *wcodes, int64_t N, int64_t K, int8_t *trits)
+{
+    if (N < 0 || K < 0 || K % 16 != 0) return BONSAI_ERR_SHAPE;
+    if (N == 0 || K == 0) return BONSAI_OK;
+    if (!trits || !wcodes) return BONSAI_ERR_NULL;
+    for (int64_t n = 0; n < N; ++n)
+        for (int64_t k = 0; k < K; ++k) {
+            const uint32_t code = (wcodes[n * (K / 16) + k / 16] >> (2 * (k % 16))) & 3u;
+            if (code == 2u) return BONSAI_ERR_CODE;
+            trits[n * K + k] = code == 0u ? 0 : (code == 1u ? 1 : -1);
+        }
+    return BONSAI_OK;
+}
+
+const char *bonsai_last_device_error(void) { return g_last_device_error; }
+
+const char *bonsai_status_str(bonsai_status s)
+{
+    switch (s) {
+    case BONSAI_OK: return "ok";
+    case BONSAI_ERR_NULL: return "a required pointer is NULL";
+    case BONSAI_ERR_SHAPE: return "M, N or K out of range, or K not a multiple of 128";
+    case BONSAI_ERR_ALIGN: return "a device pointer is not 16-byte aligned";
+    case BONSAI_ERR_VALUE: return "pack input outside the weight alphabet";
+    case BONSAI_ERR_CODE: return "reserved ternary code 0b10";
+    case BONSAI_ERR_DEVICE: return "HIP launch failed";
+    }
+    return "unknown status";
+}
+
+}  // extern "C"

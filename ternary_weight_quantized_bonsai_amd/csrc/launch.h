@@ -1,0 +1,17 @@
+// launch.h -- host-side launchers of the gfx950 kernels (arguments already validated).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace bonsai {
+
+hipError_t launch_q1_gemv(const uint32_t *wbits, const uint16_t *scales, const uint16_t *x, float *y,
+                          int M, int N, int K, hipStream_t stream);
+hipError_t launch_q2t_gemv(const uint32_t *wcodes, const uint16_t *scales, const uint16_t *x, float *y,
+                           int M, int N, int K, hipStream_t stream);
+hipError_t launch_q1_gemm(const uint32_t *wbits, const uint16_t *scales, const uint16_t *x, float *y,
+                          int M, int N, int K, hipStream_t stream);
+hipError_t launch_fill_zero(float *y, int64_t count, hipStream_t stream);
+
+}  // namespace bonsai

@@ -1,0 +1,147 @@
+"""The C ABI on the host: exported symbols, the executable layout spec (pack/unpack) and
+argument validation.  None of these touch a GPU: validation returns before any launch."""
+import ctypes
+import re
+from pathlib import Path
+
+import numpy as np
+import pytest
+
+ROOT = Path(__file__).resolve().parents[1]
+bonsai = pytest.importorskip("ternary_weight_quantized_bonsai_amd")
+
+
+def declared_functions():
+    text = (ROOT / "include" / "bonsai.h").read_text()
+    return sorted(set(re.findall(r"^\s*(?:bonsai_status|const char \*)\s*(bonsai_\w+)\s*\(", text, re.M)))
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for want in ("bonsai_q1_gemv", "bonsai_q1_gemm", "bonsai_q2t_gemv", "bonsai_q1_pack",
+                 "bonsai_q1_unpack", "bonsai_q2t_pack", "bonsai_q2t_unpack", "bonsai_status_str",
+                 "bonsai_last_device_error"):
+        assert want in names
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ctypes.CDLL(str(bonsai.LIB_PATH))
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_status_strings():
+    for s in range(7):
+        assert bonsai.status_str(s)
+    assert bonsai.status_str(99) == "unknown status"
+
+
+# ---- layout spec -----------------------------------------------------------------------
+def test_q1_pack_unpack_roundtrip_random():
+    rng = np.random.default_rng(0)
+    signs = np.where(rng.random((37, 1024)) < 0.5, 1, -1).astype(np.int8)
+    words = bonsai.q1_pack(signs)
+    assert words.shape == (37, 32) and words.nbytes == 37 * 1024 // 8
+    assert np.array_equal(bonsai.q1_unpack(words, 1024), signs)
+    # pack . unpack is the identity on arbitrary words (binary storage is a bijection)
+    w = rng.integers(0, 1 << 32, (5, 64), dtype=np.uint64).astype(np.uint32)
+    assert np.array_equal(bonsai.q1_pack(bonsai.q1_unpack(w, 2048)), w)
+
+
+def test_q1_pack_matches_little_endian_bit_order():
+    # bit j of word w <-> k = 32 w + j, i.e. numpy's little-endian bit order over the bytes
+    rng = np.random.default_rng(1)
+    signs = np.where(rng.random((3, 256)) < 0.5, 1, -1).astype(np.int8)
+    words = bonsai.q1_pack(signs)
+    bits = np.unpackbits(words.view(np.uint8), axis=1, bitorder="little")
+    assert np.array_equal(bits.astype(np.int8) * 2 - 1, signs)
+
+
+def test_q1_pack_exhaustive_halfword_patterns():
+    pats = np.arange(1 << 16, dtype=np.uint32)
+    words = np.stack([pats, pats << 16], axis=1).reshape(-1, 1)     # low half, then high half
+    signs = bonsai.q1_unpack(words, 32)
+    assert np.array_equal(bonsai.q1_pack(signs), words)
+    j = np.arange(16)
+    want_low = np.where((pats[:, None] >> j) & 1, 1, -1)
+    assert np.array_equal(signs[0::2, :16], want_low)
+    assert np.all(signs[0::2, 16:] == -1)
+    assert np.array_equal(signs[1::2, 16:], want_low)
+
+
+def test_q2t_pack_unpack_roundtrip_and_codes():
+    rng = np.random.default_rng(2)
+    trits = rng.choice(np.array([-1, 0, 1], dtype=np.int8), size=(29, 512), p=[0.3, 0.4, 0.3])
+    words = bonsai.q2t_pack(trits)
+    assert words.shape == (29, 32) and words.nbytes == 29 * 512 // 4
+    assert np.array_equal(bonsai.q2t_unpack(words, 512), trits)
+    fields = (words[..., None] >> (2 * np.arange(16, dtype=np.uint32))) & 3
+    assert np.array_equal(fields.reshape(29, 512), np.choose(trits + 1, [3, 0, 1]))
+
+
+def test_q2t_exhaustive_halfword_patterns_without_reserved_code():
+    pats = np.arange(1 << 16, dtype=np.uint32)
+    f = (pats[:, None] >> (2 * np.arange(8, dtype=np.uint32))) & 3
+    valid = pats[~(f == 2).any(axis=1)]
+    assert valid.size == 3 ** 8
+    words = np.stack([valid, valid << 16], axis=1).reshape(-1, 1)
+    trits = bonsai.q2t_unpack(words, 16)
+    assert np.array_equal(bonsai.q2t_pack(trits), words)
+
+
+def test_q2t_unpack_rejects_reserved_code():
+    w = np.zeros((1, 4), np.uint32)
+    w[0, 2] = 0b10 << 10
+    with pytest.raises(bonsai.BonsaiError) as e:
+        bonsai.q2t_unpack(w, 64)
+    assert e.value.status == bonsai.ERR_CODE
+
+
+def test_pack_rejects_values_and_shapes():
+    with pytest.raises(bonsai.BonsaiError) as e:
+        bonsai.q1_pack(np.zeros((1, 32), np.int8))
+    assert e.value.status == bonsai.ERR_VALUE
+    with pytest.raises(bonsai.BonsaiError) as e:
+        bonsai.q2t_pack(np.full((1, 16), 2, np.int8))
+    assert e.value.status == bonsai.ERR_VALUE
+    with pytest.raises(bonsai.BonsaiError) as e:
+        bonsai.q1_pack(np.ones((1, 33), np.int8))
+    assert e.value.status == bonsai.ERR_SHAPE
+
+
+# ---- GPU entry points: host-side validation only (nothing is launched) ------------------
+GPU_FNS = ["bonsai_q1_gemv", "bonsai_q1_gemm", "bonsai_q2t_gemv"]
+FAKE = 0x7F0000000000          # aligned, never dereferenced: every case below fails validation
+
+
+@pytest.mark.parametrize("fn", GPU_FNS)
+def test_gpu_entry_validation(fn):
+    f = getattr(bonsai.raw(), fn)
+    p = FAKE
+    assert f(None, p, p, p, 1, 64, 128, None) == bonsai.ERR_NULL
+    assert f(p, None, p, p, 1, 64, 128, None) == bonsai.ERR_NULL
+    assert f(p, p, None, p, 1, 64, 128, None) == bonsai.ERR_NULL
+    assert f(p, p, p, None, 1, 64, 128, None) == bonsai.ERR_NULL
+    assert f(p, p, p, p, 1, 64, 100, None) == bonsai.ERR_SHAPE
+    assert f(p, p, p, p, -1, 64, 128, None) == bonsai.ERR_SHAPE
+    assert f(p, p, p, p, 1, -5, 128, None) == bonsai.ERR_SHAPE
+    assert f(p, p, p, p, 1, 64, 131072 + 128, None) == bonsai.ERR_SHAPE
+    assert f(p + 4, p, p, p, 1, 64, 128, None) == bonsai.ERR_ALIGN
+    assert f(p, p + 2, p, p, 1, 64, 128, None) == bonsai.ERR_ALIGN
+    assert f(p, p, p + 8, p, 1, 64, 128, None) == bonsai.ERR_ALIGN
+    assert f(p, p, p, p + 4, 1, 64, 128, None) == bonsai.ERR_ALIGN
+    # empty products are no-ops that never look at the pointers
+    assert f(None, None, None, None, 0, 64, 128, None) == bonsai.OK
+    assert f(None, None, None, None, 3, 0, 128, None) == bonsai.OK
+
+
+@pytest.mark.parametrize("fn", ["bonsai_q1_gemv", "bonsai_q2t_gemv"])
+def test_gemv_rejects_m_above_8(fn):
+    f = getattr(bonsai.raw(), fn)
+    assert f(FAKE, FAKE, FAKE, FAKE, 9, 64, 128, None) == bonsai.ERR_SHAPE
+
+
+def test_gemm_accepts_large_m_in_validation_only():
+    # M = 2^30 + 1 is rejected; nothing is launched for it
+    f = bonsai.raw().bonsai_q1_gemm
+    assert f(FAKE, FAKE, FAKE, FAKE, (1 << 30) + 1, 64, 128, None) == bonsai.ERR_SHAPE
