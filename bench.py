@@ -1,0 +1,346 @@
+#!/usr/bin/env python3
+"""Throughput of the binary g128 decode GEMV (and the rest of the hot path) on one MI355X.
+
+Headline (one JSON line on stdout): packed-weight GB/s of the decode GEMV on the workload
+"binary g128 decode GEMV, M = 1, K = 5120, one MLP-shaped (N = 13824) and one attention-shaped
+(N = 5120) projection per step".  A step is those two GEMV calls, each on a distinct copy of
+the weights; the copies rotate through more than 1 GiB so no launch finds its weights in the
+256 MB Infinity Cache.  The K timed steps are replayed from a HIP graph (the way a decode loop
+is issued), with inputs resident in HBM before the timed region starts.
+
+Beside it: the roofline of the dominant kernel (per-launch algorithmic bytes over the kernel's
+device duration, timed with HIP events recorded by hipExtLaunchKernel around each launch), the
+LM-head GEMV (N = 248320), the pp512 prefill GEMM (M = 512, N = 13824, K = 5120, TFLOP/s), the
+ternary decode GEMV (M = 1 and 8), a device copy probe, and the CPU oracle timed on the host.
+
+Progress lines go to stderr.  Only the CPU-baseline leg touches the oracle.
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+from concurrent.futures import ThreadPoolExecutor
+from pathlib import Path
+
+import numpy as np
+
+ROOT = Path(__file__).resolve().parent
+sys.path.insert(0, str(ROOT))
+
+PEAK_HBM_GBPS = 8000.0          # MI355X HBM3E
+PEAK_FP16_TFLOPS = 2500.0       # MI355X dense fp16 MFMA
+ROTATE_BYTES = 1 << 30          # weight copies per shape span more than this
+
+
+def log(msg: str) -> None:
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+# ---- HIP events through the process's one HIP runtime ------------------------------------
+class Hip:
+    def __init__(self):
+        self.lib = ctypes.CDLL("libamdhip64.so.7")      # the runtime torch already loaded
+        self.lib.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.lib.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+        self.lib.hipEventSynchronize.argtypes = [ctypes.c_void_p]
+        self.lib.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                                 ctypes.c_void_p]
+        self.lib.hipEventDestroy.argtypes = [ctypes.c_void_p]
+
+    def event(self) -> int:
+        ev = ctypes.c_void_p()
+        assert self.lib.hipEventCreate(ctypes.byref(ev)) == 0
+        return ev.value
+
+    def record(self, ev: int, stream: int) -> None:
+        assert self.lib.hipEventRecord(ev, stream) == 0
+
+    def elapsed_ms(self, a: int, b: int) -> float:
+        assert self.lib.hipEventSynchronize(b) == 0
+        ms = ctypes.c_float()
+        assert self.lib.hipEventElapsedTime(ctypes.byref(ms), a, b) == 0
+        return float(ms.value)
+
+    def destroy(self, ev: int) -> None:
+        self.lib.hipEventDestroy(ev)
+
+
+def q1_bytes(N: int, K: int) -> int:
+    """Packed weight bytes: one sign bit per weight plus one binary16 scale per 128."""
+    return N * K // 8 + 2 * N * (K // 128)
+
+
+def q2t_bytes(N: int, K: int) -> int:
+    return N * K // 4 + 2 * N * (K // 128)
+
+
+def kernel_times(hip: Hip, bonsai, launches) -> list[float]:
+    """Device durations (ms) of each launch, via hipExtLaunchKernel start/stop events."""
+    evs = [(hip.event(), hip.event()) for _ in launches]
+    for (a, b), fn in zip(evs, launches):
+        bonsai.time_next_launch(a, b)
+        fn()
+    out = [hip.elapsed_ms(a, b) for a, b in evs]
+    for a, b in evs:
+        hip.destroy(a)
+        hip.destroy(b)
+    return out
+
+
+def src_digest(path: Path) -> str:
+    return hashlib.sha256(path.read_bytes()).hexdigest()[:16]
+
+
+def read_pmc(name: str, digest: str):
+    """HBM bytes per launch from a committed rocprofv3 counter summary, if it was taken on
+    the kernel source as it is now (else None)."""
+    p = ROOT / "profiles" / name
+    if not p.exists():
+        return None
+    kv = {}
+    for line in p.read_text().splitlines():
+        if ":" in line and not line.startswith("#"):
+            k, v = line.split(":", 1)
+            kv[k.strip()] = v.strip()
+    if kv.get("kernel_source_sha256_16") != digest or "hbm_bytes_per_launch" not in kv:
+        return None
+    return float(kv["hbm_bytes_per_launch"])
+
+
+# ---- the oracle on the host (CPU baseline) -----------------------------------------------
+def cpu_baseline(wA, sA, xA, wB, sB, xB, K, budget_s: float):
+    import oracle
+    orc = oracle.load()
+    threads = max(1, min(os.cpu_count() or 1, 16))
+    jobs = []
+    for (w, s, x) in ((wA, sA, xA), (wB, sB, xB)):
+        N = w.shape[0]
+        step = (N + threads - 1) // threads
+        for n0 in range(0, N, step):
+            idx = np.arange(n0, min(N, n0 + step), dtype=np.int64)
+            jobs.append((w, s, x, idx))
+    step_bytes = q1_bytes(wA.shape[0], K) + q1_bytes(wB.shape[0], K)
+    t0 = time.perf_counter()
+    passes = 0
+    with ThreadPoolExecutor(max_workers=threads) as ex:
+        while True:
+            list(ex.map(lambda j: orc.q1_matmul(j[0], j[1], j[2], K, None, j[3]), jobs))
+            passes += 1
+            if time.perf_counter() - t0 >= budget_s:
+                break
+    dt = time.perf_counter() - t0
+    return {"value": round(passes * step_bytes / dt / 1e9, 4), "unit": "GB/s", "cores": threads,
+            "kind": "oracle",
+            "sample": f"{passes} full step(s) of the workload (N=13824 and N=5120, K=5120, M=1), "
+                      f"rows split over {threads} host threads, {dt:.1f} s wall; packed-weight bytes "
+                      f"per second as in the GPU value"}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=400)
+    ap.add_argument("--warmup", type=int, default=40)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--headline-only", action="store_true", help="skip the secondary measurements")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path (the GEMV shards by "
+              "rows with no collective; see the design notes). Run with --gpus 1.", file=sys.stderr)
+        return 2
+    if args.steps < 1 or args.warmup < 0:
+        print("--steps must be >= 1 and --warmup >= 0", file=sys.stderr)
+        return 2
+
+    import torch
+    import synth
+    import ternary_weight_quantized_bonsai_amd as bonsai
+
+    dev = torch.device("cuda:0")
+    hip = Hip()
+    stream = lambda: torch.cuda.current_stream().cuda_stream  # noqa: E731
+
+    def up(a):
+        a = np.ascontiguousarray(a)
+        view = {np.dtype(np.uint32): np.int32, np.dtype(np.uint16): np.int16}[a.dtype]
+        return torch.from_numpy(a.view(view)).to(dev)
+
+    # ---- headline workload: the two decode projections at hidden 5120 -------------------
+    K = 5120
+    shapes = {"mlp": 13824, "attn": 5120}
+    host = {k: synth.make_q1(1, n, K) for k, n in shapes.items()}
+    step_bytes = sum(q1_bytes(n, K) for n in shapes.values())
+    R = max(3, math.ceil(ROTATE_BYTES / step_bytes))
+    log(f"uploading {R} weight copies of each shape ({R * step_bytes / 2**30:.2f} GiB)")
+    W = {}
+    for k in shapes:
+        w0, s0, x0 = (up(a) for a in host[k])
+        W[k] = ([w0] + [w0.clone() for _ in range(R - 1)], [s0] + [s0.clone() for _ in range(R - 1)], x0,
+                torch.empty((1, shapes[k]), dtype=torch.float32, device=dev))
+
+    def step(i):
+        j = i % R
+        for k in ("mlp", "attn"):
+            ws, ss, x, y = W[k]
+            bonsai.q1_gemv(ws[j], ss[j], x, out=y)
+
+    step(0)
+    torch.cuda.synchronize()
+    log("capturing graphs")
+    g_warm, g_main = torch.cuda.CUDAGraph(), torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g_warm):
+        for i in range(max(args.warmup, 1)):
+            step(i)
+    with torch.cuda.graph(g_main):
+        for i in range(args.steps):
+            step(i + args.warmup)
+    if args.warmup:
+        g_warm.replay()
+    torch.cuda.synchronize()
+
+    log(f"timing {args.steps} steps")
+    e0, e1 = hip.event(), hip.event()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    hip.record(e0, stream())
+    g_main.replay()
+    hip.record(e1, stream())
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = hip.elapsed_ms(e0, e1)
+    value = args.steps * step_bytes / (ms / 1e3) / 1e9
+    log(f"{ms:.3f} ms for {args.steps} steps ({wall * 1e3:.3f} ms wall): {value:.1f} GB/s")
+
+    # ---- dominant kernel: device durations of the same launches, no graph ----------------
+    n_t = min(args.steps, 300)
+    launches = []
+    for i in range(n_t):
+        j = i % R
+        for k in ("mlp", "attn"):
+            ws, ss, x, y = W[k]
+            launches.append(lambda ws=ws, ss=ss, x=x, y=y, j=j: bonsai.q1_gemv(ws[j], ss[j], x, out=y))
+    kt = kernel_times(hip, bonsai, launches)
+    t_mlp, t_attn = np.mean(kt[0::2]), np.mean(kt[1::2])
+    alg = {k: q1_bytes(n, K) + 2 * K + 4 * n for k, n in shapes.items()}    # weights + x + y
+    per_launch_bytes = (alg["mlp"] + alg["attn"]) / 2
+    per_launch_ms = float(np.mean(kt))
+    achieved = per_launch_bytes / (per_launch_ms / 1e3) / 1e9
+    digest = src_digest(ROOT / "ternary_weight_quantized_bonsai_amd" / "csrc" / "q1_gemv.hip")
+    traffic = read_pmc("q1_gemv_decode_pair_pmc.txt", digest)
+    roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                "frac": round(achieved / PEAK_HBM_GBPS, 4), "traffic": traffic,
+                "kernel": "q1_gemv_kernel<1>", "avg_launch_us": round(per_launch_ms * 1e3, 3),
+                "bytes_per_launch": per_launch_bytes,
+                "per_shape_us": {"mlp_13824x5120": round(t_mlp * 1e3, 3), "attn_5120x5120": round(t_attn * 1e3, 3)}}
+    log(f"q1_gemv device time: mlp {t_mlp * 1e3:.2f} us, attn {t_attn * 1e3:.2f} us -> {achieved:.1f} GB/s")
+
+    extra = {}
+    if not args.headline_only:
+        # LM head: N = 248320 vocabulary rows
+        N3 = 248320
+        w, s, x = (up(a) for a in synth.make_q1(1, N3, K))
+        R3 = max(3, math.ceil(ROTATE_BYTES / q1_bytes(N3, K)))
+        ws = [w] + [w.clone() for _ in range(R3 - 1)]
+        ss = [s] + [s.clone() for _ in range(R3 - 1)]
+        y = torch.empty((1, N3), dtype=torch.float32, device=dev)
+        bonsai.q1_gemv(ws[0], ss[0], x, out=y)
+        kt3 = kernel_times(hip, bonsai, [lambda j=j: bonsai.q1_gemv(ws[j % R3], ss[j % R3], x, out=y)
+                                         for j in range(4 * R3)])
+        t3 = float(np.mean(kt3))
+        gb3 = q1_bytes(N3, K) / (t3 / 1e3) / 1e9
+        extra["lm_head_gemv"] = {"shape": "M=1 N=248320 K=5120", "avg_kernel_us": round(t3 * 1e3, 2),
+                                 "packed_weight_GBps": round(gb3, 1), "frac_of_8TBps": round(gb3 / PEAK_HBM_GBPS, 4)}
+        log(f"lm head: {t3 * 1e3:.1f} us, {gb3:.1f} GB/s")
+        del ws, ss, w, s, x, y
+
+        # Prefill GEMM pp512
+        M4, N4 = 512, 13824
+        w, s, x = (up(a) for a in synth.make_q1(M4, N4, K))
+        ws = [w] + [w.clone() for _ in range(2)]
+        ss = [s] + [s.clone() for _ in range(2)]
+        y = torch.empty((M4, N4), dtype=torch.float32, device=dev)
+        bonsai.q1_gemm(ws[0], ss[0], x, out=y)
+        kt4 = kernel_times(hip, bonsai, [lambda j=j: bonsai.q1_gemm(ws[j % 3], ss[j % 3], x, out=y)
+                                         for j in range(30)])
+        t4 = float(np.mean(kt4))
+        tf = 2.0 * M4 * N4 * K / (t4 / 1e3) / 1e12
+        extra["prefill_gemm"] = {"shape": "M=512 N=13824 K=5120", "avg_kernel_us": round(t4 * 1e3, 2),
+                                 "TFLOPs": round(tf, 2),
+                                 "roofline": {"bound": "mfma", "achieved": round(tf, 2), "peak": PEAK_FP16_TFLOPS,
+                                              "unit": "TFLOP/s", "frac": round(tf / PEAK_FP16_TFLOPS, 4)}}
+        log(f"prefill gemm: {t4 * 1e3:.1f} us, {tf:.1f} TFLOP/s")
+        del ws, ss, w, s, x, y
+
+        # Ternary decode GEMV, M = 1 and 8
+        N5 = 5120
+        tern = {}
+        for M5 in (1, 8):
+            w, s, x = (up(a) for a in synth.make_q2t(M5, N5, K))
+            R5 = max(3, math.ceil(ROTATE_BYTES / q2t_bytes(N5, K)))
+            ws = [w] + [w.clone() for _ in range(R5 - 1)]
+            ss = [s] + [s.clone() for _ in range(R5 - 1)]
+            y = torch.empty((M5, N5), dtype=torch.float32, device=dev)
+            bonsai.q2t_gemv(ws[0], ss[0], x, out=y)
+            kt5 = kernel_times(hip, bonsai, [lambda j=j: bonsai.q2t_gemv(ws[j % R5], ss[j % R5], x, out=y)
+                                             for j in range(R5)])
+            t5 = float(np.mean(kt5))
+            gb5 = q2t_bytes(N5, K) / (t5 / 1e3) / 1e9
+            tern[f"M{M5}"] = {"avg_kernel_us": round(t5 * 1e3, 2), "packed_weight_GBps": round(gb5, 1),
+                              "frac_of_8TBps": round(gb5 / PEAK_HBM_GBPS, 4)}
+            log(f"ternary M={M5}: {t5 * 1e3:.2f} us, {gb5:.1f} GB/s")
+            del ws, ss, w, s, x, y
+        extra["ternary_gemv"] = {"shape": "N=5120 K=5120", **tern}
+
+        # Device copy probe: what a plain copy kernel reaches on this machine (read + write bytes)
+        nbytes = 1 << 30
+        a = torch.empty(nbytes // 4, dtype=torch.float32, device=dev)
+        b = torch.empty_like(a)
+        b.copy_(a)
+        torch.cuda.synchronize()
+        c0, c1 = hip.event(), hip.event()
+        hip.record(c0, stream())
+        for _ in range(10):
+            b.copy_(a)
+        hip.record(c1, stream())
+        tc = hip.elapsed_ms(c0, c1) / 10
+        extra["copy_probe"] = {"bytes_moved": 2 * nbytes, "GBps": round(2 * nbytes / (tc / 1e3) / 1e9, 1)}
+        log(f"copy probe: {2 * nbytes / (tc / 1e3) / 1e9:.1f} GB/s")
+        del a, b
+
+    line = {
+        "metric": "Binary g128 GEMV packed-weight GB/s (% HBM peak); PP512 GEMM TFLOP/s",
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms / args.steps, 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16",
+        "data": "synthetic",
+        "config": {"workload": "binary g128 decode GEMV, M=1, K=5120: one MLP-shaped (N=13824) and one "
+                               "attention-shaped (N=5120) projection per step",
+                   "weight_copies_rotated": R, "accumulate": "f32", "frac_of_8TBps": round(value / PEAK_HBM_GBPS, 4),
+                   "timed_as": "HIP graph replay of the steps, HIP events on the launch stream"},
+        "roofline": roofline,
+    }
+    line.update(extra)
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle")
+        hA, hB = host["mlp"], host["attn"]
+        line["cpu_baseline"] = cpu_baseline(hA[0], hA[1], hA[2], hB[0], hB[1], hB[2], K, args.cpu_seconds)
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -26,7 +26,8 @@
  * CONVENTIONS
  *   Ownership : the caller allocates and owns every buffer; for the GPU entry points they are
  *               device memory.  The library allocates nothing, frees nothing and never
- *               synchronises in these calls; it keeps no state between calls.
+ *               synchronises in these calls; apart from the per-thread measurement hook
+ *               and last-error name below, it keeps no state between calls.
  *   Streams   : GPU work is enqueued on `hip_stream` (a hipStream_t; NULL = default stream).
  *               BONSAI_OK means "validated and enqueued"; faults during execution surface at
  *               the caller's next synchronisation.
@@ -91,6 +92,13 @@ bonsai_status bonsai_q2t_unpack(const uint32_t *wcodes, int64_t N, int64_t K, in
 /* Name of the HIP runtime error behind the most recent BONSAI_ERR_DEVICE returned on the
  * calling thread ("none" if there was none).  Static string; never NULL. */
 const char *bonsai_last_device_error(void);
+
+/* Measurement hook.  The next GPU entry point called on this thread launches its kernel with
+ * hipExtLaunchKernel, recording start_event when the kernel starts executing and stop_event
+ * when it completes, so hipEventElapsedTime(start, stop) is that kernel's device duration.
+ * The events are hipEvent_t handles created and owned by the caller (either may be NULL);
+ * the hook is consumed by that one call.  Do not arm it around stream capture. */
+bonsai_status bonsai_time_next_launch(void *start_event, void *stop_event);
 
 /* Static, NUL-terminated description of a status value. */
 const char *bonsai_status_str(bonsai_status s);

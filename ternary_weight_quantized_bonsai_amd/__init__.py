@@ -39,6 +39,8 @@ for _name in ("bonsai_q1_pack", "bonsai_q1_unpack", "bonsai_q2t_pack", "bonsai_q
     _f = getattr(_lib, _name)
     _f.argtypes = [_vp, _c_i64, _c_i64, _vp]
     _f.restype = ctypes.c_int
+_lib.bonsai_time_next_launch.argtypes = [_vp, _vp]
+_lib.bonsai_time_next_launch.restype = ctypes.c_int
 _lib.bonsai_last_device_error.argtypes = []
 _lib.bonsai_last_device_error.restype = ctypes.c_char_p
 _lib.bonsai_status_str.argtypes = [ctypes.c_int]
@@ -59,6 +61,12 @@ def status_str(status: int) -> str:
 def raw():
     """The ctypes handle of libbonsai.so (argtypes set), for callers passing raw pointers."""
     return _lib
+
+
+def time_next_launch(start_event: int, stop_event: int) -> None:
+    """Arm the measurement hook: the next GPU call on this thread records the two hipEvent_t
+    handles around its kernel's execution (bonsai_time_next_launch)."""
+    _check("bonsai_time_next_launch", _lib.bonsai_time_next_launch(start_event, stop_event))
 
 
 def _check(fn: str, status: int):

@@ -3,6 +3,8 @@
 // normative layout are in include/bonsai.h.
 #include <limits.h>
 
+#include <hip/hip_ext.h>
+
 #include "../../include/bonsai.h"
 #include "launch.h"
 
@@ -16,6 +18,7 @@ __global__ void fill_zero_kernel(float *y, int64_t count)
 }
 
 thread_local const char *g_last_device_error = "none";
+thread_local hipEvent_t g_time_start = nullptr, g_time_stop = nullptr;
 
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
@@ -49,11 +52,19 @@ bonsai_status run(const void *w, const void *s, const void *x, float *y, int64_t
 
 }  // namespace
 
+hipError_t launch_kernel(const void *fn, dim3 grid, dim3 block, void **args, size_t lds, hipStream_t stream)
+{
+    hipEvent_t start = g_time_start, stop = g_time_stop;
+    g_time_start = g_time_stop = nullptr;
+    if (!start && !stop) return hipLaunchKernel(fn, grid, block, args, lds, stream);
+    return hipExtLaunchKernel(fn, grid, block, args, lds, stream, start, stop, 0);
+}
+
 hipError_t launch_fill_zero(float *y, int64_t count, hipStream_t stream)
 {
     const int64_t blocks = (count + 255) / 256;
     void *args[] = {&y, &count};
-    return hipLaunchKernel(reinterpret_cast<const void *>(&fill_zero_kernel),
+    return launch_kernel(reinterpret_cast<const void *>(&fill_zero_kernel),
                            dim3((unsigned)(blocks < 4096 ? blocks : 4096)), dim3(256), args, 0, stream);
 }
 
@@ -150,6 +161,13 @@ bonsai_status bonsai_q2t_unpack(const uint32_t *wcodes, int64_t N, int64_t K, in
 }
 
 const char *bonsai_last_device_error(void) { return g_last_device_error; }
+
+bonsai_status bonsai_time_next_launch(void *start_event, void *stop_event)
+{
+    g_time_start = static_cast<hipEvent_t>(start_event);
+    g_time_stop = static_cast<hipEvent_t>(stop_event);
+    return BONSAI_OK;
+}
 
 const char *bonsai_status_str(bonsai_status s)
 {

@@ -14,4 +14,8 @@ hipError_t launch_q1_gemm(const uint32_t *wbits, const uint16_t *scales, const u
                           int M, int N, int K, hipStream_t stream);
 hipError_t launch_fill_zero(float *y, int64_t count, hipStream_t stream);
 
+// Every kernel launch of the library goes through here: a plain hipLaunchKernel, or, when the
+// caller armed the timing hook on this thread, hipExtLaunchKernel with the caller's events.
+hipError_t launch_kernel(const void *fn, dim3 grid, dim3 block, void **args, size_t lds, hipStream_t stream);
+
 }  // namespace bonsai

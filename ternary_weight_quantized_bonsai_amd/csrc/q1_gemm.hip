@@ -128,7 +128,7 @@ hipError_t launch_q1_gemm(const uint32_t *wbits, const uint16_t *scales, const u
     const int64_t tiles = (int64_t)((N + BN - 1) / BN) * ((M + BM - 1) / BM);
     if (tiles > INT_MAX) return hipErrorInvalidValue;
     void *args[] = {&wbits, &scales, &x, &y, &M, &N, &K};
-    return hipLaunchKernel(reinterpret_cast<const void *>(&q1_gemm_kernel), dim3((unsigned)tiles), dim3(256),
+    return launch_kernel(reinterpret_cast<const void *>(&q1_gemm_kernel), dim3((unsigned)tiles), dim3(256),
                            args, 0, stream);
 }
 

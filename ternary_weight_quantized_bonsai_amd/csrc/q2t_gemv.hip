@@ -115,7 +115,7 @@ hipError_t launch_m(const uint32_t *wcodes, const uint16_t *scales, const uint16
     slices = (G + gps - 1) / gps;
     const size_t lds = slices > 1 ? (size_t)slices * M * 64 * sizeof(float) : 0;
     void *args[] = {&wcodes, &scales, &x, &y, &N, &K, (void *)&gps};
-    return hipLaunchKernel(reinterpret_cast<const void *>(&q2t_gemv_kernel<M>), dim3(tiles), dim3(64 * slices), args,
+    return launch_kernel(reinterpret_cast<const void *>(&q2t_gemv_kernel<M>), dim3(tiles), dim3(64 * slices), args,
                            lds, stream);
 }
 

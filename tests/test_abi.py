@@ -20,7 +20,7 @@ def test_header_declares_the_boundary():
     names = declared_functions()
     for want in ("bonsai_q1_gemv", "bonsai_q1_gemm", "bonsai_q2t_gemv", "bonsai_q1_pack",
                  "bonsai_q1_unpack", "bonsai_q2t_pack", "bonsai_q2t_unpack", "bonsai_status_str",
-                 "bonsai_last_device_error"):
+                 "bonsai_last_device_error", "bonsai_time_next_launch"):
         assert want in names
 
 
