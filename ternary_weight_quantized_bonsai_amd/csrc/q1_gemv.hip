@@ -3,126 +3,412 @@
 // The matmul runs straight on the packed sign words ("1-bit Bonsai 27B" model card: the
 // weights are used packed and never expanded back to FP16; the CUDA kernel unpacks the sign
 // codes inside the matmul and applies the group scales).  Decode is the memory-bound phase
-// (model card, cross-platform throughput), so the kernel is built around streaming the
-// 1.125 bits/weight once from HBM.
+// (model card, cross-platform throughput), so the kernel is organised around streaming the
+// 1.125 bits/weight from HBM once, with as few VALU operations per weight as possible.
 //
-// Work split.  Lane <-> weight row: each lane of a wave owns one of 64 consecutive rows and
-// walks a contiguous slice of its row's groups; the waves of a workgroup take the K-slices
-// of the same 64 rows and their partial sums meet in LDS in a fixed order (deterministic).
-// Because every lane of a wave is at the same k at the same time, x is wave-uniform and is
-// read through the scalar cache into SGPRs: it costs no VGPRs and no vector bandwidth.
+// Work split.  A workgroup owns 64 consecutive weight rows; its waves take disjoint K-slices
+// (whole groups) of those rows and meet in LDS at the end, summed in a fixed order.  Inside a
+// wave, lane r owns row r, so every lane is at the same k at the same time and x is
+// wave-uniform: it is read through the scalar cache into SGPRs.
 //
-// Sign expansion (exact).  For bit pair (j, j+16) of a word, shifting the word left by 15-j
-// puts the two bits on the binary16 sign positions 15 and 31; and-or with 1.0|1.0 then gives
-// the half pair (+-1, +-1) (bit 1 -> -1.0, bit 0 -> +1.0), which v_dot2_f32_f16 multiplies
-// exactly with the x pair (x[32w+j], x[32w+16+j]) into an fp32 partial.  Once per 128-weight
-// group the partial is multiplied by -s (the minus undoes the flipped polarity).
+// Loads.  Row r's bytes for a batch of B groups are 16*B contiguous bytes, 640 B away from row
+// r+1 at K = 5120.  Each global load instruction therefore covers 64/B rows x 16*B bytes (B
+// lanes per row, every byte of each touched segment used), and the wave transposes the batch
+// through its own LDS tile so that lane r then reads its row.  The next batch is in flight
+// while the current one is consumed.
+//
+// Sign expansion (exact, about 1.1 VALU op per weight).  Masking a sign word with
+// 0x00010001 << p keeps bits p and p+16; read as two binary16 values these are b*c_p with
+// c_p = 2^-14, 2^-13, 2^-11, 2^-7, 2 for p = 10 .. 14 (exponent-field bits, never subnormal).
+// Shifting the word left by 0, 5, 10 (and right by 1 for bits 15, 31) brings every bit onto
+// one of these five positions, so 16 masks + 16 v_dot2_f32_f16 against the x pairs
+// (x[32i+j], x[32i+16+j]) give five exact per-class sums  A_p = c_p * sum b x.  Per group:
+//     sum_k (2b-1) x = sum_p (2/c_p) A_p - X_g,      X_g = sum_{k in group} x_k,
+// then y += s * (that).  The 2/c_p are powers of two, so the class combination is exact; X_g
+// is formed once per group per wave by 16 lanes per group and broadcast with v_readlane.
 #include "device.h"
 #include "launch.h"
 
 namespace bonsai {
 namespace {
 
-constexpr int kGroupsPerBatch = 4;   // loads issued together before the batch is consumed
+// Pair (lo(a), lo(b)) / (hi(a), hi(b)) of two uniform dwords, on the scalar unit.
+__device__ __forceinline__ uint32_t s_pack_ll(uint32_t a, uint32_t b)
+{
+    uint32_t r;
+    asm("s_pack_ll_b32_b16 %0, %1, %2" : "=s"(r) : "s"(a), "s"(b));
+    return r;
+}
+__device__ __forceinline__ uint32_t s_pack_hh(uint32_t a, uint32_t b)
+{
+    uint32_t r;
+    asm("s_pack_hh_b32_b16 %0, %1, %2" : "=s"(r) : "s"(a), "s"(b));
+    return r;
+}
 
-template <int M>
-__global__ __launch_bounds__(1024) void q1_gemv_kernel(const uint32_t *__restrict__ wbits,
+// Class sums of one 32-bit sign word against its 32 x values (16 uniform dwords at xw).
+// acc[0..4] collect the classes p = 10 .. 14.
+__device__ __forceinline__ void word_classes(uint32_t w, const uint32_t *__restrict__ xw, float acc[5])
+{
+    const uint32_t v0 = w, v1 = w << 5, v2 = w << 10, v3 = w >> 1;
+    uint32_t xp[16];
+#pragma unroll
+    for (int j = 0; j < 16; j += 2) {
+        const uint32_t a = xw[j >> 1], b = xw[8 + (j >> 1)];
+        xp[j] = s_pack_ll(a, b);          // (x[j],   x[16+j])
+        xp[j + 1] = s_pack_hh(a, b);      // (x[j+1], x[17+j])
+    }
+#pragma unroll
+    for (int p = 10; p <= 14; ++p) {
+        const uint32_t mask = 0x00010001u << p;
+        float a = acc[p - 10];
+        a = dot2(v0 & mask, xp[p], a);                 // bit p
+        a = dot2(v1 & mask, xp[p - 5], a);             // bit p - 5
+        a = dot2(v2 & mask, xp[p - 10], a);            // bit p - 10
+        if (p == 14) a = dot2(v3 & mask, xp[15], a);   // bit 15
+        acc[p - 10] = a;
+    }
+}
+
+template <int M, int BATCH>
+__global__ __launch_bounds__(768) void q1_gemv_mask_kernel(const uint32_t *__restrict__ wbits,
                                                        const uint16_t *__restrict__ scales,
                                                        const uint16_t *__restrict__ x,
                                                        float *__restrict__ y, int N, int K, int gps)
 {
-    extern __shared__ float red[];                      // [slices][M][64] partial sums
+    constexpr int STRIDE = BATCH + 1;           // 16-byte cells per LDS tile row (one of padding)
+    constexpr int RPI = 64 / BATCH;             // rows per global load instruction
+    constexpr int XH = (BATCH + 3) / 4;         // X_g passes (4 groups per pass)
+    extern __shared__ u32x4 lds[];              // [waves][64][STRIDE] tiles, then [waves][M][64] floats
+
     const int lane = threadIdx.x & 63;
-    const int slice = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int nslices = blockDim.x >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int nwaves = blockDim.x >> 6;
     const int G = K >> 7;
-    const int row = blockIdx.x * 64 + lane;
-    const int r = row < N ? row : N - 1;               // tail lanes read a valid row, store nothing
-    const int g0 = slice * gps;
+    const int row0 = blockIdx.x * 64;
+    const int row = row0 + lane;
+    const int rclamp = min(row, N - 1);
+    const int g0 = wave * gps;
     const int g1 = min(G, g0 + gps);
 
-    const uint4 *wrow = reinterpret_cast<const uint4 *>(wbits + (size_t)r * (K >> 5));
-    const uint16_t *srow = scales + (size_t)r * G;
+    u32x4 *tile = lds + wave * 64 * STRIDE;
+    const u32x4 *wg = reinterpret_cast<const u32x4 *>(wbits);     // (row n, group g) at n * G + g
     const uint32_t *xd = reinterpret_cast<const uint32_t *>(x);
+    const uint16_t *srow = scales + (size_t)rclamp * G;
 
+    // global load mapping: instruction i reads row lrow + i*RPI of the tile, group lchunk of
+    // the batch.  Rows past N (last tile only) are not loaded; their lanes store nothing.
+    const int lrow = lane / BATCH, lchunk = lane % BATCH;
+    const u32x4 *wbase = wg + (size_t)(row0 + lrow) * G;
+    const int nrows = N - row0 - lrow;                 // rows of this lane's column still valid
     float acc[M];
 #pragma unroll
     for (int m = 0; m < M; ++m) acc[m] = 0.f;
 
-    for (int gb = g0; gb < g1; gb += kGroupsPerBatch) {
-        uint4 q[kGroupsPerBatch];
-        float s[kGroupsPerBatch];
+    // batch in flight: BATCH 16-byte cells of the tile and the lane's BATCH scales
+    u32x4 v[BATCH];
+    float sc[BATCH];
+    {
+        const int gg = min(g0 + lchunk, g1 - 1);
 #pragma unroll
-        for (int u = 0; u < kGroupsPerBatch; ++u) {
-            const int g = min(gb + u, g1 - 1);
-            q[u] = wrow[g];
-            s[u] = f16_bits_to_f32(srow[g]);
+        for (int i = 0; i < BATCH; ++i)
+            if (i * RPI < nrows) v[i] = wbase[(size_t)i * RPI * G + gg];
+#pragma unroll
+        for (int u = 0; u < BATCH; ++u) sc[u] = f16_bits_to_f32(srow[min(g0 + u, g1 - 1)]);
+    }
+    for (int gb = g0; gb < g1; gb += BATCH) {
+#pragma unroll
+        for (int i = 0; i < BATCH; ++i) tile[(lrow + i * RPI) * STRIDE + lchunk] = v[i];
+        float s_cur[BATCH];
+#pragma unroll
+        for (int u = 0; u < BATCH; ++u) s_cur[u] = sc[u];
+        const int gn = gb + BATCH;
+        if (gn < g1) {                                      // next batch in flight
+            const int gg = min(gn + lchunk, g1 - 1);
+#pragma unroll
+            for (int i = 0; i < BATCH; ++i)
+                if (i * RPI < nrows) v[i] = wbase[(size_t)i * RPI * G + gg];
+#pragma unroll
+            for (int u = 0; u < BATCH; ++u) sc[u] = f16_bits_to_f32(srow[min(gn + u, g1 - 1)]);
         }
+
+        // X_g of the batch's groups: 16 lanes per group, 8 values each, summed across the 16.
+        float xg[M][XH];
 #pragma unroll
-        for (int u = 0; u < kGroupsPerBatch; ++u) {
+        for (int m = 0; m < M; ++m)
+#pragma unroll
+            for (int h = 0; h < XH; ++h) {
+                const int g = min(gb + 4 * h + (lane >> 4), G - 1);
+                const u32x4 xv = *reinterpret_cast<const u32x4 *>(x + (size_t)m * K + (size_t)g * 128 +
+                                                                  8 * (lane & 15));
+                float t = dot2(xv.x, 0x3C003C00u, 0.f);
+                t = dot2(xv.y, 0x3C003C00u, t);
+                t = dot2(xv.z, 0x3C003C00u, t);
+                t = dot2(xv.w, 0x3C003C00u, t);
+                xg[m][h] = row16_sum(t);
+            }
+
+#pragma unroll
+        for (int u = 0; u < BATCH; ++u) {
             const int g = gb + u;
             if (g >= g1) break;
-            const uint32_t words[4] = {q[u].x, q[u].y, q[u].z, q[u].w};
-            float part[M];
+            const u32x4 q = tile[lane * STRIDE + u];
+            const uint32_t words[4] = {q.x, q.y, q.z, q.w};
 #pragma unroll
-            for (int m = 0; m < M; ++m) part[m] = 0.f;
+            for (int m = 0; m < M; ++m) {
+                float cls[5] = {0.f, 0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                uint32_t e[16];
-#pragma unroll
-                for (int j = 0; j < 16; ++j)
-                    e[j] = ((words[i] << (15 - j)) & 0x80008000u) | 0x3C003C00u;
-#pragma unroll
-                for (int m = 0; m < M; ++m) {
-                    // x[32i .. 32i+31] of group g of row m, as 16 dwords of half pairs
-                    const uint32_t *xw = xd + (size_t)m * (K >> 1) + (size_t)g * 64 + i * 16;
-#pragma unroll
-                    for (int j = 0; j < 16; ++j) {
-                        const uint32_t a = xw[j >> 1], b = xw[8 + (j >> 1)];
-                        part[m] = dot2(e[j], (j & 1) ? pack_hi(a, b) : pack_lo(a, b), part[m]);
-                    }
-                }
+                for (int i = 0; i < 4; ++i)
+                    word_classes(words[i], xd + (size_t)m * (K >> 1) + (size_t)g * 64 + i * 16, cls);
+                const float t = cls[0] * 32768.f + cls[1] * 16384.f + cls[2] * 4096.f + cls[3] * 256.f + cls[4];
+                const int xi = __builtin_amdgcn_readlane(__builtin_bit_cast(int, xg[m][u / 4]), 16 * (u % 4));
+                acc[m] = fmaf(s_cur[u], t - __builtin_bit_cast(float, xi), acc[m]);
             }
-#pragma unroll
-            for (int m = 0; m < M; ++m) acc[m] = fmaf(-s[u], part[m], acc[m]);
         }
     }
 
-    if (nslices == 1) {
+    if (nwaves == 1) {
         if (row < N)
 #pragma unroll
             for (int m = 0; m < M; ++m) y[(size_t)m * N + row] = acc[m];
         return;
     }
+    float *red = reinterpret_cast<float *>(lds + nwaves * 64 * STRIDE);
 #pragma unroll
-    for (int m = 0; m < M; ++m) red[(slice * M + m) * 64 + lane] = acc[m];
+    for (int m = 0; m < M; ++m) red[(wave * M + m) * 64 + lane] = acc[m];
     __syncthreads();
-    if (slice == 0 && row < N) {
+    if (wave == 0 && row < N) {
 #pragma unroll
         for (int m = 0; m < M; ++m) {
             float t = red[m * 64 + lane];
-            for (int sl = 1; sl < nslices; ++sl) t += red[(sl * M + m) * 64 + lane];
+            for (int w = 1; w < nwaves; ++w) t += red[(w * M + m) * 64 + lane];
             y[(size_t)m * N + row] = t;
         }
     }
+}
+
+constexpr size_t kMaxLds = 65536;
+constexpr int kTargetWaves = 8192;     // ~8 resident waves per SIMD on 1024 SIMDs
+
+template <int M, int BATCH>
+size_t lds_bytes(int slices)
+{
+    return (size_t)slices * 64 * (BATCH + 1) * sizeof(u32x4) + (slices > 1 ? (size_t)slices * M * 64 * sizeof(float) : 0);
+}
+
+template <int M, int BATCH>
+hipError_t launch_mb(const uint32_t *wbits, const uint16_t *scales, const uint16_t *x, float *y,
+                     int N, int K, hipStream_t stream)
+{
+    const int G = K / 128;
+    const int tiles = (N + 63) / 64;
+    // Aim for about two waves per SIMD (1024 SIMDs) by splitting K across the waves of a
+    // workgroup, within the 64 KiB of LDS a workgroup may take.
+    int want = min(12, max(1, (kTargetWaves + tiles - 1) / tiles));
+    while (want > 1 && lds_bytes<M, BATCH>(want) > kMaxLds) --want;
+    int gps = (G + want - 1) / want;
+    gps = ((gps + BATCH - 1) / BATCH) * BATCH;
+    const int slices = (G + gps - 1) / gps;
+    const size_t lds = lds_bytes<M, BATCH>(slices);
+    void *args[] = {&wbits, &scales, &x, &y, &N, &K, &gps};
+    return launch_kernel(reinterpret_cast<const void *>(&q1_gemv_mask_kernel<M, BATCH>), dim3(tiles),
+                         dim3(64 * slices), args, lds, stream);
+}
+
+
+// ---- M = 1: nibble lookup tables ------------------------------------------------------------
+//
+// For every 4-wide chunk c of a group, a 16-entry fp32 table holds T_c[v] = sum_{j<4} +-x_{4c+j}
+// with the sign of term j given by bit j of v (bit 1 -> +x, bit 0 -> -x).  A row's 128 sign
+// bits of the group are then 32 nibbles, and the group's signed sum is sum_c T_c[nibble_c]:
+// one LDS read and one add per 4 weights, about 0.6 VALU operations per weight in all.  The
+// 32 tables of a group (2 KB) are built by the wave itself (two 16-byte LDS writes per lane).
+//
+// Addressing: with l = w << 2 and h = w >> 2, the low / high nibble of byte k of w, times 4, is
+// one SDWA and of byte k of l / h with 0x3C, written into byte 0 of an address register whose
+// bits 8..31 hold the (256-aligned) table base.  Chunk c's table is 16 consecutive floats at
+// byte offset 64*c (the read's immediate offset), so the 16 possible addresses of a lookup lie
+// in 16 distinct LDS banks: lookups never conflict, equal nibbles broadcast.
+//
+// Weight tile: 8 groups (128 B) of each of the wave's 64 rows arrive through direct
+// global->LDS loads, 8 rows x 128 B per instruction (fully used lines).  The 16-byte cell of
+// (row r, group u) of a batch sits at 128*r + 16*(u ^ ((r >> 1) & 7)): the swizzle keeps a
+// wave's row-wise reads of one column free of bank conflicts.
+
+// r[7:0] = 4 * nibble (byte KB of v masked with 0x3C); r[31:8] keep the LUT base (256-aligned).
+template <int KB>
+__device__ __forceinline__ void nib_addr(uint32_t &r, uint32_t v, uint32_t mask_3c)
+{
+    if constexpr (KB == 0)
+        asm("v_and_b32_sdwa %0, %1, %2 dst_sel:BYTE_0 dst_unused:UNUSED_PRESERVE src0_sel:DWORD src1_sel:BYTE_0" : "+v"(r) : "s"(mask_3c), "v"(v));
+    else if constexpr (KB == 1)
+        asm("v_and_b32_sdwa %0, %1, %2 dst_sel:BYTE_0 dst_unused:UNUSED_PRESERVE src0_sel:DWORD src1_sel:BYTE_1" : "+v"(r) : "s"(mask_3c), "v"(v));
+    else if constexpr (KB == 2)
+        asm("v_and_b32_sdwa %0, %1, %2 dst_sel:BYTE_0 dst_unused:UNUSED_PRESERVE src0_sel:DWORD src1_sel:BYTE_2" : "+v"(r) : "s"(mask_3c), "v"(v));
+    else
+        asm("v_and_b32_sdwa %0, %1, %2 dst_sel:BYTE_0 dst_unused:UNUSED_PRESERVE src0_sel:DWORD src1_sel:BYTE_3" : "+v"(r) : "s"(mask_3c), "v"(v));
+}
+
+typedef __attribute__((address_space(3))) float lds_f32_t;
+typedef __attribute__((address_space(3))) char lds_char_t;
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(1))) const void glb_void_t;
+
+// float at LDS byte address addr + imm (imm becomes the instruction's offset field)
+__device__ __forceinline__ float lds_f32(uint32_t addr, int imm)
+{
+    return reinterpret_cast<const lds_f32_t *>(static_cast<uintptr_t>(addr))[imm / 4];
+}
+
+// The 8 table addresses of one word (chunks 8i .. 8i+7 of the group); r[] keep the base.
+__device__ __forceinline__ void word_addrs(uint32_t w, uint32_t r[8], uint32_t mask_3c)
+{
+    const uint32_t l = w << 2, h = w >> 2;
+    nib_addr<0>(r[0], l, mask_3c); nib_addr<0>(r[1], h, mask_3c);
+    nib_addr<1>(r[2], l, mask_3c); nib_addr<1>(r[3], h, mask_3c);
+    nib_addr<2>(r[4], l, mask_3c); nib_addr<2>(r[5], h, mask_3c);
+    nib_addr<3>(r[6], l, mask_3c); nib_addr<3>(r[7], h, mask_3c);
+}
+
+constexpr int kLutBatch = 8;                        // groups per weight tile (128 B per row)
+constexpr int kLutTileBytes = 64 * kLutBatch * 16;  // 8 KB
+constexpr int kLutBytes = 32 * 16 * 4;              // 2 KB of tables per group
+
+__global__ __launch_bounds__(384) void q1_gemv_lut_kernel(const uint32_t *__restrict__ wbits,
+                                                          const uint16_t *__restrict__ scales,
+                                                          const uint16_t *__restrict__ x,
+                                                          float *__restrict__ y, int N, int K, int gps)
+{
+    constexpr int B = kLutBatch;
+    extern __shared__ u32x4 lds[];
+
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int nwaves = blockDim.x >> 6;
+    const int G = K >> 7;
+    const int row0 = blockIdx.x * 64;
+    const int row = row0 + lane;
+    const int g0 = wave * gps;
+    const int g1 = min(G, g0 + gps);
+
+    char *wl = reinterpret_cast<char *>(lds) + wave * (kLutTileBytes + kLutBytes);
+    char *tile = wl;
+    char *lut = wl + kLutTileBytes;
+    const u32x4 *wg = reinterpret_cast<const u32x4 *>(wbits);      // (row n, group g) at n * G + g
+    const uint16_t *srow = scales + (size_t)min(row, N - 1) * G;
+    const uint32_t mask_3c = __builtin_amdgcn_readfirstlane(0x3Cu);
+    const uint32_t lut_addr = (uint32_t)(uintptr_t)((lds_char_t *)lut);
+    uint32_t raddr[16];
+#pragma unroll
+    for (int j = 0; j < 16; ++j) raddr[j] = lut_addr;
+
+    // table build: this lane writes entries 4*bt .. 4*bt+3 of chunks bc and bc + 16
+    const int bc = lane >> 2, bt = lane & 3;
+    const float sg2 = (bt & 1) ? 1.f : -1.f, sg3 = (bt & 2) ? 1.f : -1.f;
+    uint2 xq0 = *reinterpret_cast<const uint2 *>(x + (size_t)g0 * 128 + 4 * bc);
+    uint2 xq1 = *reinterpret_cast<const uint2 *>(x + (size_t)g0 * 128 + 4 * (bc + 16));
+
+    // tile load: instruction i fetches row 8i + lane/8, group (lane%8) ^ ((row >> 1) & 7)
+    float sc[B];
+    auto issue = [&](int gb) {
+#pragma unroll
+        for (int i = 0; i < B; ++i) {
+            const int r = 8 * i + (lane >> 3);
+            const int gg = min(gb + ((lane & 7) ^ ((r >> 1) & 7)), g1 - 1);
+            const int rr = min(row0 + r, N - 1);
+            __builtin_amdgcn_global_load_lds((glb_void_t *)(wg + (size_t)rr * G + gg),
+                                             (lds_void_t *)(tile + i * 1024), 16, 0, 0);
+        }
+#pragma unroll
+        for (int u = 0; u < B; ++u) sc[u] = f16_bits_to_f32(srow[min(gb + u, g1 - 1)]);
+    };
+
+    float acc = 0.f;
+    issue(g0);
+    for (int gb = g0; gb < g1; gb += B) {
+        __builtin_amdgcn_s_waitcnt(0x0F70);             // vmcnt(0): tile and scales of this batch
+#pragma unroll
+        for (int u = 0; u < B; ++u) {
+            const int g = gb + u;
+            if (g >= g1) break;
+            // build the 32 tables of group g, then fetch the next group's x
+            const uint2 xc[2] = {xq0, xq1};
+            if (g + 1 < g1) {
+                xq0 = *reinterpret_cast<const uint2 *>(x + (size_t)(g + 1) * 128 + 4 * bc);
+                xq1 = *reinterpret_cast<const uint2 *>(x + (size_t)(g + 1) * 128 + 4 * (bc + 16));
+            }
+#pragma unroll
+            for (int hq = 0; hq < 2; ++hq) {
+                const half2_t p01 = as_half2(xc[hq].x), p23 = as_half2(xc[hq].y);
+                const float x0 = (float)p01[0], x1 = (float)p01[1];
+                const float base = fmaf(sg3, (float)p23[1], fmaf(sg2, (float)p23[0], -x0 - x1));
+                u32x4 e;
+                e[0] = __builtin_bit_cast(uint32_t, base);                                  // v = 4bt
+                e[1] = __builtin_bit_cast(uint32_t, fmaf(2.f, x0, base));                  // v = 4bt + 1
+                e[2] = __builtin_bit_cast(uint32_t, fmaf(2.f, x1, base));                  // v = 4bt + 2
+                e[3] = __builtin_bit_cast(uint32_t, fmaf(2.f, x1, fmaf(2.f, x0, base)));   // v = 4bt + 3
+                *reinterpret_cast<u32x4 *>(lut + 64 * (bc + 16 * hq) + 16 * bt) = e;
+            }
+            // this lane's row: 4 words x 8 nibbles, two words (16 reads) in flight at a time
+            const u32x4 q = *reinterpret_cast<const u32x4 *>(tile + 128 * lane + 16 * (u ^ ((lane >> 1) & 7)));
+            float a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;
+#pragma unroll
+            for (int i = 0; i < 4; i += 2) {
+                word_addrs(q[i], &raddr[0], mask_3c);          // in place: only bits 0..7 change
+                word_addrs(q[i + 1], &raddr[8], mask_3c);
+                float t[16];
+#pragma unroll
+                for (int j = 0; j < 16; ++j) t[j] = lds_f32(raddr[j], 64 * (8 * i + j));
+                a0 += (t[0] + t[1]) + (t[2] + t[3]);
+                a1 += (t[4] + t[5]) + (t[6] + t[7]);
+                a2 += (t[8] + t[9]) + (t[10] + t[11]);
+                a3 += (t[12] + t[13]) + (t[14] + t[15]);
+            }
+            acc = fmaf(sc[u], (a0 + a1) + (a2 + a3), acc);
+        }
+        __builtin_amdgcn_s_waitcnt(0xC07F);             // lgkmcnt(0): tile reads done before reuse
+        if (gb + B < g1) issue(gb + B);
+    }
+
+    if (nwaves == 1) {
+        if (row < N) y[row] = acc;
+        return;
+    }
+    float *red = reinterpret_cast<float *>(reinterpret_cast<char *>(lds) + nwaves * (kLutTileBytes + kLutBytes));
+    red[wave * 64 + lane] = acc;
+    __syncthreads();
+    if (wave == 0 && row < N) {
+        float t = red[lane];
+        for (int w = 1; w < nwaves; ++w) t += red[w * 64 + lane];
+        y[row] = t;
+    }
+}
+
+hipError_t launch_lut(const uint32_t *wbits, const uint16_t *scales, const uint16_t *x, float *y,
+                      int N, int K, hipStream_t stream)
+{
+    const int G = K / 128;
+    const int tiles = (N + 63) / 64;
+    constexpr size_t per_wave = kLutTileBytes + kLutBytes;
+    // Split K across the waves of a workgroup only until the grid has a wave per SIMD
+    // (1024 SIMDs): the LDS each wave needs makes more, smaller waves a net loss.
+    int slices = 1;
+    while (slices < 6 && (int64_t)tiles * slices < 1024 && slices * kLutBatch < G) ++slices;
+    int gps = (G + slices - 1) / slices;
+    gps = ((gps + kLutBatch - 1) / kLutBatch) * kLutBatch;
+    slices = (G + gps - 1) / gps;
+    const size_t lds = (size_t)slices * per_wave + (slices > 1 ? (size_t)slices * 64 * sizeof(float) : 0);
+    void *args[] = {&wbits, &scales, &x, &y, &N, &K, &gps};
+    return launch_kernel(reinterpret_cast<const void *>(&q1_gemv_lut_kernel), dim3(tiles), dim3(64 * slices),
+                         args, lds, stream);
 }
 
 template <int M>
 hipError_t launch_m(const uint32_t *wbits, const uint16_t *scales, const uint16_t *x, float *y,
                     int N, int K, hipStream_t stream)
 {
-    const int G = K / 128;
-    const int tiles = (N + 63) / 64;
-    // Enough waves to cover the chip (1024 SIMDs) at least twice: split K across the waves
-    // of a workgroup when there are few row tiles.
-    int slices = 1;
-    if (tiles < 2048) slices = min(16, min(G, (2048 + tiles - 1) / tiles));
-    const int gps = (G + slices - 1) / slices;
-    slices = (G + gps - 1) / gps;
-    const size_t lds = slices > 1 ? (size_t)slices * M * 64 * sizeof(float) : 0;
-    void *args[] = {&wbits, &scales, &x, &y, &N, &K, (void *)&gps};
-    return launch_kernel(reinterpret_cast<const void *>(&q1_gemv_kernel<M>), dim3(tiles), dim3(64 * slices), args,
-                           lds, stream);
+    if constexpr (M == 1) return launch_lut(wbits, scales, x, y, N, K, stream);
+    return launch_mb<M, 4>(wbits, scales, x, y, N, K, stream);
 }
 
 }  // namespace
