@@ -142,6 +142,107 @@ def cpu_baseline(wA, sA, xA, wB, sB, xB, K, budget_s: float):
                       f"per second as in the GPU value"}
 
 
+# ---- rocprofv3 CSV summaries for profiles/ (host only, no GPU) ---------------------------
+def short_name(name: str) -> str:
+    name = name.replace("bonsai::(anonymous namespace)::", "").replace("bonsai::", "")
+    return name.split("(", 1)[0]
+
+
+def _csv_rows(d: str, suffix: str):
+    import csv
+    import glob
+    files = sorted(glob.glob(os.path.join(d, "**", f"*{suffix}"), recursive=True))
+    if not files:
+        raise SystemExit(f"no *{suffix} under {d}")
+    rows = []
+    for f in files:
+        with open(f, newline="") as fh:
+            rows.extend(csv.DictReader(fh))
+    return rows
+
+
+def summarize_trace(d: str, out: str, cmds: list[str]) -> None:
+    """Per-kernel durations from a --kernel-trace --stats run: the stats table plus the mean
+    per (kernel, grid), which separates the shapes one kernel runs on."""
+    stats = _csv_rows(d, "_kernel_stats.csv")
+    trace = _csv_rows(d, "_kernel_trace.csv")
+    lines = [f"# rocprofv3 kernel trace: {out}", "# command:"] + [f"#   {c}" for c in cmds]
+    lines += ["# summarised by: python bench.py --summarize-trace <output dir> --out " + out, "",
+              "kernel | calls | average ns | min ns | max ns | share %", "---|---|---|---|---|---"]
+    for r in sorted(stats, key=lambda r: -float(r["TotalDurationNs"])):
+        lines.append(f"{short_name(r['Name'])} | {r['Calls']} | {float(r['AverageNs']):.1f} | {r['MinNs']} | "
+                     f"{r['MaxNs']} | {float(r['Percentage']):.2f}")
+    per = {}
+    for r in trace:
+        k = (short_name(r["Kernel_Name"]), int(r["Grid_Size_X"]), int(r["Workgroup_Size_X"]),
+             r["LDS_Block_Size"], r["VGPR_Count"], r["Accum_VGPR_Count"], r["Scratch_Size"])
+        per.setdefault(k, []).append(int(r["End_Timestamp"]) - int(r["Start_Timestamp"]))
+    lines += ["", "kernel | grid (threads) | workgroup | LDS B | VGPR | AGPR | scratch | calls | average ns",
+              "---|---|---|---|---|---|---|---|---"]
+    for k, v in sorted(per.items(), key=lambda kv: (kv[0][0], kv[0][1])):
+        if k[0].startswith("__amd"):
+            continue
+        lines.append(" | ".join(str(x) for x in k) + f" | {len(v)} | {sum(v) / len(v):.1f}")
+    (ROOT / "profiles" / out).write_text("\n".join(lines) + "\n")
+    print((ROOT / "profiles" / out).read_text())
+
+
+def summarize_pmc(fetch_dir: str, write_dir: str, out: str, cmds: list[str], kernel: str, src: str) -> None:
+    """HBM bytes per launch of `kernel` from a FETCH_SIZE run and a WRITE_SIZE run (KiB per
+    dispatch), each scaled by what the counter reads for the 1 GiB device copy of the copy
+    probe (1 GiB read, 1 GiB written)."""
+    def per_dispatch(d, counter):
+        acc = {}
+        for r in _csv_rows(d, "_counter_collection.csv"):
+            if r["Counter_Name"] != counter:
+                continue
+            key = (r["Dispatch_Id"], short_name(r["Kernel_Name"]), int(r["Grid_Size"]))
+            acc[key] = acc.get(key, 0.0) + float(r["Counter_Value"])
+        return acc
+    f, w = per_dispatch(fetch_dir, "FETCH_SIZE"), per_dispatch(write_dir, "WRITE_SIZE")
+
+    def copy_kib(acc):
+        # the copy probe's dispatches are the largest copies of the run (the weight clones
+        # before them move a few MB each)
+        cp = [v for (_, n, _), v in acc.items() if n.startswith("__amd_rocclr_copyBuffer")]
+        top = max(cp)
+        vals = sorted(v for v in cp if v >= 0.9 * top)
+        return vals[len(vals) // 2], len(vals)
+    cf, ncf = copy_kib(f)
+    cw, ncw = copy_kib(w)
+    gib_kib = float(1 << 20)
+    sf, sw = gib_kib / cf, gib_kib / cw
+
+    def kern(acc):
+        by = {}
+        for (_, n, g), v in acc.items():
+            if n == kernel:
+                by.setdefault(g, []).append(v)
+        return by
+    kf, kw = kern(f), kern(w)
+    lines = [f"# HBM traffic per launch of {kernel} ({out})", "# commands:"] + [f"#   {c}" for c in cmds]
+    lines += [f"# summarised by: python bench.py --summarize-pmc <fetch dir> <write dir> --out {out}",
+              "# Counters are KiB per dispatch; each is scaled by 1 GiB over what it reads for the copy",
+              "# probe's 1 GiB device-to-device copy (median over its dispatches).", "",
+              f"kernel: {kernel}",
+              f"kernel_source_sha256_16: {src_digest(ROOT / src)}",
+              f"copy_kernel: __amd_rocclr_copyBuffer, the {ncf} (fetch run) / {ncw} (write run) 1 GiB copies",
+              f"copy_fetch_kib: {cf:.1f}", f"copy_write_kib: {cw:.1f}",
+              f"fetch_scale: {sf:.4f}", f"write_scale: {sw:.4f}", ""]
+    tot, n = 0.0, 0
+    for g in sorted(kf):
+        mf = sum(kf[g]) / len(kf[g])
+        mw = sum(kw.get(g, [0.0])) / max(1, len(kw.get(g, [])))
+        b = (mf * sf + mw * sw) * 1024.0
+        lines.append(f"grid {g}: {len(kf[g])} dispatches, FETCH_SIZE {mf:.1f} KiB, WRITE_SIZE {mw:.1f} KiB, "
+                     f"scaled {b:.0f} B")
+        tot += b * len(kf[g])
+        n += len(kf[g])
+    lines += ["", f"hbm_bytes_per_launch: {tot / n:.0f}"]
+    (ROOT / "profiles" / out).write_text("\n".join(lines) + "\n")
+    print((ROOT / "profiles" / out).read_text())
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -150,7 +251,19 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--headline-only", action="store_true", help="skip the secondary measurements")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--summarize-trace", metavar="DIR", help="write a profiles/ summary of a kernel-trace run")
+    ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="write the profiles/ HBM-traffic summary of the decode GEMV from two --pmc runs")
+    ap.add_argument("--out", help="file name under profiles/ for --summarize-*")
+    ap.add_argument("--cmd", action="append", default=[], help="profiler command recorded in the summary")
     args = ap.parse_args()
+    if args.summarize_trace:
+        summarize_trace(args.summarize_trace, args.out, args.cmd)
+        return 0
+    if args.summarize_pmc:
+        summarize_pmc(*args.summarize_pmc, args.out, args.cmd, "q1_gemv_lut_kernel",
+                      "ternary_weight_quantized_bonsai_amd/csrc/q1_gemv.hip")
+        return 0
     if args.gpus != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path (the GEMV shards by "
               "rows with no collective; see the design notes). Run with --gpus 1.", file=sys.stderr)
@@ -233,10 +346,10 @@ def main() -> int:
     per_launch_ms = float(np.mean(kt))
     achieved = per_launch_bytes / (per_launch_ms / 1e3) / 1e9
     digest = src_digest(ROOT / "ternary_weight_quantized_bonsai_amd" / "csrc" / "q1_gemv.hip")
-    traffic = read_pmc("q1_gemv_decode_pair_pmc.txt", digest)
+    traffic = read_pmc("q1_gemv_lut_kernel_decode_pair_hbm_traffic.txt", digest)
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                 "frac": round(achieved / PEAK_HBM_GBPS, 4), "traffic": traffic,
-                "kernel": "q1_gemv_kernel<1>", "avg_launch_us": round(per_launch_ms * 1e3, 3),
+                "kernel": "q1_gemv_lut_kernel", "avg_launch_us": round(per_launch_ms * 1e3, 3),
                 "bytes_per_launch": per_launch_bytes,
                 "per_shape_us": {"mlp_13824x5120": round(t_mlp * 1e3, 3), "attn_5120x5120": round(t_attn * 1e3, 3)}}
     log(f"q1_gemv device time: mlp {t_mlp * 1e3:.2f} us, attn {t_attn * 1e3:.2f} us -> {achieved:.1f} GB/s")
@@ -298,21 +411,23 @@ def main() -> int:
             del ws, ss, w, s, x, y
         extra["ternary_gemv"] = {"shape": "N=5120 K=5120", **tern}
 
-        # Device copy probe: what a plain copy kernel reaches on this machine (read + write bytes)
-        nbytes = 1 << 30
-        a = torch.empty(nbytes // 4, dtype=torch.float32, device=dev)
-        b = torch.empty_like(a)
+    # Device copy probe: what a plain 1 GiB copy reaches on this machine (read + write bytes); its
+    # dispatches also calibrate the HBM byte counters of the traffic summary
+    nbytes = 1 << 30
+    a = torch.empty(nbytes // 4, dtype=torch.float32, device=dev)
+    b = torch.empty_like(a)
+    b.copy_(a)
+    torch.cuda.synchronize()
+    c0, c1 = hip.event(), hip.event()
+    hip.record(c0, stream())
+    for _ in range(10):
         b.copy_(a)
-        torch.cuda.synchronize()
-        c0, c1 = hip.event(), hip.event()
-        hip.record(c0, stream())
-        for _ in range(10):
-            b.copy_(a)
-        hip.record(c1, stream())
-        tc = hip.elapsed_ms(c0, c1) / 10
-        extra["copy_probe"] = {"bytes_moved": 2 * nbytes, "GBps": round(2 * nbytes / (tc / 1e3) / 1e9, 1)}
-        log(f"copy probe: {2 * nbytes / (tc / 1e3) / 1e9:.1f} GB/s")
-        del a, b
+    hip.record(c1, stream())
+    tc = hip.elapsed_ms(c0, c1) / 10
+    copy_probe = {"bytes_moved": 2 * nbytes, "GBps": round(2 * nbytes / (tc / 1e3) / 1e9, 1)}
+    log(f"copy probe: {2 * nbytes / (tc / 1e3) / 1e9:.1f} GB/s")
+    del a, b
+
 
     line = {
         "metric": "Binary g128 GEMV packed-weight GB/s (% HBM peak); PP512 GEMM TFLOP/s",
@@ -333,6 +448,7 @@ def main() -> int:
                    "timed_as": "HIP graph replay of the steps, HIP events on the launch stream"},
         "roofline": roofline,
     }
+    line["copy_probe"] = copy_probe
     line.update(extra)
     if not args.no_cpu_baseline:
         log("timing the CPU oracle")
