@@ -7,12 +7,30 @@
 // sign bit flipped), so the group scale is folded into the operand and one accumulator set
 // runs across all groups.  No FP16 copy of W is written anywhere.
 //
-// Tiling.  A workgroup of 4 waves computes a 128 (M) x 256 (N) tile; wave w owns columns
-// 64w .. 64w+63 of it, all 128 rows, as 4 x 2 MFMA tiles of 32 x 32.  K advances 64 at a
-// time.  The X tile (128 rows x 128 B) is staged in LDS by direct global->LDS loads, double
-// buffered, with the 16-byte chunk c of row r stored at 128 r + 16 (c ^ ((r >> 1) & 7)) so
-// the MFMA A-operand reads (32 rows, one 16-byte chunk each) are free of bank conflicts.
-// Each lane reads its two columns' sign words straight into registers.
+// Tiling.  A workgroup of 4 waves (one per SIMD) computes a 128 (M) x 256 (N) tile; wave w
+// owns columns 64w .. 64w+63 of it, all 128 rows, as 4 x 2 MFMA tiles of 32 x 32.  K advances
+// 64 per step.
+//
+// Operand staging.
+//  * X: 128 rows x 128 B per step, copied into a 4-deep LDS ring by direct global->LDS loads
+//    (8 rows x 128 B per instruction), the 16-byte chunk c of row r stored at
+//    128 r + 16 (c ^ ((r >> 1) & 7)) so the A-operand reads are free of bank conflicts.
+//  * W: each lane keeps its two columns' sign words and scales in registers, one 512-k chunk
+//    (64 B of words, 4 scales per column) at a time.  The next chunk is fetched during the
+//    current one with 16-byte loads (each lane reads its own column's bytes, so a load touches
+//    whole lines that the next three loads reuse), and the two lane halves exchange their
+//    columns with v_permlane32_swap.
+//
+// Pipeline.  Within a step, the A fragments and the expanded B fragments of the next k16
+// slice are produced while the 8 MFMAs of the current one run; sched_group_barrier interleaves
+// them (MFMA, LDS read, VALU, ...) so the matrix core stays busy.  Once per step, between the
+// third and fourth k16 slice, each wave waits for its own copies of the next X stage
+// (s_waitcnt with an exact count of the loads issued after them), a bare s_barrier makes all
+// waves' copies visible (__syncthreads would also drain every later stage), the stage three
+// steps ahead is issued into the slot just freed, and the last slice runs while the first
+// operands of the next step are fetched.  Every step issues the same loads (clamped to the
+// last chunk and stage near the end, into buffers no longer read), so the counts hold on every
+// path; steps past K in the last chunk skip only their arithmetic.
 //
 // Sign expansion in natural k order.  An MFMA lane holds 8 consecutive k of its operand as 4
 // half pairs (k, k+1).  Merging a word with itself shifted (u = bits 0..15 | bits 1..16 in the
@@ -29,23 +47,37 @@ namespace bonsai {
 namespace {
 
 constexpr int BM = 128, BN = 256, BK = 64;
-constexpr int XTILE = BM * BK * 2;               // 16 KB per buffer
+constexpr int NS = 4;                           // X stages in the LDS ring
+constexpr int XTILE = BM * BK * 2;              // 16 KB per stage
+constexpr int CH = 8;                           // K-steps per register chunk of sign words (512 k)
 
 typedef float float16_t __attribute__((ext_vector_type(16)));
 typedef __attribute__((address_space(3))) void lds_void_t;
 typedef __attribute__((address_space(1))) const void glb_void_t;
 
-// 4 dwords (k = p .. p+7 of a 16-k half-word) of +-s from the merged word v, whose bits q and
-// 16+q hold k = q and q+1 of that half-word; c = (-s, -s).
-__device__ __forceinline__ half8_t expand8(uint32_t v, int p, uint32_t c)
+// s_waitcnt vmcnt(n) (fields: vmcnt [3:0] and [15:14], expcnt [6:4], lgkmcnt [11:8])
+template <int n>
+__device__ __forceinline__ void wait_vmcnt()
 {
-    u32x4 e;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) e[i] = ((v << (15 - (p + 2 * i))) & 0x80008000u) ^ c;
-    return __builtin_bit_cast(half8_t, e);
+    __builtin_amdgcn_s_waitcnt((n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
-constexpr int NS = 4;                            // pipeline depth (X tiles in LDS, B words in registers)
+// sched_group_barrier masks
+constexpr int SG_MFMA = 0x008, SG_VALU = 0x002, SG_DS_READ = 0x100;
+
+// 8 halves (+-s) of the k16 slice s of one 64-k step: w is the word holding it, q selects
+// k 0..7 or 8..15 of the slice, cs = (-s, -s)
+__device__ __forceinline__ half8_t expand8(uint32_t w, int s, int q, uint32_t cs)
+{
+    const uint32_t hi = 0xFFFF0000u;
+    const uint32_t v = (s & 1) ? (((w >> 1) & hi) | (((w >> 16) | (w << 16)) & ~hi))
+                               : (((w << 15) & hi) | (w & ~hi));
+    const int p = 8 * q;
+    u32x4 e;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) e[i] = ((v << (15 - (p + 2 * i))) & 0x80008000u) ^ cs;
+    return __builtin_bit_cast(half8_t, e);
+}
 
 __global__ __launch_bounds__(256) void q1_gemm_kernel(const uint32_t *__restrict__ wbits,
                                                       const uint16_t *__restrict__ scales,
@@ -55,12 +87,14 @@ __global__ __launch_bounds__(256) void q1_gemm_kernel(const uint32_t *__restrict
     __shared__ __attribute__((aligned(16))) char xs[NS * XTILE];
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int q = lane >> 5, l32 = lane & 31;
     const int tiles_n = (N + BN - 1) / BN;
     const int m0 = (blockIdx.x / tiles_n) * BM, n0 = (blockIdx.x % tiles_n) * BN;
-    const int G = K >> 7, W = K >> 5;
+    const int G = K >> 7;                       // groups per row = 16-byte units of sign words per row
     const int KT = K / BK;
+    const int nchunks = (KT + CH - 1) / CH;
 
-    // X staging: this wave issues instructions 4 wave .. 4 wave + 3 of the tile's 16
+    // X staging: this wave issues instructions 4 wave .. 4 wave + 3 of a stage's 16
     // (8 rows x 128 B each): lane -> row 8i + lane/8, chunk (lane%8) ^ ((row >> 1) & 7)
     const u32x4 *xg = reinterpret_cast<const u32x4 *>(x);           // row m, chunk c at m * (K/8) + c
     size_t xsrc[4];
@@ -71,14 +105,42 @@ __global__ __launch_bounds__(256) void q1_gemm_kernel(const uint32_t *__restrict
         xsrc[j] = (size_t)min(m0 + r, M - 1) * (K >> 3) + c;
     }
 
-    // B: this lane's columns n0 + 64 wave + (lane % 32) + 32 t, t = 0, 1; its k-block lane / 32
-    const int q = lane >> 5;
-    int ncol[2];
+    // W: this lane fetches column 64 wave + 32 q + l32 (its MFMA column t = q); the swap
+    // with the other lane half supplies column t = 1 - q
+    const int ncol = min(n0 + 64 * wave + 32 * q + l32, N - 1);
+    const u32x4 *wrow = reinterpret_cast<const u32x4 *>(wbits) + (size_t)ncol * G;
+    const uint16_t *srow = scales + (size_t)ncol * G;
+    u32x4 rw[4];                                 // next chunk, own column: 16 words
+    uint32_t rs[4];                              // next chunk, own column: 4 scales
+    uint32_t cw[2][16], csc[2][4];               // current chunk, columns t = 0, 1
+
+    auto issue_x = [&](int kt, int slot) {
 #pragma unroll
-    for (int t = 0; t < 2; ++t) ncol[t] = min(n0 + 64 * wave + (lane & 31) + 32 * t, N - 1);
-    const uint2 *wrow[2] = {reinterpret_cast<const uint2 *>(wbits + (size_t)ncol[0] * W),
-                            reinterpret_cast<const uint2 *>(wbits + (size_t)ncol[1] * W)};
-    const uint16_t *srow[2] = {scales + (size_t)ncol[0] * G, scales + (size_t)ncol[1] * G};
+        for (int j = 0; j < 4; ++j)
+            __builtin_amdgcn_global_load_lds((glb_void_t *)(xg + xsrc[j] + kt * (BK / 8)),
+                                             (lds_void_t *)(xs + slot * XTILE + (4 * wave + j) * 1024), 16, 0, 0);
+    };
+    // piece i (0..3) of chunk cc: 16 bytes of sign words and one scale
+    auto issue_c = [&](int cc, int i) {
+        rw[i] = wrow[min(cc * 4 + i, G - 1)];
+        rs[i] = srow[min(cc * 4 + i, G - 1)];
+    };
+    auto swap_in = [&]() {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const auto r = __builtin_amdgcn_permlane32_swap(rw[i][e], rw[i][e], false, false);
+                cw[0][4 * i + e] = r[0];        // the value of lanes 0..31: column t = 0
+                cw[1][4 * i + e] = r[1];        // lanes 32..63: column t = 1
+            }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const auto r = __builtin_amdgcn_permlane32_swap(rs[i], rs[i], false, false);
+            csc[0][i] = ((r[0] & 0xFFFFu) | (r[0] << 16)) ^ 0x80008000u;   // (-s, -s)
+            csc[1][i] = ((r[1] & 0xFFFFu) | (r[1] << 16)) ^ 0x80008000u;
+        }
+    };
 
     float16_t acc[4][2];
 #pragma unroll
@@ -88,97 +150,112 @@ __global__ __launch_bounds__(256) void q1_gemm_kernel(const uint32_t *__restrict
 #pragma unroll
             for (int i = 0; i < 16; ++i) acc[a][b][i] = 0.f;
 
-    // One pipeline stage = 8 VMEM instructions per wave: 4 X DMAs, 2 B word pairs, 2 scales.
-    uint2 wd[NS][2];
-    uint32_t sb[NS][2];
-    auto issue = [&](int kt, auto slot_c) {
-        constexpr int slot = decltype(slot_c)::value;
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-            __builtin_amdgcn_global_load_lds((glb_void_t *)(xg + xsrc[j] + kt * (BK / 8)),
-                                             (lds_void_t *)(xs + slot * XTILE + (4 * wave + j) * 1024), 16, 0, 0);
-#pragma unroll
-        for (int t = 0; t < 2; ++t) {
-            wd[slot][t] = wrow[t][kt];
-            sb[slot][t] = srow[t][kt >> 1];
-        }
-    };
+    half8_t af[2][4], bf[2][2];                  // operands of the current / next k16 slice
+    uint32_t wcur[2][2], cs[2];                  // sign words and (-s, -s) of the step being expanded
 
-    auto compute = [&](auto slot_c) {
-        constexpr int slot = decltype(slot_c)::value;
+    auto read_a = [&](int slot, int s, int buf) {
         const char *xb = xs + slot * XTILE;
-        uint32_t cs[2];
-#pragma unroll
-        for (int t = 0; t < 2; ++t) cs[t] = (sb[slot][t] | (sb[slot][t] << 16)) ^ 0x80008000u;   // (-s, -s)
-        half8_t af[2][4];
 #pragma unroll
         for (int mt = 0; mt < 4; ++mt) {
-            const int r = 32 * mt + (lane & 31);
-            af[0][mt] = *reinterpret_cast<const half8_t *>(xb + 128 * r + 16 * (q ^ ((r >> 1) & 7)));
+            const int r = 32 * mt + l32;
+            const int c = 2 * s + q;
+            af[buf][mt] = *reinterpret_cast<const half8_t *>(xb + 128 * r + 16 * (c ^ ((r >> 1) & 7)));
         }
+    };
+    auto read_w = [&](int j) {                   // step j of the current chunk
 #pragma unroll
-        for (int s = 0; s < 4; ++s) {                // k16 steps: word s/2, half s%2
-            if (s + 1 < 4) {                         // next k16 step's A fragments
+        for (int t = 0; t < 2; ++t) {
+            wcur[t][0] = cw[t][2 * j];
+            wcur[t][1] = cw[t][2 * j + 1];
+            cs[t] = csc[t][j >> 1];
+        }
+    };
+    auto make_b = [&](int s, int buf) {
 #pragma unroll
-                for (int mt = 0; mt < 4; ++mt) {
-                    const int r = 32 * mt + (lane & 31);
-                    const int c = 2 * (s + 1) + q;
-                    af[(s + 1) & 1][mt] = *reinterpret_cast<const half8_t *>(xb + 128 * r + 16 * (c ^ ((r >> 1) & 7)));
+        for (int t = 0; t < 2; ++t) bf[buf][t] = expand8(wcur[t][s >> 1], s, q, cs[t]);
+    };
+    auto mfma8 = [&](int buf) {
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+            for (int t = 0; t < 2; ++t)
+                acc[mt][t] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[buf][mt], bf[buf][t], acc[mt][t], 0, 0, 0);
+    };
+
+    // prologue: chunk 0 and X stages 0 .. NS - 2
+#pragma unroll
+    for (int i = 0; i < 4; ++i) issue_c(0, i);
+#pragma unroll
+    for (int st = 0; st < NS - 1; ++st) issue_x(min(st, KT - 1), st);
+    swap_in();
+    wait_vmcnt<4 * (NS - 2)>();                 // stage 0 landed
+    asm volatile("s_barrier" ::: "memory");
+    read_w(0);
+    read_a(0, 0, 0);
+    make_b(0, 0);
+
+    for (int cc = 0; cc < nchunks; ++cc) {
+        const int cn = min(cc + 1, nchunks - 1);
+        auto step = [&](auto jc) {
+            constexpr int j = decltype(jc)::value;
+            constexpr int slot = j % NS;
+            const int kt = cc * CH + j;
+            const bool live = kt < KT;
+            // k16 slices 0..2: operands of slice s + 1 are fetched / expanded under the MFMAs of s
+            if (live) {
+#pragma unroll
+                for (int s = 0; s < 3; ++s) {
+                    read_a(slot, s + 1, (s + 1) & 1);
+                    make_b(s + 1, (s + 1) & 1);
+                    mfma8(s & 1);
+#pragma unroll
+                    for (int i = 0; i < 8; ++i) {
+                        __builtin_amdgcn_sched_group_barrier(SG_MFMA, 1, 0);
+                        if (i < 4) __builtin_amdgcn_sched_group_barrier(SG_DS_READ, 1, 0);
+                        __builtin_amdgcn_sched_group_barrier(SG_VALU, 3, 0);
+                    }
+                    __builtin_amdgcn_sched_barrier(0);
                 }
             }
-            half8_t bf[2];
+            // Stage kt + 1 has landed once only the loads issued after it are outstanding:
+            // stage kt + 2 (4) plus, if the previous step was 0..3 of its chunk, two pieces.
+            wait_vmcnt<(j >= 1 && j <= 4) ? 6 : 4>();
+            asm volatile("s_barrier" ::: "memory");
+            if (j < 4) issue_c(cn, j);
+            issue_x(min(kt + NS - 1, KT - 1), (slot + NS - 1) % NS);
+            // slice 3, with the first operands of step kt + 1 fetched under it
+            if (live) {
+                if (j == CH - 1) swap_in();
+                read_w((j + 1) % CH);
+                read_a((slot + 1) % NS, 0, 0);
+                mfma8(1);
+                make_b(0, 0);
 #pragma unroll
-            for (int t = 0; t < 2; ++t) {
-                const uint32_t w = (s >> 1) ? wd[slot][t].y : wd[slot][t].x;
-                const uint32_t hi = 0xFFFF0000u;
-                const uint32_t v = (s & 1) ? (((w >> 1) & hi) | (((w >> 16) | (w << 16)) & ~hi))
-                                           : (((w << 15) & hi) | (w & ~hi));
-                bf[t] = expand8(v, 8 * q, cs[t]);
+                for (int i = 0; i < 8; ++i) {
+                    __builtin_amdgcn_sched_group_barrier(SG_MFMA, 1, 0);
+                    if (i < 4) __builtin_amdgcn_sched_group_barrier(SG_DS_READ, 1, 0);
+                    if (i >= 1) __builtin_amdgcn_sched_group_barrier(SG_VALU, 4, 0);
+                }
+                __builtin_amdgcn_sched_barrier(0);
             }
-#pragma unroll
-            for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-                for (int t = 0; t < 2; ++t)
-                    acc[mt][t] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[s & 1][mt], bf[t], acc[mt][t], 0, 0, 0);
-        }
-    };
-
-    // Step kt: wait for stage kt (later stages may stay in flight), barrier (all waves' DMAs
-    // landed, all waves done with the slot about to be refilled), refill, compute.
-    auto step = [&](int kt, auto slot_c) {
-        constexpr int slot = decltype(slot_c)::value;
-        const int ahead = min(NS - 2, KT - 1 - kt);  // stages issued after stage kt
-        // s_waitcnt fields: vmcnt[3:0] and [15:14], expcnt[6:4], lgkmcnt[11:8]
-        if (ahead >= 2) __builtin_amdgcn_s_waitcnt(0x4F70);        // vmcnt(16)
-        else if (ahead == 1) __builtin_amdgcn_s_waitcnt(0x0F78);   // vmcnt(8)
-        else __builtin_amdgcn_s_waitcnt(0x0F70);                   // vmcnt(0)
-        // Workgroup barrier without the release fence __syncthreads() implies (which would
-        // drain every in-flight stage); the clobber keeps LDS accesses on their side of it.
-        asm volatile("s_barrier" ::: "memory");
-        if (kt + NS - 1 < KT) issue(kt + NS - 1, std::integral_constant<int, (slot + NS - 1) % NS>{});
-        compute(slot_c);
-    };
-
-#pragma unroll
-    for (int i = 0; i < NS - 1; ++i)
-        if (i < KT) {
-            if (i == 0) issue(0, std::integral_constant<int, 0>{});
-            if (i == 1) issue(1, std::integral_constant<int, 1>{});
-            if (i == 2) issue(2, std::integral_constant<int, 2>{});
-        }
-    for (int kt = 0; kt < KT; kt += NS) {
-        step(kt, std::integral_constant<int, 0>{});
-        if (kt + 1 < KT) step(kt + 1, std::integral_constant<int, 1>{});
-        if (kt + 2 < KT) step(kt + 2, std::integral_constant<int, 2>{});
-        if (kt + 3 < KT) step(kt + 3, std::integral_constant<int, 3>{});
+        };
+        step(std::integral_constant<int, 0>{});
+        step(std::integral_constant<int, 1>{});
+        step(std::integral_constant<int, 2>{});
+        step(std::integral_constant<int, 3>{});
+        step(std::integral_constant<int, 4>{});
+        step(std::integral_constant<int, 5>{});
+        step(std::integral_constant<int, 6>{});
+        step(std::integral_constant<int, 7>{});
     }
+    wait_vmcnt<0>();                            // no copy into LDS outlives the workgroup
 
     // D layout (32 x 32): lane holds column lane % 32, rows 8 (i / 4) + 4 (lane / 32) + i % 4
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
         for (int t = 0; t < 2; ++t) {
-            const int col = n0 + 64 * wave + 32 * t + (lane & 31);
+            const int col = n0 + 64 * wave + 32 * t + l32;
             if (col >= N) continue;
 #pragma unroll
             for (int i = 0; i < 16; ++i) {
@@ -194,7 +271,7 @@ hipError_t launch_q1_gemm(const uint32_t *wbits, const uint16_t *scales, const u
                           int M, int N, int K, hipStream_t stream)
 {
     const int64_t tiles = (int64_t)((N + BN - 1) / BN) * ((M + BM - 1) / BM);
-    if (tiles > INT_MAX || K % BK != 0) return hipErrorInvalidValue;
+    if (tiles > INT_MAX || K % 128 != 0 || K <= 0) return hipErrorInvalidValue;
     void *args[] = {&wbits, &scales, &x, &y, &M, &N, &K};
     return launch_kernel(reinterpret_cast<const void *>(&q1_gemm_kernel), dim3((unsigned)tiles), dim3(256),
                          args, 0, stream);
