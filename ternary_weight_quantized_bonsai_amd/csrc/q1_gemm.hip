@@ -15,11 +15,14 @@
 //  * X: 128 rows x 128 B per step, copied into a 4-deep LDS ring by direct global->LDS loads
 //    (8 rows x 128 B per instruction), the 16-byte chunk c of row r stored at
 //    128 r + 16 (c ^ ((r >> 1) & 7)) so the A-operand reads are free of bank conflicts.
-//  * W: each lane keeps its two columns' sign words and scales in registers, one 512-k chunk
-//    (64 B of words, 4 scales per column) at a time.  The next chunk is fetched during the
-//    current one with 16-byte loads (each lane reads its own column's bytes, so a load touches
-//    whole lines that the next three loads reuse), and the two lane halves exchange their
-//    columns with v_permlane32_swap.
+//  * W: sign words and scales travel in 1024-k chunks (128 B of words and 8 scales per
+//    column), double buffered in LDS and copied one chunk ahead by direct global->LDS loads:
+//    8 columns x 128 B per instruction (whole lines), and the scales either as one 16-byte copy
+//    per column (K a multiple of 1024) or one 2-byte copy per column and group.  Cell u (steps
+//    2u, 2u+1) of column c sits at 128 c + 16 (u ^ ((c >> 1) & 7)).  A lane reads its two
+//    columns' cell every other step in a small asm block that also waits for it: these reads
+//    are ordered against the copies by the barriers, and keeping them out of the compiler's
+//    view keeps its conservative copy-versus-read waits off the A-operand reads.
 //
 // Pipeline.  Within a step, the A fragments and the expanded B fragments of the next k16
 // slice are produced while the 8 MFMAs of the current one run; sched_group_barrier interleaves
@@ -49,7 +52,10 @@ namespace {
 constexpr int BM = 128, BN = 256, BK = 64;
 constexpr int NS = 4;                           // X stages in the LDS ring
 constexpr int XTILE = BM * BK * 2;              // 16 KB per stage
-constexpr int CH = 8;                           // K-steps per register chunk of sign words (512 k)
+constexpr int CH = 16;                          // K-steps per LDS chunk of sign words (1024 k)
+constexpr int WCH = BN * CH * BK / 8;           // 32 KB of sign words per chunk
+constexpr int SCH = BN * 32;                    // 8 KB of scales per chunk (room for one dword per scale)
+constexpr int LDS_BYTES = NS * XTILE + 2 * WCH + 2 * SCH;   // 144 KB
 
 typedef float float16_t __attribute__((ext_vector_type(16)));
 typedef __attribute__((address_space(3))) void lds_void_t;
@@ -79,12 +85,19 @@ __device__ __forceinline__ half8_t expand8(uint32_t w, int s, int q, uint32_t cs
     return __builtin_bit_cast(half8_t, e);
 }
 
+// SMODE 16: one 16-byte scale copy per column and chunk (needs K % 1024 == 0); SMODE 2: one
+// 2-byte copy per column and group, landing in the low half of a dword.
+template <int SMODE>
 __global__ __launch_bounds__(256) void q1_gemm_kernel(const uint32_t *__restrict__ wbits,
                                                       const uint16_t *__restrict__ scales,
                                                       const uint16_t *__restrict__ x,
                                                       float *__restrict__ y, int M, int N, int K)
 {
-    __shared__ __attribute__((aligned(16))) char xs[NS * XTILE];
+    // One LDS object (X ring, sign-word chunks, scale chunks): with a single object the
+    // compiler's copy-versus-read waits stay off the A-operand reads of the ring.
+    __shared__ __attribute__((aligned(16))) char xs[LDS_BYTES];
+    char *const wls = xs + NS * XTILE;
+    char *const sls = wls + 2 * WCH;
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int q = lane >> 5, l32 = lane & 31;
@@ -105,14 +118,17 @@ __global__ __launch_bounds__(256) void q1_gemm_kernel(const uint32_t *__restrict
         xsrc[j] = (size_t)min(m0 + r, M - 1) * (K >> 3) + c;
     }
 
-    // W: this lane fetches column 64 wave + 32 q + l32 (its MFMA column t = q); the swap
-    // with the other lane half supplies column t = 1 - q
-    const int ncol = min(n0 + 64 * wave + 32 * q + l32, N - 1);
-    const u32x4 *wrow = reinterpret_cast<const u32x4 *>(wbits) + (size_t)ncol * G;
-    const uint16_t *srow = scales + (size_t)ncol * G;
-    u32x4 rw[4];                                 // next chunk, own column: 16 words
-    uint32_t rs[4];                              // next chunk, own column: 4 scales
-    uint32_t cw[2][16], csc[2][4];               // current chunk, columns t = 0, 1
+    // W chunk copies: instruction i of this wave covers columns 64 wave + 8 i .. +7, 128 B each;
+    // lane -> column 64 wave + 8 i + lane / 8, 16-byte piece (lane % 8) ^ ((column >> 1) & 7)
+    const u32x4 *wsrc[8];
+    int wu[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const int c = 64 * wave + 8 * i + (lane >> 3);
+        wu[i] = (lane & 7) ^ ((c >> 1) & 7);
+        wsrc[i] = reinterpret_cast<const u32x4 *>(wbits) + (size_t)min(n0 + c, N - 1) * G;
+    }
+    const uint16_t *ssrc = scales + (size_t)min(n0 + 64 * wave + lane, N - 1) * G;
 
     auto issue_x = [&](int kt, int slot) {
 #pragma unroll
@@ -120,26 +136,17 @@ __global__ __launch_bounds__(256) void q1_gemm_kernel(const uint32_t *__restrict
             __builtin_amdgcn_global_load_lds((glb_void_t *)(xg + xsrc[j] + kt * (BK / 8)),
                                              (lds_void_t *)(xs + slot * XTILE + (4 * wave + j) * 1024), 16, 0, 0);
     };
-    // piece i (0..3) of chunk cc: 16 bytes of sign words and one scale
-    auto issue_c = [&](int cc, int i) {
-        rw[i] = wrow[min(cc * 4 + i, G - 1)];
-        rs[i] = srow[min(cc * 4 + i, G - 1)];
+    auto issue_w = [&](int cc, int par, int i) {
+        __builtin_amdgcn_global_load_lds((glb_void_t *)(wsrc[i] + min(cc * 8 + wu[i], G - 1)),
+                                         (lds_void_t *)(wls + par * WCH + (64 * wave + 8 * i) * 128), 16, 0, 0);
     };
-    auto swap_in = [&]() {
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const auto r = __builtin_amdgcn_permlane32_swap(rw[i][e], rw[i][e], false, false);
-                cw[0][4 * i + e] = r[0];        // the value of lanes 0..31: column t = 0
-                cw[1][4 * i + e] = r[1];        // lanes 32..63: column t = 1
-            }
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const auto r = __builtin_amdgcn_permlane32_swap(rs[i], rs[i], false, false);
-            csc[0][i] = ((r[0] & 0xFFFFu) | (r[0] << 16)) ^ 0x80008000u;   // (-s, -s)
-            csc[1][i] = ((r[1] & 0xFFFFu) | (r[1] << 16)) ^ 0x80008000u;
-        }
+    auto issue_s = [&](int cc, int par, int g) {
+        if (SMODE == 16)     // the chunk's 8 scales of column 64 wave + lane
+            __builtin_amdgcn_global_load_lds((glb_void_t *)(ssrc + min(cc * 8, G - 8)),
+                                             (lds_void_t *)(sls + par * SCH + (64 * wave) * 16), 16, 0, 0);
+        else                 // group g of the chunk, one dword per column
+            __builtin_amdgcn_global_load_lds((glb_void_t *)(ssrc + min(cc * 8 + g, G - 1)),
+                                             (lds_void_t *)(sls + par * SCH + (g * 256 + 64 * wave) * 4), 2, 0, 0);
     };
 
     float16_t acc[4][2];
@@ -152,6 +159,9 @@ __global__ __launch_bounds__(256) void q1_gemm_kernel(const uint32_t *__restrict
 
     half8_t af[2][4], bf[2][2];                  // operands of the current / next k16 slice
     uint32_t wcur[2][2], cs[2];                  // sign words and (-s, -s) of the step being expanded
+    uint32_t wnxt[2][2];                         // words of the following step (second half of a cell)
+    const uint32_t wls_base = (uint32_t)(uintptr_t)((__attribute__((address_space(3))) char *)wls);
+    const uint32_t sls_base = (uint32_t)(uintptr_t)((__attribute__((address_space(3))) char *)sls);
 
     auto read_a = [&](int slot, int s, int buf) {
         const char *xb = xs + slot * XTILE;
@@ -162,12 +172,37 @@ __global__ __launch_bounds__(256) void q1_gemm_kernel(const uint32_t *__restrict
             af[buf][mt] = *reinterpret_cast<const half8_t *>(xb + 128 * r + 16 * (c ^ ((r >> 1) & 7)));
         }
     };
-    auto read_w = [&](int j) {                   // step j of the current chunk
+    // cell u of the chunk in buffer par: both columns' words for steps 2u, 2u + 1 and group u's
+    // scales, waited for inside the block
+    auto read_cell = [&](int par, int u) {
+        uint32_t aw[2], as[2];
 #pragma unroll
         for (int t = 0; t < 2; ++t) {
-            wcur[t][0] = cw[t][2 * j];
-            wcur[t][1] = cw[t][2 * j + 1];
-            cs[t] = csc[t][j >> 1];
+            const int c = 64 * wave + 32 * t + l32;
+            aw[t] = wls_base + par * WCH + c * 128 + 16 * (u ^ ((c >> 1) & 7));
+            as[t] = sls_base + par * SCH + (SMODE == 16 ? c * 16 + 2 * u : (u * 256 + c) * 4);
+        }
+        u32x4 w0, w1;
+        uint32_t s0, s1;
+        asm volatile("ds_read_b128 %0, %4\n\tds_read_b128 %1, %5\n\tds_read_u16 %2, %6\n\t"
+                     "ds_read_u16 %3, %7\n\ts_waitcnt lgkmcnt(0)"
+                     : "=v"(w0), "=v"(w1), "=v"(s0), "=v"(s1)
+                     : "v"(aw[0]), "v"(aw[1]), "v"(as[0]), "v"(as[1])
+                     : "memory");
+        wcur[0][0] = w0[0]; wcur[0][1] = w0[1]; wnxt[0][0] = w0[2]; wnxt[0][1] = w0[3];
+        wcur[1][0] = w1[0]; wcur[1][1] = w1[1]; wnxt[1][0] = w1[2]; wnxt[1][1] = w1[3];
+        cs[0] = (s0 | (s0 << 16)) ^ 0x80008000u;     // (-s, -s)
+        cs[1] = (s1 | (s1 << 16)) ^ 0x80008000u;
+    };
+    // words of step j of the chunk in buffer par: a cell read at even j, else its saved half
+    auto read_w = [&](int par, int j) {
+        if ((j & 1) == 0) read_cell(par, j >> 1);
+        else {
+#pragma unroll
+            for (int t = 0; t < 2; ++t) {
+                wcur[t][0] = wnxt[t][0];
+                wcur[t][1] = wnxt[t][1];
+            }
         }
     };
     auto make_b = [&](int s, int buf) {
@@ -184,18 +219,28 @@ __global__ __launch_bounds__(256) void q1_gemm_kernel(const uint32_t *__restrict
 
     // prologue: chunk 0 and X stages 0 .. NS - 2
 #pragma unroll
-    for (int i = 0; i < 4; ++i) issue_c(0, i);
+    for (int i = 0; i < 8; ++i) issue_w(0, 0, i);
+    if (SMODE == 16) {
+        issue_s(0, 0, 0);
+    } else {
+#pragma unroll
+        for (int g = 0; g < 8; ++g) issue_s(0, 0, g);
+    }
 #pragma unroll
     for (int st = 0; st < NS - 1; ++st) issue_x(min(st, KT - 1), st);
-    swap_in();
-    wait_vmcnt<4 * (NS - 2)>();                 // stage 0 landed
+    wait_vmcnt<4 * (NS - 2)>();                 // chunk 0 and stage 0 landed
     asm volatile("s_barrier" ::: "memory");
-    read_w(0);
+    read_w(0, 0);
     read_a(0, 0, 0);
     make_b(0, 0);
 
+    // Mid-step m issues stage m + 3 and then that position's chunk copies for the next chunk:
+    // sign-word instruction m (m < 8), then the scales (position 8, or one group at 8 .. 15).
+    // Every chunk does so (the last one re-copies itself into the idle buffer), so the number
+    // of copies issued after any stage is known at compile time.
     for (int cc = 0; cc < nchunks; ++cc) {
         const int cn = min(cc + 1, nchunks - 1);
+        const int par = cc & 1;
         auto step = [&](auto jc) {
             constexpr int j = decltype(jc)::value;
             constexpr int slot = j % NS;
@@ -217,16 +262,25 @@ __global__ __launch_bounds__(256) void q1_gemm_kernel(const uint32_t *__restrict
                     __builtin_amdgcn_sched_barrier(0);
                 }
             }
-            // Stage kt + 1 has landed once only the loads issued after it are outstanding:
-            // stage kt + 2 (4) plus, if the previous step was 0..3 of its chunk, two pieces.
-            wait_vmcnt<(j >= 1 && j <= 4) ? 6 : 4>();
+            // Stage kt + 1 has landed once only the copies issued after it are outstanding:
+            // mid-step kt - 2's chunk copies, then stage kt + 2 and mid-step kt - 1's.
+            constexpr int jm2 = (j + CH - 2) % CH, jm1 = (j + CH - 1) % CH;
+            constexpr int pm2 = jm2 < 8 ? 1 : (SMODE == 16 ? (jm2 == 8 ? 1 : 0) : 1);
+            constexpr int pm1 = jm1 < 8 ? 1 : (SMODE == 16 ? (jm1 == 8 ? 1 : 0) : 1);
+            if (j < 2 && cc == 0) {
+                if (j == 0) wait_vmcnt<4>();
+                else wait_vmcnt<4 + 1>();      // mid-step 0 issued stage 3, then sign-word copy 0
+            } else {
+                wait_vmcnt<pm2 + 4 + pm1>();
+            }
             asm volatile("s_barrier" ::: "memory");
-            if (j < 4) issue_c(cn, j);
             issue_x(min(kt + NS - 1, KT - 1), (slot + NS - 1) % NS);
+            if (j < 8) issue_w(cn, par ^ 1, j);
+            else if (SMODE == 16) { if (j == 8) issue_s(cn, par ^ 1, 0); }
+            else issue_s(cn, par ^ 1, j - 8);
             // slice 3, with the first operands of step kt + 1 fetched under it
             if (live) {
-                if (j == CH - 1) swap_in();
-                read_w((j + 1) % CH);
+                read_w(j == CH - 1 ? par ^ 1 : par, (j + 1) % CH);
                 read_a((slot + 1) % NS, 0, 0);
                 mfma8(1);
                 make_b(0, 0);
@@ -247,6 +301,14 @@ __global__ __launch_bounds__(256) void q1_gemm_kernel(const uint32_t *__restrict
         step(std::integral_constant<int, 5>{});
         step(std::integral_constant<int, 6>{});
         step(std::integral_constant<int, 7>{});
+        step(std::integral_constant<int, 8>{});
+        step(std::integral_constant<int, 9>{});
+        step(std::integral_constant<int, 10>{});
+        step(std::integral_constant<int, 11>{});
+        step(std::integral_constant<int, 12>{});
+        step(std::integral_constant<int, 13>{});
+        step(std::integral_constant<int, 14>{});
+        step(std::integral_constant<int, 15>{});
     }
     wait_vmcnt<0>();                            // no copy into LDS outlives the workgroup
 
@@ -273,8 +335,9 @@ hipError_t launch_q1_gemm(const uint32_t *wbits, const uint16_t *scales, const u
     const int64_t tiles = (int64_t)((N + BN - 1) / BN) * ((M + BM - 1) / BM);
     if (tiles > INT_MAX || K % 128 != 0 || K <= 0) return hipErrorInvalidValue;
     void *args[] = {&wbits, &scales, &x, &y, &M, &N, &K};
-    return launch_kernel(reinterpret_cast<const void *>(&q1_gemm_kernel), dim3((unsigned)tiles), dim3(256),
-                         args, 0, stream);
+    const void *fn = (K % 1024 == 0) ? reinterpret_cast<const void *>(&q1_gemm_kernel<16>)
+                                     : reinterpret_cast<const void *>(&q1_gemm_kernel<2>);
+    return launch_kernel(fn, dim3((unsigned)tiles), dim3(256), args, 0, stream);
 }
 
 }  // namespace bonsai

@@ -146,7 +146,7 @@ EDGE = {
     "q2t_gemv": [(1, 1, 128), (1, 63, 256), (2, 65, 384), (8, 1000, 1152), (7, 777, 2048),
                  (1, 130, 131072), (4, 4097, 640)],
     "q1_gemm": [(1, 1, 128), (17, 100, 256), (130, 257, 384), (128, 128, 512), (256, 384, 1024),
-                (5, 3000, 640), (300, 70, 2048), (16, 40, 131072)],
+                (5, 3000, 640), (300, 70, 2048), (16, 40, 131072), (64, 300, 1152), (200, 520, 3200)],
 }
 
 
