@@ -296,6 +296,7 @@ __global__ __launch_bounds__(384) void q1_gemv_lut_kernel(const uint32_t *__rest
     char *lut = wl + kLutTileBytes;
     const u32x4 *wg = reinterpret_cast<const u32x4 *>(wbits);      // (row n, group g) at n * G + g
     const uint16_t *srow = scales + (size_t)min(row, N - 1) * G;
+    const bool vec_scales = (G & 7) == 0;       // batches then start at multiples of 8 groups
     const uint32_t mask_3c = __builtin_amdgcn_readfirstlane(0x3Cu);
     const uint32_t lut_addr = (uint32_t)(uintptr_t)((lds_char_t *)lut);
     uint32_t raddr[16];
@@ -319,8 +320,16 @@ __global__ __launch_bounds__(384) void q1_gemv_lut_kernel(const uint32_t *__rest
             __builtin_amdgcn_global_load_lds((glb_void_t *)(wg + (size_t)rr * G + gg),
                                              (lds_void_t *)(tile + i * 1024), 16, 0, 0);
         }
+        if (vec_scales) {
+            // the batch's 8 scales of this row in one 16-byte load (K % 1024 == 0 keeps every
+            // row's scales and every batch start 16-byte aligned)
+            const u32x4 v = *reinterpret_cast<const u32x4 *>(srow + gb);
 #pragma unroll
-        for (int u = 0; u < B; ++u) sc[u] = f16_bits_to_f32(srow[min(gb + u, g1 - 1)]);
+            for (int u = 0; u < B; ++u) sc[u] = f16_bits_to_f32((uint16_t)(v[u >> 1] >> (16 * (u & 1))));
+        } else {
+#pragma unroll
+            for (int u = 0; u < B; ++u) sc[u] = f16_bits_to_f32(srow[min(gb + u, g1 - 1)]);
+        }
     };
 
     float acc = 0.f;
@@ -384,6 +393,141 @@ __global__ __launch_bounds__(384) void q1_gemv_lut_kernel(const uint32_t *__rest
     }
 }
 
+// Small N (at most 256 row tiles, one per CU): one 64-row tile per workgroup and one 4-group
+// K-slice per wave, so every wave has a single 4 KB copy and 128 lookups per lane after it
+// lands; the waves' partial sums meet in LDS in a fixed order.  A wave builds only its own 4
+// groups' tables, all at once (one wait), after its copy and x have arrived.
+constexpr int kL4Groups = 4;
+constexpr int kL4Tile = 64 * kL4Groups * 16;        // 4 KB: 64 rows x 4 groups
+constexpr int kL4Lut = kL4Groups * kLutBytes;       // 8 KB of tables
+constexpr int kL4Wave = kL4Tile + kL4Lut + 64 * 4;  // + this wave's partial sums
+constexpr int kL4MaxWaves = 13;                     // 13 x 12.25 KB fits the 160 KB of LDS
+
+template <bool VEC_SCALES>
+__global__ __launch_bounds__(kL4MaxWaves * 64) void q1_gemv_lut4_kernel(const uint32_t *__restrict__ wbits,
+                                                                        const uint16_t *__restrict__ scales,
+                                                                        const uint16_t *__restrict__ x,
+                                                                        float *__restrict__ y, int N, int K)
+{
+    extern __shared__ u32x4 lds[];
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int nwaves = blockDim.x >> 6;
+    const int G = K >> 7;
+    const int g0 = wave * kL4Groups, g1 = min(G, g0 + kL4Groups), gl = g1 - 1;
+    const int row = blockIdx.x * 64 + lane;
+    char *const tile = reinterpret_cast<char *>(lds) + wave * kL4Wave;
+    char *const lut = tile + kL4Tile;
+    float *const part = reinterpret_cast<float *>(lut + kL4Lut);
+
+    // tile copy: instruction k covers rows 16 k .. 16 k + 15, 4 lanes per row; the cell of
+    // (row r, group u) lands at 64 r + 16 (u ^ ((r >> 2) & 3))
+    const u32x4 *wg = reinterpret_cast<const u32x4 *>(wbits);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        const int r = 16 * k + (lane >> 2);
+        const int gg = min(g0 + ((lane & 3) ^ ((r >> 2) & 3)), gl);
+        const int rr = min(blockIdx.x * 64 + r, N - 1);
+        __builtin_amdgcn_global_load_lds((glb_void_t *)(wg + (size_t)rr * G + gg),
+                                         (lds_void_t *)(tile + k * 1024), 16, 0, 0);
+    }
+    const uint16_t *srow = scales + (size_t)min(row, N - 1) * G;
+    uint2 scv;                                      // VEC_SCALES: the 4 scales as loaded
+    uint32_t scs[kL4Groups];
+    if constexpr (VEC_SCALES) {
+        scv = *reinterpret_cast<const uint2 *>(srow + g0);
+    } else {
+#pragma unroll
+        for (int u = 0; u < kL4Groups; ++u) scs[u] = srow[min(g0 + u, gl)];
+    }
+
+    // tables: lane builds quads e = lane + 64 k of the wave's 4 groups (group u = e / 128,
+    // chunk c, entries 4 bt .. 4 bt + 3), from x loaded all at once
+    uint2 xq[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+        const int e = lane + 64 * k;
+        xq[k] = *reinterpret_cast<const uint2 *>(x + (size_t)min(g0 + (e >> 7), gl) * 128 + 4 * ((e >> 2) & 31));
+    }
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+        const int e = lane + 64 * k;
+        const int u = e >> 7, c = (e >> 2) & 31, bt = e & 3;
+        const half2_t p01 = as_half2(xq[k].x), p23 = as_half2(xq[k].y);
+        const float x0 = (float)p01[0], x1 = (float)p01[1];
+        const float sg2 = (bt & 1) ? 1.f : -1.f, sg3 = (bt & 2) ? 1.f : -1.f;
+        const float base = fmaf(sg3, (float)p23[1], fmaf(sg2, (float)p23[0], -x0 - x1));
+        u32x4 ev;
+        ev[0] = __builtin_bit_cast(uint32_t, base);                                 // v = 4bt
+        ev[1] = __builtin_bit_cast(uint32_t, fmaf(2.f, x0, base));                 // v = 4bt + 1
+        ev[2] = __builtin_bit_cast(uint32_t, fmaf(2.f, x1, base));                 // v = 4bt + 2
+        ev[3] = __builtin_bit_cast(uint32_t, fmaf(2.f, x1, fmaf(2.f, x0, base)));  // v = 4bt + 3
+        *reinterpret_cast<u32x4 *>(lut + u * kLutBytes + 64 * c + 16 * bt) = ev;
+    }
+    __builtin_amdgcn_s_waitcnt(0x0F70);             // vmcnt(0): the tile copy landed
+    __builtin_amdgcn_s_waitcnt(0xC07F);             // lgkmcnt(0): this wave's tables are written
+
+    const uint32_t mask_3c = __builtin_amdgcn_readfirstlane(0x3Cu);
+    const uint32_t lut_addr = (uint32_t)(uintptr_t)((lds_char_t *)lut);
+    uint32_t raddr[16];
+#pragma unroll
+    for (int j = 0; j < 16; ++j) raddr[j] = lut_addr;
+    float acc = 0.f;
+#pragma unroll
+    for (int u = 0; u < kL4Groups; ++u) {
+        const u32x4 q = *reinterpret_cast<const u32x4 *>(tile + 64 * lane + 16 * (u ^ ((lane >> 2) & 3)));
+        float a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;
+#pragma unroll
+        for (int i = 0; i < 4; i += 2) {
+            word_addrs(q[i], &raddr[0], mask_3c);
+            word_addrs(q[i + 1], &raddr[8], mask_3c);
+            float t[16];
+#pragma unroll
+            for (int j = 0; j < 16; ++j) t[j] = lds_f32(raddr[j], u * kLutBytes + 64 * (8 * i + j));
+            a0 += (t[0] + t[1]) + (t[2] + t[3]);
+            a1 += (t[4] + t[5]) + (t[6] + t[7]);
+            a2 += (t[8] + t[9]) + (t[10] + t[11]);
+            a3 += (t[12] + t[13]) + (t[14] + t[15]);
+        }
+        uint32_t sbits;
+        if constexpr (VEC_SCALES) sbits = ((u & 2) ? scv.y : scv.x) >> (16 * (u & 1));
+        else sbits = scs[u];
+        // groups past K (the last wave's slice may be short) count with scale 0
+        const float s = (g0 + u < g1) ? f16_bits_to_f32((uint16_t)sbits) : 0.f;
+        acc = fmaf(s, (a0 + a1) + (a2 + a3), acc);
+    }
+    part[lane] = acc;
+    __syncthreads();
+    if (wave == 0 && row < N) {
+        float t = acc;
+        for (int w = 1; w < nwaves; ++w)
+            t += reinterpret_cast<const float *>(reinterpret_cast<char *>(lds) + w * kL4Wave + kL4Tile + kL4Lut)[lane];
+        y[row] = t;
+    }
+}
+
+hipError_t launch_lut4(const uint32_t *wbits, const uint16_t *scales, const uint16_t *x, float *y,
+                       int N, int K, hipStream_t stream)
+{
+    const int G = K / 128;
+    const int tiles = (N + 63) / 64;
+    const int waves = (G + kL4Groups - 1) / kL4Groups;
+    const size_t lds = (size_t)waves * kL4Wave;
+    const bool vec = (G % kL4Groups) == 0;          // every wave's scales then start 8-byte aligned
+    const void *fn = vec ? reinterpret_cast<const void *>(&q1_gemv_lut4_kernel<true>)
+                         : reinterpret_cast<const void *>(&q1_gemv_lut4_kernel<false>);
+    static const bool attrs_set = [] {
+        const int most = kL4MaxWaves * kL4Wave;
+        return hipFuncSetAttribute(reinterpret_cast<const void *>(&q1_gemv_lut4_kernel<true>),
+                                   hipFuncAttributeMaxDynamicSharedMemorySize, most) == hipSuccess &&
+               hipFuncSetAttribute(reinterpret_cast<const void *>(&q1_gemv_lut4_kernel<false>),
+                                   hipFuncAttributeMaxDynamicSharedMemorySize, most) == hipSuccess;
+    }();
+    if (!attrs_set) return hipErrorInvalidValue;
+    void *args[] = {&wbits, &scales, &x, &y, &N, &K};
+    return launch_kernel(fn, dim3(tiles), dim3(64 * waves), args, lds, stream);
+}
+
 hipError_t launch_lut(const uint32_t *wbits, const uint16_t *scales, const uint16_t *x, float *y,
                       int N, int K, hipStream_t stream)
 {
@@ -407,7 +551,12 @@ template <int M>
 hipError_t launch_m(const uint32_t *wbits, const uint16_t *scales, const uint16_t *x, float *y,
                     int N, int K, hipStream_t stream)
 {
-    if constexpr (M == 1) return launch_lut(wbits, scales, x, y, N, K, stream);
+    if constexpr (M == 1) {
+        // one tile per CU at most and the 4-group slices of K fit one workgroup: small-N kernel
+        if ((N + 63) / 64 <= 256 && (K / 128 + kL4Groups - 1) / kL4Groups <= kL4MaxWaves)
+            return launch_lut4(wbits, scales, x, y, N, K, stream);
+        return launch_lut(wbits, scales, x, y, N, K, stream);
+    }
     return launch_mb<M, 4>(wbits, scales, x, y, N, K, stream);
 }
 
