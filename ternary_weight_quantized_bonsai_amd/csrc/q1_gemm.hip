@@ -173,7 +173,8 @@ __global__ __launch_bounds__(256) void q1_gemm_kernel(const uint32_t *__restrict
         }
     };
     // cell u of the chunk in buffer par: both columns' words for steps 2u, 2u + 1 and group u's
-    // scales, waited for inside the block
+    // scales, waited for inside the block; the outputs are early-clobber so that no output
+    // register doubles as an address the block has yet to use
     auto read_cell = [&](int par, int u) {
         uint32_t aw[2], as[2];
 #pragma unroll
@@ -186,9 +187,9 @@ __global__ __launch_bounds__(256) void q1_gemm_kernel(const uint32_t *__restrict
         uint32_t s0, s1;
         asm volatile("ds_read_b128 %0, %4\n\tds_read_b128 %1, %5\n\tds_read_u16 %2, %6\n\t"
                      "ds_read_u16 %3, %7\n\ts_waitcnt lgkmcnt(0)"
-                     : "=v"(w0), "=v"(w1), "=v"(s0), "=v"(s1)
-                     : "v"(aw[0]), "v"(aw[1]), "v"(as[0]), "v"(as[1])
-                     : "memory");
+                     : "=&v"(w0), "=&v"(w1), "=&v"(s0), "=&v"(s1)   // early clobber: a load landing
+                     : "v"(aw[0]), "v"(aw[1]), "v"(as[0]), "v"(as[1])  // must not overwrite a later
+                     : "memory");                                      // load's address
         wcur[0][0] = w0[0]; wcur[0][1] = w0[1]; wnxt[0][0] = w0[2]; wnxt[0][1] = w0[3];
         wcur[1][0] = w1[0]; wcur[1][1] = w1[1]; wnxt[1][0] = w1[2]; wnxt[1][1] = w1[3];
         cs[0] = (s0 | (s0 << 16)) ^ 0x80008000u;     // (-s, -s)
