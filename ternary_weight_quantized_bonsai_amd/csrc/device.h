@@ -18,25 +18,9 @@ __device__ __forceinline__ float f16_bits_to_f32(uint16_t h)
     return (float)__builtin_bit_cast(_Float16, h);
 }
 
-// fp32 += a.lo*b.lo + a.hi*b.hi, both halves exact products (v_dot2_f32_f16).
-__device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c)
-{
-    return __builtin_amdgcn_fdot2(as_half2(a), as_half2(b), c, false);
-}
-
-// Sum over each row of 16 lanes, left in every lane of the row (DPP row rotations, no LDS).
-__device__ __forceinline__ float row16_sum(float t)
-{
-    // dpp_ctrl 0x121 + (r - 1) = row_ror:r
-    t += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, t), 0x128, 0xF, 0xF, false));
-    t += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, t), 0x124, 0xF, 0xF, false));
-    t += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, t), 0x122, 0xF, 0xF, false));
-    t += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, t), 0x121, 0xF, 0xF, false));
-    return t;
-}
-
 // Two binary16 halves picked from two dwords: (lo(a), lo(b)) or (hi(a), hi(b)).
-__device__ __forceinline__ uint32_t pack_lo(uint32_t a, uint32_t b) { return (a & 0xFFFFu) | (b << 16); }
-__device__ __forceinline__ uint32_t pack_hi(uint32_t a, uint32_t b) { return (a >> 16) | (b & 0xFFFF0000u); }
+// One v_perm_b32 each: selector bytes 0..3 pick bytes of the second source (a), 4..7 of the first (b).
+__device__ __forceinline__ uint32_t pack_lo(uint32_t a, uint32_t b) { return __builtin_amdgcn_perm(b, a, 0x05040100u); }
+__device__ __forceinline__ uint32_t pack_hi(uint32_t a, uint32_t b) { return __builtin_amdgcn_perm(b, a, 0x07060302u); }
 
 }  // namespace bonsai

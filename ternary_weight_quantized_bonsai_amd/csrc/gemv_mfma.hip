@@ -1,0 +1,328 @@
+// gemv_mfma.hip -- small-M GEMV on the matrix cores: ternary M = 1..8 and binary M = 2..8.
+//
+// y[m][n] = sum_k W[n][k] x[m][k] for a handful of rows of x.  The weight rows play the MFMA
+// row dimension and x the (zero-padded) 16-wide column dimension of v_mfma_f32_16x16x32_f16,
+// so one instruction consumes 16 weight rows x 32 k and the expansion of the packed codes to
+// binary16 costs about one VALU op per weight; the matrix core does the multiply-adds that
+// would otherwise cost M VALU ops per weight.
+//
+// Operands.  An MFMA lane (row i = lane % 16, quarter q = lane / 16) holds 8 halves of A and
+// of B for the same 8 k of a 32-k block.  Which 8 k is a free choice as long as A and B agree,
+// so each quarter takes k whose codes sit 16 bits apart in a word; one shift and one mask then
+// put a pair of them onto the two binary16 halves:
+//   binary  word = the 32 k of the block: quarter q takes bits 4q+i and 4q+i+16 (i = 0..3);
+//           ((w << (15 - 4q - i)) & 0x80008000) ^ 0xBC00BC00 is the pair (+-1, +-1), bit 1 -> +1.
+//   ternary the block is two words of 16 codes: pair i of quarter q is fields j = 2q + (i % 2)
+//           and j + 8 of word i / 2; (w << (14 - 2j)) & 0xC000C000 reads codes 00, 01, 11 as
+//           0, +2, -2 (the exponent MSB is the code's low bit, the sign its high bit).
+// B holds x at the same k.  Column j of D depends on column j of B alone, so the lanes of the
+// columns past M read row M - 1 again (a broadcast) and those columns are never stored.
+// The group scale multiplies each group's four chained MFMAs afterwards, one mixed-precision
+// FMA per output straight from the binary16 scale, so the operands stay exact small integers
+// and every product is exact; the ternary factor 2 comes off the sums once at the end.
+//
+// Work split.  A workgroup owns R = 16 RT weight rows; its waves take 4-group slices of K.
+// Each slice's codes (R rows x 4 groups), scales and x (M rows x 512 k) are copied straight
+// into the wave's LDS (direct global->LDS loads, whole lines), the wave's partial sums of the
+// R x M outputs meet the other waves' in LDS and are added in a fixed order.
+#include <limits.h>
+
+#include <type_traits>
+
+#include "device.h"
+#include "launch.h"
+
+namespace bonsai {
+namespace {
+
+typedef float float4_v __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(1))) const void glb_void_t;
+
+constexpr int kSmGroups = 4;                   // groups per K-slice
+constexpr int kSmMaxWaves = 16;
+constexpr int kSmScaleBytes = 64 * kSmGroups * 4;   // room for one dword per (row, group)
+
+template <bool TERN>
+struct SmLayout {
+    static constexpr int cell = TERN ? 32 : 16;           // bytes per (row, group)
+    static constexpr int row_bytes = kSmGroups * cell;     // bytes per row and slice
+    static constexpr int lanes_per_row = row_bytes / 16;
+    static constexpr int rows_per_copy = 64 / lanes_per_row;
+    // LDS bytes per row of x (512 k): the pad puts the x rows a lane quarter reads on distinct
+    // banks (4 dwords apart for the one-dword ternary reads, 8 for the two-dword binary ones)
+    static constexpr int xstride = 1024 + (TERN ? 16 : 32);
+};
+
+// LDS bytes of one wave: codes, scales and the M rows of x
+template <bool TERN>
+constexpr int sm_wave_bytes(int rt, int m)
+{
+    return 16 * rt * SmLayout<TERN>::row_bytes + kSmScaleBytes + m * SmLayout<TERN>::xstride;
+}
+
+// four row tiles per wave need more than the 128 VGPRs that 16 waves per workgroup leave
+constexpr int sm_max_waves(int rt) { return rt >= 4 ? 12 : kSmMaxWaves; }
+
+// PAIRS: the group count is even, so a row's scales of groups 2p, 2p + 1 are one aligned dword
+template <bool TERN, int RT, bool PAIRS>
+__global__ __launch_bounds__(sm_max_waves(RT) * 64) void gemv_mfma_kernel(const uint32_t *__restrict__ codes,
+                                                                     const uint16_t *__restrict__ scales,
+                                                                     const uint16_t *__restrict__ x,
+                                                                     float *__restrict__ y, int M, int N, int K)
+{
+    using L = SmLayout<TERN>;
+    constexpr int R = 16 * RT;
+    constexpr int TILE = R * L::row_bytes;
+    extern __shared__ u32x4 lds[];
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int nw = blockDim.x >> 6;
+    const int G = K >> 7;
+    const int ns = (G + kSmGroups - 1) / kSmGroups;       // slices of K
+    const int n0 = blockIdx.x * R;
+    const int wbytes = sm_wave_bytes<TERN>(RT, M);
+    char *const mine = reinterpret_cast<char *>(lds) + wave * wbytes;
+    char *const tile = mine;
+    char *const sc = mine + TILE;
+    char *const xs = sc + kSmScaleBytes;
+    float *const red = reinterpret_cast<float *>(reinterpret_cast<char *>(lds) + nw * wbytes);
+    const int q = lane >> 4, i16 = lane & 15;
+    const int units = G * (L::cell / 16);                  // 16-byte units per weight row
+    const u32x4 *cg = reinterpret_cast<const u32x4 *>(codes);
+    const u32x4 *xg = reinterpret_cast<const u32x4 *>(x);
+
+    float4_v acc[RT];
+#pragma unroll
+    for (int t = 0; t < RT; ++t) acc[t] = float4_v{0.f, 0.f, 0.f, 0.f};
+    const float4_v zero4 = float4_v{0.f, 0.f, 0.f, 0.f};
+
+    for (int s = wave; s < ns; s += nw) {
+        const int g0 = s * kSmGroups;
+        const int g1 = min(G, g0 + kSmGroups), gl = g1 - 1;
+        // codes: copy k covers rows rows_per_copy * k + lane / lanes_per_row; the 16-byte
+        // chunk c of row r lands at row_bytes * r + 16 (c ^ swizzle(r))
+#pragma unroll
+        for (int k = 0; k < TILE / 1024; ++k) {
+            const int r = L::rows_per_copy * k + lane / L::lanes_per_row;
+            const int sw = TERN ? ((r >> 1) & 7) : ((r >> 2) & 3);
+            const int c = (lane % L::lanes_per_row) ^ sw;
+            const int unit = min(g0 * (L::cell / 16) + c, units - 1);
+            __builtin_amdgcn_global_load_lds((glb_void_t *)(cg + (size_t)min(n0 + r, N - 1) * units + unit),
+                                             (lds_void_t *)(tile + k * 1024), 16, 0, 0);
+        }
+        // scales: the scale of (row r, group u) is half u of the 8 bytes at sc + 8 r (PAIRS:
+        // one 4-byte copy per row and pair of groups), or the low half of the dword at
+        // sc + 16 r + 4 u (one 2-byte copy per row and group)
+        if constexpr (PAIRS) {
+#pragma unroll
+            for (int k = 0; k < (2 * R + 63) / 64; ++k) {
+                const int e = 64 * k + lane, r = min(e >> 1, R - 1), p = e & 1;
+                __builtin_amdgcn_global_load_lds((glb_void_t *)(scales + (size_t)min(n0 + r, N - 1) * G + min(g0 + 2 * p, G - 2)),
+                                                 (lds_void_t *)(sc + 256 * k), 4, 0, 0);
+            }
+        } else {
+#pragma unroll
+            for (int k = 0; k < (4 * R + 63) / 64; ++k) {
+                const int e = 64 * k + lane, r = min(e >> 2, R - 1), u = e & 3;
+                __builtin_amdgcn_global_load_lds((glb_void_t *)(scales + (size_t)min(n0 + r, N - 1) * G + min(g0 + u, gl)),
+                                                 (lds_void_t *)(sc + 256 * k), 2, 0, 0);
+            }
+        }
+        // x: row m, k = 128 g0 .. 128 g0 + 511 (clamped inside K; past-K groups count 0)
+        for (int m = 0; m < M; ++m)
+            __builtin_amdgcn_global_load_lds((glb_void_t *)(xg + (size_t)m * (K >> 3) + min(16 * g0 + lane, (K >> 3) - 1)),
+                                             (lds_void_t *)(xs + m * L::xstride), 16, 0, 0);
+        __builtin_amdgcn_s_waitcnt(0x0F70);               // vmcnt(0): this wave's slice landed
+        if (g1 - g0 < kSmGroups) {
+            // groups past K (last slice only) hold clamped copies: their scales become zero
+            for (int e = lane; e < R * kSmGroups; e += 64) {
+                const int r = e >> 2, u = e & 3;
+                if (g0 + u >= g1) *reinterpret_cast<uint16_t *>(sc + (PAIRS ? 8 * r + 2 * u : 16 * r + 4 * u)) = 0;
+            }
+        }
+        // the scales of this lane's D rows 16 t + 4 q + r, all four groups: the binary16 of
+        // group u is half u % 2 of sp[t][r][u / 2] (PAIRS) or the low half of sp[t][r][u]
+        constexpr int SW = PAIRS ? 2 : 4;
+        uint32_t sp[RT][4][SW];
+#pragma unroll
+        for (int t = 0; t < RT; ++t)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int row = 16 * t + 4 * q + r;
+                if constexpr (PAIRS) {
+                    const uint2 v = *reinterpret_cast<const uint2 *>(sc + 8 * row);
+                    sp[t][r][0] = v.x;
+                    sp[t][r][1] = v.y;
+                } else {
+                    const u32x4 v = *reinterpret_cast<const u32x4 *>(sc + 16 * row);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) sp[t][r][e] = v[e];
+                }
+            }
+
+#pragma unroll
+        for (int u = 0; u < kSmGroups; ++u) {
+            // this lane's weight rows: 16 t + i16, one cell each
+            uint32_t wd[RT][L::cell / 4];
+#pragma unroll
+            for (int t = 0; t < RT; ++t) {
+                const int r = 16 * t + i16;
+                const int sw = TERN ? ((r >> 1) & 7) : ((r >> 2) & 3);
+#pragma unroll
+                for (int h = 0; h < L::cell / 16; ++h) {
+                    const int c = (L::cell / 16) * u + h;
+                    const u32x4 v = *reinterpret_cast<const u32x4 *>(tile + L::row_bytes * r + 16 * (c ^ sw));
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) wd[t][4 * h + e] = v[e];
+                }
+            }
+            float4_v d[RT];
+            const char *xrow = xs + min(i16, M - 1) * L::xstride;   // row i16 of x (M - 1 past M)
+#pragma unroll
+            for (int kb = 0; kb < 4; ++kb) {
+                // B: this quarter's 8 k of block kb, in the order of the A pairs
+                u32x4 bv;
+                if constexpr (TERN) {
+                    const int k0 = 128 * u + 32 * kb + 2 * q;
+                    const uint32_t a0 = *reinterpret_cast<const uint32_t *>(xrow + 2 * k0);
+                    const uint32_t a1 = *reinterpret_cast<const uint32_t *>(xrow + 2 * (k0 + 8));
+                    const uint32_t a2 = *reinterpret_cast<const uint32_t *>(xrow + 2 * (k0 + 16));
+                    const uint32_t a3 = *reinterpret_cast<const uint32_t *>(xrow + 2 * (k0 + 24));
+                    bv[0] = pack_lo(a0, a1);
+                    bv[1] = pack_hi(a0, a1);
+                    bv[2] = pack_lo(a2, a3);
+                    bv[3] = pack_hi(a2, a3);
+                } else {
+                    const int k0 = 128 * u + 32 * kb + 4 * q;
+                    const uint2 xa = *reinterpret_cast<const uint2 *>(xrow + 2 * k0);
+                    const uint2 xb = *reinterpret_cast<const uint2 *>(xrow + 2 * (k0 + 16));
+                    bv[0] = pack_lo(xa.x, xb.x);
+                    bv[1] = pack_hi(xa.x, xb.x);
+                    bv[2] = pack_lo(xa.y, xb.y);
+                    bv[3] = pack_hi(xa.y, xb.y);
+                }
+                const half8_t bf = __builtin_bit_cast(half8_t, bv);
+#pragma unroll
+                for (int t = 0; t < RT; ++t) {
+                    u32x4 av;
+                    if constexpr (TERN) {
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) {
+                            const uint32_t w = wd[t][2 * kb + (i >> 1)];
+                            av[i] = (w << (14 - 4 * q - 2 * (i & 1))) & 0xC000C000u;
+                        }
+                    } else {
+                        const uint32_t w = wd[t][kb];
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) av[i] = ((w << (15 - 4 * q - i)) & 0x80008000u) ^ 0xBC00BC00u;
+                    }
+                    const half8_t af = __builtin_bit_cast(half8_t, av);
+                    d[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af, bf, kb == 0 ? zero4 : d[t], 0, 0, 0);
+                }
+            }
+#pragma unroll
+            for (int t = 0; t < RT; ++t)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const half2_t h = as_half2(sp[t][r][PAIRS ? u >> 1 : u]);
+                    acc[t][r] = fmaf((float)h[PAIRS ? u & 1 : 0], d[t][r], acc[t][r]);
+                }
+        }
+        __builtin_amdgcn_s_waitcnt(0xC07F);               // LDS reads done before the next slice's copies
+    }
+
+    // D rows 16 t + 4 q + r, column i16: the wave's partial sums into red[wave][column][row]
+    if (i16 < M) {
+#pragma unroll
+        for (int t = 0; t < RT; ++t)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) red[(wave * M + i16) * R + 16 * t + 4 * q + r] = TERN ? 0.5f * acc[t][r] : acc[t][r];
+    }
+    __syncthreads();
+    for (int o = threadIdx.x; o < M * R; o += blockDim.x) {
+        const int m = o / R, row = o % R;
+        float v = 0.f;
+        for (int w = 0; w < nw; ++w) v += red[(w * M + m) * R + row];
+        if (n0 + row < N) y[(size_t)m * N + n0 + row] = v;
+    }
+}
+
+constexpr int kLdsPerCu = 160 * 1024;
+
+// waves of a workgroup: one per slice of K, at most 16 and as many as the LDS holds
+template <bool TERN>
+int sm_waves(int rt, int M, int K)
+{
+    const int ns = (K / 128 + kSmGroups - 1) / kSmGroups;
+    const int per_wave = sm_wave_bytes<TERN>(rt, M) + M * 16 * rt * 4;
+    int nw = ns < sm_max_waves(rt) ? ns : sm_max_waves(rt);
+    if (nw > kLdsPerCu / per_wave) nw = kLdsPerCu / per_wave;
+    return nw;
+}
+
+template <bool TERN, int RT>
+hipError_t launch_rt(const uint32_t *codes, const uint16_t *scales, const uint16_t *x, float *y,
+                     int M, int N, int K, hipStream_t stream)
+{
+    const int nw = sm_waves<TERN>(RT, M, K);
+    if (nw < 1) return hipErrorInvalidValue;
+    const size_t lds = (size_t)nw * sm_wave_bytes<TERN>(RT, M) + (size_t)nw * M * 16 * RT * 4;
+    const int64_t blocks = ((int64_t)N + 16 * RT - 1) / (16 * RT);
+    if (blocks > INT_MAX) return hipErrorInvalidValue;
+    const void *fn = (K / 128) % 2 == 0 ? reinterpret_cast<const void *>(&gemv_mfma_kernel<TERN, RT, true>)
+                                        : reinterpret_cast<const void *>(&gemv_mfma_kernel<TERN, RT, false>);
+    static const bool attr =
+        hipFuncSetAttribute(reinterpret_cast<const void *>(&gemv_mfma_kernel<TERN, RT, true>),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, kLdsPerCu) == hipSuccess &&
+        hipFuncSetAttribute(reinterpret_cast<const void *>(&gemv_mfma_kernel<TERN, RT, false>),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, kLdsPerCu) == hipSuccess;
+    if (!attr) return hipErrorInvalidValue;
+    void *args[] = {&codes, &scales, &x, &y, &M, &N, &K};
+    return launch_kernel(fn, dim3((unsigned)blocks), dim3(64 * nw), args, lds, stream);
+}
+
+template <bool TERN>
+hipError_t launch_sm(const uint32_t *codes, const uint16_t *scales, const uint16_t *x, float *y,
+                     int M, int N, int K, hipStream_t stream)
+{
+    // Every wave loads its slice at once and then computes, so a second round of workgroups
+    // on a CU pays the load latency again: take the row tile (16, 32 or 64 rows) whose grid
+    // needs the fewest rounds of the chip's 256 CUs, given what the LDS and the 32 wave slots
+    // of a CU hold, and among those the smallest tile (the most workgroups).
+    constexpr int kCus = 256, kWavesPerCu = 32;
+    auto rounds = [&](int rt) -> int64_t {
+        const int nw = sm_waves<TERN>(rt, M, K);
+        if (nw < 1) return INT64_MAX;
+        const int64_t lds = (int64_t)nw * sm_wave_bytes<TERN>(rt, M) + (int64_t)nw * M * 16 * rt * 4;
+        int64_t per_cu = kLdsPerCu / lds;
+        if (per_cu > kWavesPerCu / nw) per_cu = kWavesPerCu / nw;
+        if (per_cu < 1) return INT64_MAX;
+        const int64_t blocks = ((int64_t)N + 16 * rt - 1) / (16 * rt);
+        return (blocks + per_cu * kCus - 1) / (per_cu * kCus);
+    };
+    const int64_t r1 = rounds(1), r2 = rounds(2), r4 = rounds(4);
+    if (r1 <= r2 && r1 <= r4) return launch_rt<TERN, 1>(codes, scales, x, y, M, N, K, stream);
+    if (r2 <= r4) return launch_rt<TERN, 2>(codes, scales, x, y, M, N, K, stream);
+    return launch_rt<TERN, 4>(codes, scales, x, y, M, N, K, stream);
+}
+
+}  // namespace
+
+hipError_t launch_gemv_mfma(bool ternary, const uint32_t *codes, const uint16_t *scales, const uint16_t *x,
+                            float *y, int M, int N, int K, hipStream_t stream)
+{
+    return ternary ? launch_sm<true>(codes, scales, x, y, M, N, K, stream)
+                   : launch_sm<false>(codes, scales, x, y, M, N, K, stream);
+}
+
+// Ternary weights ("Ternary Bonsai 27B" article, ternary format: {-1, 0, +1} times the FP16
+// group scale, two bits per weight in the current release) take this kernel for every M.
+hipError_t launch_q2t_gemv(const uint32_t *wcodes, const uint16_t *scales, const uint16_t *x, float *y,
+                           int M, int N, int K, hipStream_t stream)
+{
+    if (M < 1 || M > 8) return hipErrorInvalidValue;
+    return launch_sm<true>(wcodes, scales, x, y, M, N, K, stream);
+}
+
+}  // namespace bonsai

@@ -1,220 +1,21 @@
-// q1_gemv.hip -- binary g128 decode GEMV on gfx950:  y[m][n] = sum_k W[n][k] x[m][k],  M <= 8.
+// q1_gemv.hip -- binary g128 decode GEMV on gfx950 for one row of x:  y[n] = sum_k W[n][k] x[k].
 //
 // The matmul runs straight on the packed sign words ("1-bit Bonsai 27B" model card: the
 // weights are used packed and never expanded back to FP16; the CUDA kernel unpacks the sign
 // codes inside the matmul and applies the group scales).  Decode is the memory-bound phase
-// (model card, cross-platform throughput), so the kernel is organised around streaming the
-// 1.125 bits/weight from HBM once, with as few VALU operations per weight as possible.
+// (model card, cross-platform throughput), so the kernels are organised around streaming the
+// 1.125 bits/weight from HBM once, with as few VALU operations per weight as possible: the
+// signs of four weights index a table of the 16 signed sums of their x values.
 //
-// Work split.  A workgroup owns 64 consecutive weight rows; its waves take disjoint K-slices
-// (whole groups) of those rows and meet in LDS at the end, summed in a fixed order.  Inside a
-// wave, lane r owns row r, so every lane is at the same k at the same time and x is
-// wave-uniform: it is read through the scalar cache into SGPRs.
-//
-// Loads.  Row r's bytes for a batch of B groups are 16*B contiguous bytes, 640 B away from row
-// r+1 at K = 5120.  Each global load instruction therefore covers 64/B rows x 16*B bytes (B
-// lanes per row, every byte of each touched segment used), and the wave transposes the batch
-// through its own LDS tile so that lane r then reads its row.  The next batch is in flight
-// while the current one is consumed.
-//
-// Sign expansion (exact, about 1.1 VALU op per weight).  Masking a sign word with
-// 0x00010001 << p keeps bits p and p+16; read as two binary16 values these are b*c_p with
-// c_p = 2^-14, 2^-13, 2^-11, 2^-7, 2 for p = 10 .. 14 (exponent-field bits, never subnormal).
-// Shifting the word left by 0, 5, 10 (and right by 1 for bits 15, 31) brings every bit onto
-// one of these five positions, so 16 masks + 16 v_dot2_f32_f16 against the x pairs
-// (x[32i+j], x[32i+16+j]) give five exact per-class sums  A_p = c_p * sum b x.  Per group:
-//     sum_k (2b-1) x = sum_p (2/c_p) A_p - X_g,      X_g = sum_{k in group} x_k,
-// then y += s * (that).  The 2/c_p are powers of two, so the class combination is exact; X_g
-// is formed once per group per wave by 16 lanes per group and broadcast with v_readlane.
+// Work split.  A workgroup owns 64 consecutive weight rows (lane r of every wave <-> row r);
+// its waves take disjoint K-slices (whole groups) of those rows and meet in LDS at the end,
+// summed in a fixed order.  Weight bytes reach LDS by direct global->LDS loads of whole lines.
+// Two to eight rows of x (M = 2..8) go to the matrix-core GEMV instead (gemv_mfma.hip).
 #include "device.h"
 #include "launch.h"
 
 namespace bonsai {
 namespace {
-
-// Pair (lo(a), lo(b)) / (hi(a), hi(b)) of two uniform dwords, on the scalar unit.
-__device__ __forceinline__ uint32_t s_pack_ll(uint32_t a, uint32_t b)
-{
-    uint32_t r;
-    asm("s_pack_ll_b32_b16 %0, %1, %2" : "=s"(r) : "s"(a), "s"(b));
-    return r;
-}
-__device__ __forceinline__ uint32_t s_pack_hh(uint32_t a, uint32_t b)
-{
-    uint32_t r;
-    asm("s_pack_hh_b32_b16 %0, %1, %2" : "=s"(r) : "s"(a), "s"(b));
-    return r;
-}
-
-// Class sums of one 32-bit sign word against its 32 x values (16 uniform dwords at xw).
-// acc[0..4] collect the classes p = 10 .. 14.
-__device__ __forceinline__ void word_classes(uint32_t w, const uint32_t *__restrict__ xw, float acc[5])
-{
-    const uint32_t v0 = w, v1 = w << 5, v2 = w << 10, v3 = w >> 1;
-    uint32_t xp[16];
-#pragma unroll
-    for (int j = 0; j < 16; j += 2) {
-        const uint32_t a = xw[j >> 1], b = xw[8 + (j >> 1)];
-        xp[j] = s_pack_ll(a, b);          // (x[j],   x[16+j])
-        xp[j + 1] = s_pack_hh(a, b);      // (x[j+1], x[17+j])
-    }
-#pragma unroll
-    for (int p = 10; p <= 14; ++p) {
-        const uint32_t mask = 0x00010001u << p;
-        float a = acc[p - 10];
-        a = dot2(v0 & mask, xp[p], a);                 // bit p
-        a = dot2(v1 & mask, xp[p - 5], a);             // bit p - 5
-        a = dot2(v2 & mask, xp[p - 10], a);            // bit p - 10
-        if (p == 14) a = dot2(v3 & mask, xp[15], a);   // bit 15
-        acc[p - 10] = a;
-    }
-}
-
-template <int M, int BATCH>
-__global__ __launch_bounds__(768) void q1_gemv_mask_kernel(const uint32_t *__restrict__ wbits,
-                                                       const uint16_t *__restrict__ scales,
-                                                       const uint16_t *__restrict__ x,
-                                                       float *__restrict__ y, int N, int K, int gps)
-{
-    constexpr int STRIDE = BATCH + 1;           // 16-byte cells per LDS tile row (one of padding)
-    constexpr int RPI = 64 / BATCH;             // rows per global load instruction
-    constexpr int XH = (BATCH + 3) / 4;         // X_g passes (4 groups per pass)
-    extern __shared__ u32x4 lds[];              // [waves][64][STRIDE] tiles, then [waves][M][64] floats
-
-    const int lane = threadIdx.x & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int nwaves = blockDim.x >> 6;
-    const int G = K >> 7;
-    const int row0 = blockIdx.x * 64;
-    const int row = row0 + lane;
-    const int rclamp = min(row, N - 1);
-    const int g0 = wave * gps;
-    const int g1 = min(G, g0 + gps);
-
-    u32x4 *tile = lds + wave * 64 * STRIDE;
-    const u32x4 *wg = reinterpret_cast<const u32x4 *>(wbits);     // (row n, group g) at n * G + g
-    const uint32_t *xd = reinterpret_cast<const uint32_t *>(x);
-    const uint16_t *srow = scales + (size_t)rclamp * G;
-
-    // global load mapping: instruction i reads row lrow + i*RPI of the tile, group lchunk of
-    // the batch.  Rows past N (last tile only) are not loaded; their lanes store nothing.
-    const int lrow = lane / BATCH, lchunk = lane % BATCH;
-    const u32x4 *wbase = wg + (size_t)(row0 + lrow) * G;
-    const int nrows = N - row0 - lrow;                 // rows of this lane's column still valid
-    float acc[M];
-#pragma unroll
-    for (int m = 0; m < M; ++m) acc[m] = 0.f;
-
-    // batch in flight: BATCH 16-byte cells of the tile and the lane's BATCH scales
-    u32x4 v[BATCH];
-    float sc[BATCH];
-    {
-        const int gg = min(g0 + lchunk, g1 - 1);
-#pragma unroll
-        for (int i = 0; i < BATCH; ++i)
-            if (i * RPI < nrows) v[i] = wbase[(size_t)i * RPI * G + gg];
-#pragma unroll
-        for (int u = 0; u < BATCH; ++u) sc[u] = f16_bits_to_f32(srow[min(g0 + u, g1 - 1)]);
-    }
-    for (int gb = g0; gb < g1; gb += BATCH) {
-#pragma unroll
-        for (int i = 0; i < BATCH; ++i) tile[(lrow + i * RPI) * STRIDE + lchunk] = v[i];
-        float s_cur[BATCH];
-#pragma unroll
-        for (int u = 0; u < BATCH; ++u) s_cur[u] = sc[u];
-        const int gn = gb + BATCH;
-        if (gn < g1) {                                      // next batch in flight
-            const int gg = min(gn + lchunk, g1 - 1);
-#pragma unroll
-            for (int i = 0; i < BATCH; ++i)
-                if (i * RPI < nrows) v[i] = wbase[(size_t)i * RPI * G + gg];
-#pragma unroll
-            for (int u = 0; u < BATCH; ++u) sc[u] = f16_bits_to_f32(srow[min(gn + u, g1 - 1)]);
-        }
-
-        // X_g of the batch's groups: 16 lanes per group, 8 values each, summed across the 16.
-        float xg[M][XH];
-#pragma unroll
-        for (int m = 0; m < M; ++m)
-#pragma unroll
-            for (int h = 0; h < XH; ++h) {
-                const int g = min(gb + 4 * h + (lane >> 4), G - 1);
-                const u32x4 xv = *reinterpret_cast<const u32x4 *>(x + (size_t)m * K + (size_t)g * 128 +
-                                                                  8 * (lane & 15));
-                float t = dot2(xv.x, 0x3C003C00u, 0.f);
-                t = dot2(xv.y, 0x3C003C00u, t);
-                t = dot2(xv.z, 0x3C003C00u, t);
-                t = dot2(xv.w, 0x3C003C00u, t);
-                xg[m][h] = row16_sum(t);
-            }
-
-#pragma unroll
-        for (int u = 0; u < BATCH; ++u) {
-            const int g = gb + u;
-            if (g >= g1) break;
-            const u32x4 q = tile[lane * STRIDE + u];
-            const uint32_t words[4] = {q.x, q.y, q.z, q.w};
-#pragma unroll
-            for (int m = 0; m < M; ++m) {
-                float cls[5] = {0.f, 0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                for (int i = 0; i < 4; ++i)
-                    word_classes(words[i], xd + (size_t)m * (K >> 1) + (size_t)g * 64 + i * 16, cls);
-                const float t = cls[0] * 32768.f + cls[1] * 16384.f + cls[2] * 4096.f + cls[3] * 256.f + cls[4];
-                const int xi = __builtin_amdgcn_readlane(__builtin_bit_cast(int, xg[m][u / 4]), 16 * (u % 4));
-                acc[m] = fmaf(s_cur[u], t - __builtin_bit_cast(float, xi), acc[m]);
-            }
-        }
-    }
-
-    if (nwaves == 1) {
-        if (row < N)
-#pragma unroll
-            for (int m = 0; m < M; ++m) y[(size_t)m * N + row] = acc[m];
-        return;
-    }
-    float *red = reinterpret_cast<float *>(lds + nwaves * 64 * STRIDE);
-#pragma unroll
-    for (int m = 0; m < M; ++m) red[(wave * M + m) * 64 + lane] = acc[m];
-    __syncthreads();
-    if (wave == 0 && row < N) {
-#pragma unroll
-        for (int m = 0; m < M; ++m) {
-            float t = red[m * 64 + lane];
-            for (int w = 1; w < nwaves; ++w) t += red[(w * M + m) * 64 + lane];
-            y[(size_t)m * N + row] = t;
-        }
-    }
-}
-
-constexpr size_t kMaxLds = 65536;
-constexpr int kTargetWaves = 8192;     // ~8 resident waves per SIMD on 1024 SIMDs
-
-template <int M, int BATCH>
-size_t lds_bytes(int slices)
-{
-    return (size_t)slices * 64 * (BATCH + 1) * sizeof(u32x4) + (slices > 1 ? (size_t)slices * M * 64 * sizeof(float) : 0);
-}
-
-template <int M, int BATCH>
-hipError_t launch_mb(const uint32_t *wbits, const uint16_t *scales, const uint16_t *x, float *y,
-                     int N, int K, hipStream_t stream)
-{
-    const int G = K / 128;
-    const int tiles = (N + 63) / 64;
-    // Aim for about two waves per SIMD (1024 SIMDs) by splitting K across the waves of a
-    // workgroup, within the 64 KiB of LDS a workgroup may take.
-    int want = min(12, max(1, (kTargetWaves + tiles - 1) / tiles));
-    while (want > 1 && lds_bytes<M, BATCH>(want) > kMaxLds) --want;
-    int gps = (G + want - 1) / want;
-    gps = ((gps + BATCH - 1) / BATCH) * BATCH;
-    const int slices = (G + gps - 1) / gps;
-    const size_t lds = lds_bytes<M, BATCH>(slices);
-    void *args[] = {&wbits, &scales, &x, &y, &N, &K, &gps};
-    return launch_kernel(reinterpret_cast<const void *>(&q1_gemv_mask_kernel<M, BATCH>), dim3(tiles),
-                         dim3(64 * slices), args, lds, stream);
-}
-
 
 // ---- M = 1: nibble lookup tables ------------------------------------------------------------
 //
@@ -547,35 +348,17 @@ hipError_t launch_lut(const uint32_t *wbits, const uint16_t *scales, const uint1
                          args, lds, stream);
 }
 
-template <int M>
-hipError_t launch_m(const uint32_t *wbits, const uint16_t *scales, const uint16_t *x, float *y,
-                    int N, int K, hipStream_t stream)
-{
-    if constexpr (M == 1) {
-        // one tile per CU at most and the 4-group slices of K fit one workgroup: small-N kernel
-        if ((N + 63) / 64 <= 256 && (K / 128 + kL4Groups - 1) / kL4Groups <= kL4MaxWaves)
-            return launch_lut4(wbits, scales, x, y, N, K, stream);
-        return launch_lut(wbits, scales, x, y, N, K, stream);
-    }
-    return launch_mb<M, 4>(wbits, scales, x, y, N, K, stream);
-}
-
 }  // namespace
 
 hipError_t launch_q1_gemv(const uint32_t *wbits, const uint16_t *scales, const uint16_t *x, float *y,
                           int M, int N, int K, hipStream_t stream)
 {
-    switch (M) {
-    case 1: return launch_m<1>(wbits, scales, x, y, N, K, stream);
-    case 2: return launch_m<2>(wbits, scales, x, y, N, K, stream);
-    case 3: return launch_m<3>(wbits, scales, x, y, N, K, stream);
-    case 4: return launch_m<4>(wbits, scales, x, y, N, K, stream);
-    case 5: return launch_m<5>(wbits, scales, x, y, N, K, stream);
-    case 6: return launch_m<6>(wbits, scales, x, y, N, K, stream);
-    case 7: return launch_m<7>(wbits, scales, x, y, N, K, stream);
-    case 8: return launch_m<8>(wbits, scales, x, y, N, K, stream);
-    default: return hipErrorInvalidValue;
-    }
+    if (M >= 2 && M <= 8) return launch_gemv_mfma(false, wbits, scales, x, y, M, N, K, stream);
+    if (M != 1) return hipErrorInvalidValue;
+    // one tile per CU at most and the 4-group slices of K fit one workgroup: small-N kernel
+    if ((N + 63) / 64 <= 256 && (K / 128 + kL4Groups - 1) / kL4Groups <= kL4MaxWaves)
+        return launch_lut4(wbits, scales, x, y, N, K, stream);
+    return launch_lut(wbits, scales, x, y, N, K, stream);
 }
 
 }  // namespace bonsai
