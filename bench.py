@@ -93,6 +93,11 @@ def kernel_times(hip: Hip, bonsai, launches) -> list[float]:
     return out
 
 
+# The decode GEMV kernel both headline shapes run on (one 64-row tile per workgroup, 4-group
+# K-slices per wave); its HBM-traffic summary under profiles/ carries this name.
+HEADLINE_KERNEL = "q1_gemv_lut4_kernel"
+
+
 def src_digest(path: Path) -> str:
     return hashlib.sha256(path.read_bytes()).hexdigest()[:16]
 
@@ -145,6 +150,8 @@ def cpu_baseline(wA, sA, xA, wB, sB, xB, K, budget_s: float):
 # ---- rocprofv3 CSV summaries for profiles/ (host only, no GPU) ---------------------------
 def short_name(name: str) -> str:
     name = name.replace("bonsai::(anonymous namespace)::", "").replace("bonsai::", "")
+    if name.startswith("void "):          # the counter runs print the return type
+        name = name[5:]
     return name.split("(", 1)[0]
 
 
@@ -183,6 +190,7 @@ def summarize_trace(d: str, out: str, cmds: list[str]) -> None:
         if k[0].startswith("__amd"):
             continue
         lines.append(" | ".join(str(x) for x in k) + f" | {len(v)} | {sum(v) / len(v):.1f}")
+    (ROOT / "profiles").mkdir(exist_ok=True)
     (ROOT / "profiles" / out).write_text("\n".join(lines) + "\n")
     print((ROOT / "profiles" / out).read_text())
 
@@ -216,7 +224,7 @@ def summarize_pmc(fetch_dir: str, write_dir: str, out: str, cmds: list[str], ker
     def kern(acc):
         by = {}
         for (_, n, g), v in acc.items():
-            if n == kernel:
+            if n.split("<")[0] == kernel:
                 by.setdefault(g, []).append(v)
         return by
     kf, kw = kern(f), kern(w)
@@ -239,6 +247,7 @@ def summarize_pmc(fetch_dir: str, write_dir: str, out: str, cmds: list[str], ker
         tot += b * len(kf[g])
         n += len(kf[g])
     lines += ["", f"hbm_bytes_per_launch: {tot / n:.0f}"]
+    (ROOT / "profiles").mkdir(exist_ok=True)
     (ROOT / "profiles" / out).write_text("\n".join(lines) + "\n")
     print((ROOT / "profiles" / out).read_text())
 
@@ -261,7 +270,7 @@ def main() -> int:
         summarize_trace(args.summarize_trace, args.out, args.cmd)
         return 0
     if args.summarize_pmc:
-        summarize_pmc(*args.summarize_pmc, args.out, args.cmd, "q1_gemv_lut_kernel",
+        summarize_pmc(*args.summarize_pmc, args.out, args.cmd, HEADLINE_KERNEL,
                       "ternary_weight_quantized_bonsai_amd/csrc/q1_gemv.hip")
         return 0
     if args.gpus != 1:
@@ -346,10 +355,10 @@ def main() -> int:
     per_launch_ms = float(np.mean(kt))
     achieved = per_launch_bytes / (per_launch_ms / 1e3) / 1e9
     digest = src_digest(ROOT / "ternary_weight_quantized_bonsai_amd" / "csrc" / "q1_gemv.hip")
-    traffic = read_pmc("q1_gemv_lut_kernel_decode_pair_hbm_traffic.txt", digest)
+    traffic = read_pmc(f"{HEADLINE_KERNEL}_decode_pair_hbm_traffic.txt", digest)
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                 "frac": round(achieved / PEAK_HBM_GBPS, 4), "traffic": traffic,
-                "kernel": "q1_gemv_lut_kernel", "avg_launch_us": round(per_launch_ms * 1e3, 3),
+                "kernel": HEADLINE_KERNEL, "avg_launch_us": round(per_launch_ms * 1e3, 3),
                 "bytes_per_launch": per_launch_bytes,
                 "per_shape_us": {"mlp_13824x5120": round(t_mlp * 1e3, 3), "attn_5120x5120": round(t_attn * 1e3, 3)}}
     log(f"q1_gemv device time: mlp {t_mlp * 1e3:.2f} us, attn {t_attn * 1e3:.2f} us -> {achieved:.1f} GB/s")
