@@ -194,66 +194,130 @@ __global__ __launch_bounds__(384) void q1_gemv_lut_kernel(const uint32_t *__rest
     }
 }
 
-// Small N (at most 256 row tiles, one per CU): one 64-row tile per workgroup and one 4-group
-// K-slice per wave, so every wave has a single 4 KB copy and 128 lookups per lane after it
-// lands; the waves' partial sums meet in LDS in a fixed order.  A wave builds only its own 4
-// groups' tables, all at once (one wait), after its copy and x have arrived.
-constexpr int kL4Groups = 4;
-constexpr int kL4Tile = 64 * kL4Groups * 16;        // 4 KB: 64 rows x 4 groups
-constexpr int kL4Lut = kL4Groups * kLutBytes;       // 8 KB of tables
-constexpr int kL4Wave = kL4Tile + kL4Lut + 64 * 4;  // + this wave's partial sums
-constexpr int kL4MaxWaves = 13;                     // 13 x 12.25 KB fits the 160 KB of LDS
-
-template <bool VEC_SCALES>
-__global__ __launch_bounds__(kL4MaxWaves * 64) void q1_gemv_lut4_kernel(const uint32_t *__restrict__ wbits,
-                                                                        const uint16_t *__restrict__ scales,
-                                                                        const uint16_t *__restrict__ x,
-                                                                        float *__restrict__ y, int N, int K)
+// 16-byte LDS store at addr, issued from asm: the compiler cannot tell it apart from the LDS
+// the in-flight direct global->LDS copies write, and would otherwise wait for every copy
+// (s_waitcnt vmcnt(0)) before the first such store.  Callers order it with explicit waits.
+__device__ __forceinline__ void lds_store_b128(uint32_t addr, u32x4 v)
 {
+    asm volatile("ds_write_b128 %0, %1" : : "v"(addr), "v"(v) : "memory");
+}
+
+// Small N (at most 256 row tiles, one per CU): one tile of ROWS = 64 or 32 rows per
+// workgroup.  A wave owns GPW = 4 * 64 / ROWS consecutive groups of the tile's rows: lane l
+// takes row l % ROWS and the 4 groups 4 (l / ROWS) .. + 3 of the wave's, so every wave has a
+// single 4 KB tile copy and 128 lookups per lane after it lands, whatever ROWS.  32-row tiles
+// spread a small N over twice the CUs, at the price of tables for twice the groups per wave.
+// The waves' partial sums meet in LDS and are added in a fixed order.
+//
+// Everything a wave needs reaches its LDS by direct global->LDS copies, issued in this order:
+// its x values, the weight tile, the scales.  Copies complete in issue order, so waiting until
+// at most the tile's and the scales' copies are outstanding means x has landed: the wave builds
+// its tables while the tile is still on its way from HBM.  (Read through the compiler, x would
+// wait for every copy: it cannot tell the copies' LDS writes from the table writes, and orders
+// loads of mixed kinds by waiting for all of them.)
+template <int ROWS>
+struct L4 {
+    static constexpr int lpr = 64 / ROWS;               // lanes per row
+    static constexpr int gpw = 4 * lpr;                 // groups per wave
+    static constexpr int tile = ROWS * gpw * 16;        // 4 KB of cells
+    static constexpr int lut = gpw * kLutBytes;         // tables; x is staged in the first gpw * 256 B
+    static constexpr int scales = ROWS * gpw * 4;       // 1 KB: one dword per (row, group) at most;
+                                                        // the wave's partial sums once the lookups end
+    static constexpr int wave = tile + lut + scales;    // 13 KB (ROWS 64) or 21 KB (ROWS 32)
+    static constexpr int max_waves = (160 * 1024) / wave;   // 12 or 7
+    static constexpr int rows_per_copy = 1024 / (gpw * 16);  // tile rows per 1 KB copy
+    // the 16-byte cell of (row r, group u) sits at gpw * 16 * r + 16 (u ^ swz(r))
+    static __device__ __forceinline__ int swz(int r) { return (r / (16 / gpw)) & (gpw - 1); }
+};
+
+// Ordering point for the compiler only: no memory access moves across it.
+__device__ __forceinline__ void compiler_fence() { asm volatile("" : : : "memory"); }
+
+// Eight 8-byte LDS reads at addr + 128 k (k < 8), after WAIT (an s_waitcnt, or nothing), and
+// waited for in the same block.
+#define BONSAI_L4_XREAD8(WAIT, Q, ADDR)                                                                \
+    asm volatile(WAIT "ds_read_b64 %0, %8\n\tds_read_b64 %1, %8 offset:128\n\t"                        \
+                 "ds_read_b64 %2, %8 offset:256\n\tds_read_b64 %3, %8 offset:384\n\t"                  \
+                 "ds_read_b64 %4, %8 offset:512\n\tds_read_b64 %5, %8 offset:640\n\t"                  \
+                 "ds_read_b64 %6, %8 offset:768\n\tds_read_b64 %7, %8 offset:896\n\t"                  \
+                 "s_waitcnt lgkmcnt(0)"                                                                \
+                 : "=&v"((Q)[0]), "=&v"((Q)[1]), "=&v"((Q)[2]), "=&v"((Q)[3]), "=&v"((Q)[4]),          \
+                   "=&v"((Q)[5]), "=&v"((Q)[6]), "=&v"((Q)[7])                                         \
+                 : "v"(ADDR)                                                                           \
+                 : "memory")
+
+// PAIRS: G is even, so the scales of groups 2p, 2p + 1 of a row are one aligned dword.
+template <int ROWS, bool PAIRS>
+__global__ __launch_bounds__(L4<ROWS>::max_waves * 64) void q1_gemv_lut4_kernel(const uint32_t *__restrict__ wbits,
+                                                                                const uint16_t *__restrict__ scales,
+                                                                                const uint16_t *__restrict__ x,
+                                                                                float *__restrict__ y, int N, int K)
+{
+    using L = L4<ROWS>;
     extern __shared__ u32x4 lds[];
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int nwaves = blockDim.x >> 6;
     const int G = K >> 7;
-    const int g0 = wave * kL4Groups, g1 = min(G, g0 + kL4Groups), gl = g1 - 1;
-    const int row = blockIdx.x * 64 + lane;
-    char *const tile = reinterpret_cast<char *>(lds) + wave * kL4Wave;
-    char *const lut = tile + kL4Tile;
-    float *const part = reinterpret_cast<float *>(lut + kL4Lut);
+    const int g0 = wave * L::gpw, g1 = min(G, g0 + L::gpw), gl = g1 - 1;
+    const int r = lane % ROWS, h = lane / ROWS;             // this lane's row and group quarter
+    const int n0 = blockIdx.x * ROWS;
+    char *const tile = reinterpret_cast<char *>(lds) + wave * L::wave;
+    char *const lut = tile + L::tile;
+    char *const sc = lut + L::lut;
+    float *const part = reinterpret_cast<float *>(sc);
 
-    // tile copy: instruction k covers rows 16 k .. 16 k + 15, 4 lanes per row; the cell of
-    // (row r, group u) lands at 64 r + 16 (u ^ ((r >> 2) & 3))
+    // x: copy j, lane l brings x[128 g0 + 512 j + 8 l .. + 7] to lut + 1 KB j + 16 l (clamped
+    // inside x past K)
+    const u32x4 *xg = reinterpret_cast<const u32x4 *>(x);
+#pragma unroll
+    for (int j = 0; j < L::gpw / 4; ++j)
+        __builtin_amdgcn_global_load_lds((glb_void_t *)(xg + min(16 * g0 + 64 * j + lane, 16 * G - 1)),
+                                         (lds_void_t *)(lut + 1024 * j), 16, 0, 0);
+    compiler_fence();
+    // tile: copy k covers rows rows_per_copy * k + lane / gpw, one 16-byte cell per lane
     const u32x4 *wg = reinterpret_cast<const u32x4 *>(wbits);
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
-        const int r = 16 * k + (lane >> 2);
-        const int gg = min(g0 + ((lane & 3) ^ ((r >> 2) & 3)), gl);
-        const int rr = min(blockIdx.x * 64 + r, N - 1);
-        __builtin_amdgcn_global_load_lds((glb_void_t *)(wg + (size_t)rr * G + gg),
+        const int rr = L::rows_per_copy * k + lane / L::gpw;
+        const int gg = min(g0 + ((lane % L::gpw) ^ L::swz(rr)), gl);
+        __builtin_amdgcn_global_load_lds((glb_void_t *)(wg + (size_t)min(n0 + rr, N - 1) * G + gg),
                                          (lds_void_t *)(tile + k * 1024), 16, 0, 0);
     }
-    const uint16_t *srow = scales + (size_t)min(row, N - 1) * G;
-    uint2 scv;                                      // VEC_SCALES: the 4 scales as loaded
-    uint32_t scs[kL4Groups];
-    if constexpr (VEC_SCALES) {
-        scv = *reinterpret_cast<const uint2 *>(srow + g0);
-    } else {
+    // scales: element d = 64 k + lane of copy k is (row d % ROWS, pair d / ROWS) for PAIRS
+    // (4 bytes), else (row d % ROWS, group d / ROWS) (2 bytes, the low half of its dword); it
+    // lands in the dword at sc + 4 d
+    constexpr int kScaleCopies = PAIRS ? 2 : 4;
 #pragma unroll
-        for (int u = 0; u < kL4Groups; ++u) scs[u] = srow[min(g0 + u, gl)];
+    for (int k = 0; k < kScaleCopies; ++k) {
+        const int d = 64 * k + lane;
+        const size_t rbase = (size_t)min(n0 + d % ROWS, N - 1) * G;
+        if constexpr (PAIRS)
+            __builtin_amdgcn_global_load_lds((glb_void_t *)(scales + rbase + min(g0 + 2 * (d / ROWS), G - 2)),
+                                             (lds_void_t *)(sc + 256 * k), 4, 0, 0);
+        else
+            __builtin_amdgcn_global_load_lds((glb_void_t *)(scales + rbase + min(g0 + d / ROWS, gl)),
+                                             (lds_void_t *)(sc + 256 * k), 2, 0, 0);
     }
+    compiler_fence();
 
-    // tables: lane builds quads e = lane + 64 k of the wave's 4 groups (group u = e / 128,
-    // chunk c, entries 4 bt .. 4 bt + 3), from x loaded all at once
-    uint2 xq[8];
+    // x quads: quad k of this lane is x[128 g0 + 64 k + 4 (lane / 4) .. + 3], at
+    // lut + 128 k + 8 (lane / 4); the first block waits until at most the tile and scale
+    // copies are in flight
+    constexpr int kQuads = 8 * L::lpr;
+    uint2 xq[kQuads];
+    const uint32_t xa = (uint32_t)(uintptr_t)((lds_char_t *)lut) + 8 * (lane >> 2);
+    if constexpr (PAIRS) BONSAI_L4_XREAD8("s_waitcnt vmcnt(6)\n\t", xq, xa);
+    else BONSAI_L4_XREAD8("s_waitcnt vmcnt(8)\n\t", xq, xa);
+    if constexpr (kQuads == 16) BONSAI_L4_XREAD8("", xq + 8, xa + 1024);
+
+    // tables: lane builds quads e = lane + 64 k of the wave's groups (group e / 128, chunk
+    // (e / 4) % 32, entries 4 bt .. 4 bt + 3); they overwrite the staged x, which this wave
+    // alone has read, and whose reads have completed
+    const uint32_t lut_lane = (uint32_t)(uintptr_t)((lds_char_t *)lut) + 16 * lane;
 #pragma unroll
-    for (int k = 0; k < 8; ++k) {
-        const int e = lane + 64 * k;
-        xq[k] = *reinterpret_cast<const uint2 *>(x + (size_t)min(g0 + (e >> 7), gl) * 128 + 4 * ((e >> 2) & 31));
-    }
-#pragma unroll
-    for (int k = 0; k < 8; ++k) {
-        const int e = lane + 64 * k;
-        const int u = e >> 7, c = (e >> 2) & 31, bt = e & 3;
+    for (int k = 0; k < kQuads; ++k) {
+        const int bt = lane & 3;                    // quad e = lane + 64 k: bt = e % 4
         const half2_t p01 = as_half2(xq[k].x), p23 = as_half2(xq[k].y);
         const float x0 = (float)p01[0], x1 = (float)p01[1];
         const float sg2 = (bt & 1) ? 1.f : -1.f, sg3 = (bt & 2) ? 1.f : -1.f;
@@ -263,20 +327,29 @@ __global__ __launch_bounds__(kL4MaxWaves * 64) void q1_gemv_lut4_kernel(const ui
         ev[1] = __builtin_bit_cast(uint32_t, fmaf(2.f, x0, base));                 // v = 4bt + 1
         ev[2] = __builtin_bit_cast(uint32_t, fmaf(2.f, x1, base));                 // v = 4bt + 2
         ev[3] = __builtin_bit_cast(uint32_t, fmaf(2.f, x1, fmaf(2.f, x0, base)));  // v = 4bt + 3
-        *reinterpret_cast<u32x4 *>(lut + u * kLutBytes + 64 * c + 16 * bt) = ev;
+        // quad e sits at lut + (e / 128) * 2 KB + 64 ((e / 4) % 32) + 16 (e % 4) = lut + 16 lane + 1 KB * k
+        lds_store_b128(lut_lane + 1024 * k, ev);
     }
-    __builtin_amdgcn_s_waitcnt(0x0F70);             // vmcnt(0): the tile copy landed
+    __builtin_amdgcn_s_waitcnt(0x0F70);             // vmcnt(0): the tile and the scales landed
     __builtin_amdgcn_s_waitcnt(0xC07F);             // lgkmcnt(0): this wave's tables are written
 
+    // this lane's scales (row r, groups 4 h .. 4 h + 3 of the wave's), before the lookups
+    uint32_t sw[PAIRS ? 2 : 4];
+#pragma unroll
+    for (int k = 0; k < (PAIRS ? 2 : 4); ++k)
+        sw[k] = *reinterpret_cast<const uint32_t *>(sc + 4 * ((PAIRS ? 2 * h : 4 * h) + k) * ROWS + 4 * r);
+
     const uint32_t mask_3c = __builtin_amdgcn_readfirstlane(0x3Cu);
-    const uint32_t lut_addr = (uint32_t)(uintptr_t)((lds_char_t *)lut);
+    // the tables of this lane's 4 groups start at lut + 8 KB h (256-aligned)
+    const uint32_t lut_addr = (uint32_t)(uintptr_t)((lds_char_t *)lut) + 4 * kLutBytes * h;
     uint32_t raddr[16];
 #pragma unroll
     for (int j = 0; j < 16; ++j) raddr[j] = lut_addr;
     float acc = 0.f;
 #pragma unroll
-    for (int u = 0; u < kL4Groups; ++u) {
-        const u32x4 q = *reinterpret_cast<const u32x4 *>(tile + 64 * lane + 16 * (u ^ ((lane >> 2) & 3)));
+    for (int u = 0; u < 4; ++u) {
+        const int ug = 4 * h + u;                   // group of the wave's slice
+        const u32x4 q = *reinterpret_cast<const u32x4 *>(tile + L::gpw * 16 * r + 16 * (ug ^ L::swz(r)));
         float a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;
 #pragma unroll
         for (int i = 0; i < 4; i += 2) {
@@ -290,38 +363,42 @@ __global__ __launch_bounds__(kL4MaxWaves * 64) void q1_gemv_lut4_kernel(const ui
             a2 += (t[8] + t[9]) + (t[10] + t[11]);
             a3 += (t[12] + t[13]) + (t[14] + t[15]);
         }
-        uint32_t sbits;
-        if constexpr (VEC_SCALES) sbits = ((u & 2) ? scv.y : scv.x) >> (16 * (u & 1));
-        else sbits = scs[u];
+        const uint16_t sbits = (uint16_t)(PAIRS ? sw[u >> 1] >> (16 * (u & 1)) : sw[u]);
         // groups past K (the last wave's slice may be short) count with scale 0
-        const float s = (g0 + u < g1) ? f16_bits_to_f32((uint16_t)sbits) : 0.f;
+        const float s = (g0 + ug < g1) ? f16_bits_to_f32(sbits) : 0.f;
         acc = fmaf(s, (a0 + a1) + (a2 + a3), acc);
     }
-    part[lane] = acc;
+    part[lane] = acc;                               // the scales were read before the lookups
     __syncthreads();
-    if (wave == 0 && row < N) {
-        float t = acc;
-        for (int w = 1; w < nwaves; ++w)
-            t += reinterpret_cast<const float *>(reinterpret_cast<char *>(lds) + w * kL4Wave + kL4Tile + kL4Lut)[lane];
-        y[row] = t;
+    if (wave == 0 && lane < ROWS && n0 + lane < N) {
+        float t = 0.f;
+        for (int w = 0; w < nwaves; ++w) {
+            const float *pw = reinterpret_cast<const float *>(reinterpret_cast<char *>(lds) + w * L::wave + L::tile + L::lut);
+#pragma unroll
+            for (int hh = 0; hh < L::lpr; ++hh) t += pw[hh * ROWS + lane];
+        }
+        y[n0 + lane] = t;
     }
 }
+#undef BONSAI_L4_XREAD8
 
+template <int ROWS>
 hipError_t launch_lut4(const uint32_t *wbits, const uint16_t *scales, const uint16_t *x, float *y,
                        int N, int K, hipStream_t stream)
 {
+    using L = L4<ROWS>;
     const int G = K / 128;
-    const int tiles = (N + 63) / 64;
-    const int waves = (G + kL4Groups - 1) / kL4Groups;
-    const size_t lds = (size_t)waves * kL4Wave;
-    const bool vec = (G % kL4Groups) == 0;          // every wave's scales then start 8-byte aligned
-    const void *fn = vec ? reinterpret_cast<const void *>(&q1_gemv_lut4_kernel<true>)
-                         : reinterpret_cast<const void *>(&q1_gemv_lut4_kernel<false>);
+    const int tiles = (N + ROWS - 1) / ROWS;
+    const int waves = (G + L::gpw - 1) / L::gpw;
+    const size_t lds = (size_t)waves * L::wave;
+    const bool pairs = (G % 2) == 0;                // a row's scale pairs are then dword aligned
+    const void *fn = pairs ? reinterpret_cast<const void *>(&q1_gemv_lut4_kernel<ROWS, true>)
+                           : reinterpret_cast<const void *>(&q1_gemv_lut4_kernel<ROWS, false>);
     static const bool attrs_set = [] {
-        const int most = kL4MaxWaves * kL4Wave;
-        return hipFuncSetAttribute(reinterpret_cast<const void *>(&q1_gemv_lut4_kernel<true>),
+        const int most = L::max_waves * L::wave;
+        return hipFuncSetAttribute(reinterpret_cast<const void *>(&q1_gemv_lut4_kernel<ROWS, true>),
                                    hipFuncAttributeMaxDynamicSharedMemorySize, most) == hipSuccess &&
-               hipFuncSetAttribute(reinterpret_cast<const void *>(&q1_gemv_lut4_kernel<false>),
+               hipFuncSetAttribute(reinterpret_cast<const void *>(&q1_gemv_lut4_kernel<ROWS, false>),
                                    hipFuncAttributeMaxDynamicSharedMemorySize, most) == hipSuccess;
     }();
     if (!attrs_set) return hipErrorInvalidValue;
@@ -355,9 +432,13 @@ hipError_t launch_q1_gemv(const uint32_t *wbits, const uint16_t *scales, const u
 {
     if (M >= 2 && M <= 8) return launch_gemv_mfma(false, wbits, scales, x, y, M, N, K, stream);
     if (M != 1) return hipErrorInvalidValue;
-    // one tile per CU at most and the 4-group slices of K fit one workgroup: small-N kernel
-    if ((N + 63) / 64 <= 256 && (K / 128 + kL4Groups - 1) / kL4Groups <= kL4MaxWaves)
-        return launch_lut4(wbits, scales, x, y, N, K, stream);
+    // small N: one tile per CU at most, and the wave slices of K fit one workgroup; 32-row
+    // tiles while they still fit, for twice the CUs
+    const int G = K / 128;
+    if ((N + 31) / 32 <= 256 && (G + L4<32>::gpw - 1) / L4<32>::gpw <= L4<32>::max_waves)
+        return launch_lut4<32>(wbits, scales, x, y, N, K, stream);
+    if ((N + 63) / 64 <= 256 && (G + L4<64>::gpw - 1) / L4<64>::gpw <= L4<64>::max_waves)
+        return launch_lut4<64>(wbits, scales, x, y, N, K, stream);
     return launch_lut(wbits, scales, x, y, N, K, stream);
 }
 
