@@ -18,6 +18,16 @@ __device__ __forceinline__ float f16_bits_to_f32(uint16_t h)
     return (float)__builtin_bit_cast(_Float16, h);
 }
 
+// s_waitcnt as asm statements with a memory clobber.  The builtin is modelled as touching no
+// memory, so the compiler may move a load above it; no memory access moves across these.  Any
+// LDS read of data that a direct global->LDS copy brings in is ordered after one of them.
+template <int N>
+__device__ __forceinline__ void vm_wait()
+{
+    asm volatile("s_waitcnt vmcnt(%0)" : : "n"(N) : "memory");
+}
+__device__ __forceinline__ void lgkm_wait0() { asm volatile("s_waitcnt lgkmcnt(0)" : : : "memory"); }
+
 // Two binary16 halves picked from two dwords: (lo(a), lo(b)) or (hi(a), hi(b)).
 // One v_perm_b32 each: selector bytes 0..3 pick bytes of the second source (a), 4..7 of the first (b).
 __device__ __forceinline__ uint32_t pack_lo(uint32_t a, uint32_t b) { return __builtin_amdgcn_perm(b, a, 0x05040100u); }

@@ -133,7 +133,7 @@ __global__ __launch_bounds__(sm_max_waves(RT) * 64) void gemv_mfma_kernel(const 
         for (int m = 0; m < M; ++m)
             __builtin_amdgcn_global_load_lds((glb_void_t *)(xg + (size_t)m * (K >> 3) + min(16 * g0 + lane, (K >> 3) - 1)),
                                              (lds_void_t *)(xs + m * L::xstride), 16, 0, 0);
-        __builtin_amdgcn_s_waitcnt(0x0F70);               // vmcnt(0): this wave's slice landed
+        vm_wait<0>();                                     // this wave's slice landed
         if (g1 - g0 < kSmGroups) {
             // groups past K (last slice only) hold clamped copies: their scales become zero
             for (int e = lane; e < R * kSmGroups; e += 64) {
@@ -229,7 +229,7 @@ __global__ __launch_bounds__(sm_max_waves(RT) * 64) void gemv_mfma_kernel(const 
                     acc[t][r] = fmaf((float)h[PAIRS ? u & 1 : 0], d[t][r], acc[t][r]);
                 }
         }
-        __builtin_amdgcn_s_waitcnt(0xC07F);               // LDS reads done before the next slice's copies
+        lgkm_wait0();                                     // LDS reads done before the next slice's copies
     }
 
     // D rows 16 t + 4 q + r, column i16: the wave's partial sums into red[wave][column][row]

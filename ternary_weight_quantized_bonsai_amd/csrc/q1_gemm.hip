@@ -61,11 +61,11 @@ typedef float float16_t __attribute__((ext_vector_type(16)));
 typedef __attribute__((address_space(3))) void lds_void_t;
 typedef __attribute__((address_space(1))) const void glb_void_t;
 
-// s_waitcnt vmcnt(n) (fields: vmcnt [3:0] and [15:14], expcnt [6:4], lgkmcnt [11:8])
+// s_waitcnt vmcnt(n), as an asm statement no memory access moves across
 template <int n>
 __device__ __forceinline__ void wait_vmcnt()
 {
-    __builtin_amdgcn_s_waitcnt((n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8));
+    vm_wait<n>();
 }
 
 // sched_group_barrier masks

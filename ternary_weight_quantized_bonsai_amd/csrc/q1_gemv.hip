@@ -136,7 +136,7 @@ __global__ __launch_bounds__(384) void q1_gemv_lut_kernel(const uint32_t *__rest
     float acc = 0.f;
     issue(g0);
     for (int gb = g0; gb < g1; gb += B) {
-        __builtin_amdgcn_s_waitcnt(0x0F70);             // vmcnt(0): tile and scales of this batch
+        vm_wait<0>();                                   // tile and scales of this batch
 #pragma unroll
         for (int u = 0; u < B; ++u) {
             const int g = gb + u;
@@ -176,7 +176,7 @@ __global__ __launch_bounds__(384) void q1_gemv_lut_kernel(const uint32_t *__rest
             }
             acc = fmaf(sc[u], (a0 + a1) + (a2 + a3), acc);
         }
-        __builtin_amdgcn_s_waitcnt(0xC07F);             // lgkmcnt(0): tile reads done before reuse
+        lgkm_wait0();                                   // tile reads done before reuse
         if (gb + B < g1) issue(gb + B);
     }
 
@@ -330,8 +330,8 @@ __global__ __launch_bounds__(L4<ROWS>::max_waves * 64) void q1_gemv_lut4_kernel(
         // quad e sits at lut + (e / 128) * 2 KB + 64 ((e / 4) % 32) + 16 (e % 4) = lut + 16 lane + 1 KB * k
         lds_store_b128(lut_lane + 1024 * k, ev);
     }
-    __builtin_amdgcn_s_waitcnt(0x0F70);             // vmcnt(0): the tile and the scales landed
-    __builtin_amdgcn_s_waitcnt(0xC07F);             // lgkmcnt(0): this wave's tables are written
+    vm_wait<0>();                                   // the tile and the scales landed
+    lgkm_wait0();                                   // this wave's tables are written
 
     // this lane's scales (row r, groups 4 h .. 4 h + 3 of the wave's), before the lookups
     uint32_t sw[PAIRS ? 2 : 4];
@@ -380,7 +380,6 @@ __global__ __launch_bounds__(L4<ROWS>::max_waves * 64) void q1_gemv_lut4_kernel(
         y[n0 + lane] = t;
     }
 }
-#undef BONSAI_L4_XREAD8
 
 template <int ROWS>
 hipError_t launch_lut4(const uint32_t *wbits, const uint16_t *scales, const uint16_t *x, float *y,
@@ -406,6 +405,205 @@ hipError_t launch_lut4(const uint32_t *wbits, const uint16_t *scales, const uint
     return launch_kernel(fn, dim3(tiles), dim3(64 * waves), args, lds, stream);
 }
 
+// ---- M = 1, large N: persistent workgroups, tables built once ------------------------------
+//
+// With many row tiles, rebuilding the tables for every tile costs as much VALU work as the
+// lookups.  Here one workgroup per CU builds the tables of every group of K once (2 KB per
+// group, shared by its waves) and each wave then owns whole 64-row tiles: wave gw of the W
+// waves in the grid takes tiles gw, gw + W, ..., and lane r accumulates row r over all of K,
+// so no partial sums cross waves (gw numbers the waves wave-major, gw = wave * grid + block,
+// so that fewer tiles than waves still spread over every CU).  A tile goes past in batches of 4 groups (64 rows x 64 B of
+// sign words and the rows' scales), double buffered in the wave's LDS: the copies of batch
+// i + 1 are in flight while batch i is looked up.  Every iteration issues exactly one batch's
+// copies (past the wave's last batch, that batch again), so one wait with a fixed count finds
+// the older batch landed.
+constexpr int kLPGroups = 4;
+constexpr int kLPTile = 64 * kLPGroups * 16;        // 4 KB of cells per batch
+constexpr int kLPScales = 64 * kLPGroups * 4;       // 1 KB: one dword per (row, group) at most
+constexpr int kLPBuf = kLPTile + kLPScales;         // 5 KB; buffer 1 first stages the wave's x
+constexpr int kLPMaxWaves = 8;
+constexpr int kLPMaxPer = kLPBuf / 256;             // groups of x one buffer can stage
+
+template <bool PAIRS>
+__global__ __launch_bounds__(kLPMaxWaves * 64) void q1_gemv_lutp_kernel(const uint32_t *__restrict__ wbits,
+                                                                        const uint16_t *__restrict__ scales,
+                                                                        const uint16_t *__restrict__ x,
+                                                                        float *__restrict__ y, int N, int K)
+{
+    extern __shared__ u32x4 lds[];
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int nwaves = blockDim.x >> 6;
+    const int G = K >> 7;
+    const int nb = (G + kLPGroups - 1) / kLPGroups;         // batches per tile
+    const int GT = kLPGroups * nb;                          // groups with tables (past G: scale 0)
+    char *const tables = reinterpret_cast<char *>(lds);     // group g at tables + 2 KB g
+    char *const bufs = tables + GT * kLutBytes + wave * (2 * kLPBuf);
+    const int tiles = (N + 63) / 64;
+    const int W = gridDim.x * nwaves;
+    const int gw = wave * gridDim.x + blockIdx.x;
+    const int nbat = (gw < tiles ? (tiles - 1 - gw) / W + 1 : 0) * nb;     // this wave's batches
+    const u32x4 *wg = reinterpret_cast<const u32x4 *>(wbits);
+    constexpr int kCopies = 4 + (PAIRS ? 2 : 4);            // copies per batch
+
+    // batch i of this wave (tile i / nb, groups 4 (i % nb) ..) into buffer i % 2
+    auto issue = [&](int i) {
+        const int ic = min(i, max(nbat - 1, 0));
+        const int n0 = (gw + W * (ic / nb)) * 64;           // rows clamp to N - 1 (a wave without tiles too)
+        const int g0 = kLPGroups * (ic % nb);
+        char *const buf = bufs + (i & 1) * kLPBuf;
+        // cells: copy k covers rows 16 k .. 16 k + 15, 4 lanes per row; cell (r, u) at 64 r + 16 (u ^ ((r >> 2) & 3))
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const int r = 16 * k + (lane >> 2);
+            const int gg = min(g0 + ((lane & 3) ^ ((r >> 2) & 3)), G - 1);
+            __builtin_amdgcn_global_load_lds((glb_void_t *)(wg + (size_t)min(n0 + r, N - 1) * G + gg),
+                                             (lds_void_t *)(buf + 1024 * k), 16, 0, 0);
+        }
+        // scales of row `lane`: PAIRS, copy p brings groups g0 + 2p, g0 + 2p + 1 as the dword at
+        // buf + 4 KB + 256 p + 4 lane; else copy u brings group g0 + u as that dword's low half
+        const size_t rbase = (size_t)min(n0 + lane, N - 1) * G;
+#pragma unroll
+        for (int k = 0; k < (PAIRS ? 2 : 4); ++k) {
+            if constexpr (PAIRS)
+                __builtin_amdgcn_global_load_lds((glb_void_t *)(scales + rbase + min(g0 + 2 * k, G - 2)),
+                                                 (lds_void_t *)(buf + kLPTile + 256 * k), 4, 0, 0);
+            else
+                __builtin_amdgcn_global_load_lds((glb_void_t *)(scales + rbase + min(g0 + k, G - 1)),
+                                                 (lds_void_t *)(buf + kLPTile + 256 * k), 2, 0, 0);
+        }
+    };
+
+    // tables: this wave builds groups [ga, gb) from their x, staged in its buffer 1: copy j,
+    // lane l brings x[128 ga + 512 j + 8 l .. + 7] (clamped inside x) to buffer 1 + 1 KB j + 16 l
+    const int per = (GT + nwaves - 1) / nwaves;             // at most kLPMaxPer (host check)
+    const int ga = min(GT, wave * per), gb = min(GT, ga + per);
+    char *const xs = bufs + kLPBuf;
+    const u32x4 *xg = reinterpret_cast<const u32x4 *>(x);
+    for (int j = 0; j < (gb - ga + 3) / 4; ++j)
+        __builtin_amdgcn_global_load_lds((glb_void_t *)(xg + min(16 * ga + 64 * j + lane, 16 * G - 1)),
+                                         (lds_void_t *)(xs + 1024 * j), 16, 0, 0);
+    compiler_fence();
+    issue(0);
+    compiler_fence();
+
+    // quad k of this lane: group ga + k / 2, chunk 16 (k % 2) + lane / 4, entries 4 bt .. + 3
+    // (bt = lane % 4), from x[128 ga + 64 k + 4 (lane / 4) .. + 3] at xs + 128 k + 8 (lane / 4);
+    // it goes to tables + 2 KB ga + 1 KB k + 16 lane.  Quads are read 8 at a time, the first
+    // eight once at most batch 0's copies are in flight.
+    const uint32_t xa = (uint32_t)(uintptr_t)((lds_char_t *)xs) + 8 * (lane >> 2);
+    const uint32_t tl = (uint32_t)(uintptr_t)((lds_char_t *)tables) + kLutBytes * ga + 16 * lane;
+    const int nq = 2 * (gb - ga);
+    for (int kb = 0; kb < nq; kb += 8) {
+        uint2 xq[8];
+        if (kb == 0) {
+            if constexpr (PAIRS) BONSAI_L4_XREAD8("s_waitcnt vmcnt(6)\n\t", xq, xa);
+            else BONSAI_L4_XREAD8("s_waitcnt vmcnt(8)\n\t", xq, xa);
+        } else {
+            BONSAI_L4_XREAD8("", xq, xa + 128 * kb);
+        }
+        const int bt = lane & 3;
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+            if (kb + k >= nq) break;
+            const half2_t p01 = as_half2(xq[k].x), p23 = as_half2(xq[k].y);
+            const float x0 = (float)p01[0], x1 = (float)p01[1];
+            const float sg2 = (bt & 1) ? 1.f : -1.f, sg3 = (bt & 2) ? 1.f : -1.f;
+            const float base = fmaf(sg3, (float)p23[1], fmaf(sg2, (float)p23[0], -x0 - x1));
+            u32x4 ev;
+            ev[0] = __builtin_bit_cast(uint32_t, base);                                 // v = 4bt
+            ev[1] = __builtin_bit_cast(uint32_t, fmaf(2.f, x0, base));                 // v = 4bt + 1
+            ev[2] = __builtin_bit_cast(uint32_t, fmaf(2.f, x1, base));                 // v = 4bt + 2
+            ev[3] = __builtin_bit_cast(uint32_t, fmaf(2.f, x1, fmaf(2.f, x0, base)));  // v = 4bt + 3
+            lds_store_b128(tl + 1024 * (kb + k), ev);
+        }
+    }
+    issue(1);                                       // buffer 1: its staged x has been read
+    lgkm_wait0();                                   // this wave's tables are written ...
+    asm volatile("s_barrier" : : : "memory");       // ... and every wave's
+
+    const uint32_t mask_3c = __builtin_amdgcn_readfirstlane(0x3Cu);
+    const uint32_t tbase = (uint32_t)(uintptr_t)((lds_char_t *)tables);
+    float acc = 0.f;
+    int b = 0, t = gw;                              // batch of the tile, tile
+    for (int i = 0; i < nbat; ++i) {
+        vm_wait<kCopies>();                         // batch i landed; batch i + 1 may be in flight
+        const char *buf = bufs + (i & 1) * kLPBuf;
+        uint32_t sw[PAIRS ? 2 : 4];
+#pragma unroll
+        for (int k = 0; k < (PAIRS ? 2 : 4); ++k) sw[k] = *reinterpret_cast<const uint32_t *>(buf + kLPTile + 256 * k + 4 * lane);
+        // tables of groups 4 b .. 4 b + 3 start at tbase + 8 KB b (256-aligned)
+        uint32_t raddr[16];
+#pragma unroll
+        for (int j = 0; j < 16; ++j) raddr[j] = tbase + 4 * kLutBytes * b;
+#pragma unroll
+        for (int u = 0; u < kLPGroups; ++u) {
+            const u32x4 q = *reinterpret_cast<const u32x4 *>(buf + 64 * lane + 16 * (u ^ ((lane >> 2) & 3)));
+            float a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;
+#pragma unroll
+            for (int i2 = 0; i2 < 4; i2 += 2) {
+                word_addrs(q[i2], &raddr[0], mask_3c);
+                word_addrs(q[i2 + 1], &raddr[8], mask_3c);
+                float tv[16];
+#pragma unroll
+                for (int j = 0; j < 16; ++j) tv[j] = lds_f32(raddr[j], u * kLutBytes + 64 * (8 * i2 + j));
+                a0 += (tv[0] + tv[1]) + (tv[2] + tv[3]);
+                a1 += (tv[4] + tv[5]) + (tv[6] + tv[7]);
+                a2 += (tv[8] + tv[9]) + (tv[10] + tv[11]);
+                a3 += (tv[12] + tv[13]) + (tv[14] + tv[15]);
+            }
+            const uint16_t sbits = (uint16_t)(PAIRS ? sw[u >> 1] >> (16 * (u & 1)) : sw[u]);
+            const float s = (kLPGroups * b + u < G) ? f16_bits_to_f32(sbits) : 0.f;
+            acc = fmaf(s, (a0 + a1) + (a2 + a3), acc);
+        }
+        if (++b == nb) {                            // the tile is complete
+            const int row = 64 * t + lane;
+            if (row < N) y[row] = acc;
+            acc = 0.f;
+            b = 0;
+            t += W;
+        }
+        lgkm_wait0();                               // this buffer's reads are done before it refills
+        issue(i + 2);
+    }
+    vm_wait<0>();                                   // no copy into LDS outlives the wave
+}
+
+template <bool PAIRS>
+size_t lutp_lds(int G, int nwaves) { return (size_t)kLutBytes * 4 * ((G + 3) / 4) + (size_t)nwaves * 2 * kLPBuf; }
+
+// Waves per workgroup for the persistent kernel (0: the tables of K do not fit the LDS).
+int lutp_waves(int G)
+{
+    const int GT = 4 * ((G + 3) / 4);
+    const long room = 160L * 1024 - (long)kLutBytes * GT;
+    int nw = room > 0 ? (int)(room / (2 * kLPBuf)) : 0;
+    if (nw > kLPMaxWaves) nw = kLPMaxWaves;
+    if (nw < 4 || (GT + nw - 1) / nw > kLPMaxPer) return 0;
+    return nw;
+}
+
+hipError_t launch_lutp(const uint32_t *wbits, const uint16_t *scales, const uint16_t *x, float *y,
+                       int N, int K, int nwaves, hipStream_t stream)
+{
+    constexpr int kCus = 256;
+    const int G = K / 128;
+    const int tiles = (N + 63) / 64;
+    const int grid = min(kCus, (tiles + nwaves - 1) / nwaves);
+    const size_t lds = lutp_lds<true>(G, nwaves);
+    const bool pairs = (G % 2) == 0;
+    const void *fn = pairs ? reinterpret_cast<const void *>(&q1_gemv_lutp_kernel<true>)
+                           : reinterpret_cast<const void *>(&q1_gemv_lutp_kernel<false>);
+    static const bool attrs_set =
+        hipFuncSetAttribute(reinterpret_cast<const void *>(&q1_gemv_lutp_kernel<true>),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024) == hipSuccess &&
+        hipFuncSetAttribute(reinterpret_cast<const void *>(&q1_gemv_lutp_kernel<false>),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024) == hipSuccess;
+    if (!attrs_set) return hipErrorInvalidValue;
+    void *args[] = {&wbits, &scales, &x, &y, &N, &K};
+    return launch_kernel(fn, dim3(grid), dim3(64 * nwaves), args, lds, stream);
+}
+
 hipError_t launch_lut(const uint32_t *wbits, const uint16_t *scales, const uint16_t *x, float *y,
                       int N, int K, hipStream_t stream)
 {
@@ -425,6 +623,8 @@ hipError_t launch_lut(const uint32_t *wbits, const uint16_t *scales, const uint1
                          args, lds, stream);
 }
 
+#undef BONSAI_L4_XREAD8
+
 }  // namespace
 
 hipError_t launch_q1_gemv(const uint32_t *wbits, const uint16_t *scales, const uint16_t *x, float *y,
@@ -439,6 +639,8 @@ hipError_t launch_q1_gemv(const uint32_t *wbits, const uint16_t *scales, const u
         return launch_lut4<32>(wbits, scales, x, y, N, K, stream);
     if ((N + 63) / 64 <= 256 && (G + L4<64>::gpw - 1) / L4<64>::gpw <= L4<64>::max_waves)
         return launch_lut4<64>(wbits, scales, x, y, N, K, stream);
+    // large N: persistent workgroups with the tables of all of K, when they fit the LDS
+    if (const int nw = lutp_waves(G)) return launch_lutp(wbits, scales, x, y, N, K, nw, stream);
     return launch_lut(wbits, scales, x, y, N, K, stream);
 }
 

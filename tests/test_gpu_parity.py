@@ -142,7 +142,12 @@ def test_q1_gemm_identity_gives_dequantized_weights(orc):
 # ---- ragged and edge shapes ---------------------------------------------------------------
 EDGE = {
     "q1_gemv": [(1, 1, 128), (1, 63, 256), (1, 65, 384), (3, 1000, 1152), (8, 777, 2048), (5, 64, 128),
-                (2, 130, 131072), (1, 4097, 640)],
+                (2, 130, 131072), (1, 4097, 640),
+                # M = 1 around the kernel boundaries: 32-row tiles up to N = 8192, 64-row tiles up
+                # to 16384, then the persistent kernel (odd G, G not a multiple of 4, ragged N, the
+                # most groups whose tables fit), and past that K the batched kernel
+                (1, 8192, 640), (1, 8193, 640), (1, 16384, 384), (1, 16385, 1152), (1, 20000, 640),
+                (1, 40000, 256), (1, 17000, 6144), (1, 16500, 8192)],
     "q2t_gemv": [(1, 1, 128), (1, 63, 256), (2, 65, 384), (8, 1000, 1152), (7, 777, 2048),
                  (1, 130, 131072), (4, 4097, 640)],
     "q1_gemm": [(1, 1, 128), (17, 100, 256), (130, 257, 384), (128, 128, 512), (256, 384, 1024),
