@@ -252,6 +252,37 @@ def summarize_pmc(fetch_dir: str, write_dir: str, out: str, cmds: list[str], ker
     print((ROOT / "profiles" / out).read_text())
 
 
+def summarize_counters(d: str, out: str, cmds: list[str]) -> None:
+    """Mean of every collected counter per (kernel, grid) from a --pmc run (values per dispatch,
+    summed over the hardware instances by rocprofv3; derived metrics as rocprofv3 computes them)."""
+    rows = _csv_rows(d, "_counter_collection.csv")
+    per = {}
+    names = []
+    for r in rows:
+        k = (short_name(r["Kernel_Name"]), int(r["Grid_Size"]))
+        c = r["Counter_Name"]
+        if c not in names:
+            names.append(c)
+        per.setdefault(k, {}).setdefault(c, {})[r["Dispatch_Id"]] = float(r["Counter_Value"])
+    lines = [f"# rocprofv3 counters: {out}", "# command:"] + [f"#   {c}" for c in cmds]
+    lines += ["# summarised by: python bench.py --summarize-counters <output dir> --out " + out,
+              "# mean per dispatch over the dispatches of each (kernel, grid)", "",
+              "kernel | grid (threads) | dispatches | " + " | ".join(names),
+              "---|---|---|" + "|".join("---" for _ in names)]
+    for (kname, grid), cs in sorted(per.items()):
+        if kname.startswith("__amd") or kname.startswith("at::"):
+            continue
+        n = max(len(v) for v in cs.values())
+        vals = []
+        for c in names:
+            v = list(cs.get(c, {}).values())
+            vals.append(f"{sum(v) / len(v):.4g}" if v else "")
+        lines.append(f"{kname} | {grid} | {n} | " + " | ".join(vals))
+    (ROOT / "profiles").mkdir(exist_ok=True)
+    (ROOT / "profiles" / out).write_text("\n".join(lines) + "\n")
+    print((ROOT / "profiles" / out).read_text())
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -263,11 +294,16 @@ def main() -> int:
     ap.add_argument("--summarize-trace", metavar="DIR", help="write a profiles/ summary of a kernel-trace run")
     ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="write the profiles/ HBM-traffic summary of the decode GEMV from two --pmc runs")
+    ap.add_argument("--summarize-counters", metavar="DIR",
+                    help="write a profiles/ summary of any rocprofv3 --pmc run (mean per kernel and grid)")
     ap.add_argument("--out", help="file name under profiles/ for --summarize-*")
     ap.add_argument("--cmd", action="append", default=[], help="profiler command recorded in the summary")
     args = ap.parse_args()
     if args.summarize_trace:
         summarize_trace(args.summarize_trace, args.out, args.cmd)
+        return 0
+    if args.summarize_counters:
+        summarize_counters(args.summarize_counters, args.out, args.cmd)
         return 0
     if args.summarize_pmc:
         summarize_pmc(*args.summarize_pmc, args.out, args.cmd, HEADLINE_KERNEL,
