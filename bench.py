@@ -399,6 +399,36 @@ def main() -> int:
                 "per_shape_us": {"mlp_13824x5120": round(t_mlp * 1e3, 3), "attn_5120x5120": round(t_attn * 1e3, 3)}}
     log(f"q1_gemv device time: mlp {t_mlp * 1e3:.2f} us, attn {t_attn * 1e3:.2f} us -> {achieved:.1f} GB/s")
 
+    # ---- launch floor: the same two calls per step with no work (K = 0 launches one kernel
+    # that zero-fills y), timed both ways the headline is ----------------------------------
+    z_w = torch.empty((64, 0), dtype=torch.int32, device=dev)
+    z_s = torch.empty((64, 0), dtype=torch.int16, device=dev)
+    z_x = torch.empty((1, 0), dtype=torch.int16, device=dev)
+    z_y = torch.empty((1, 64), dtype=torch.float32, device=dev)
+
+    def zcall():
+        bonsai.q1_gemv(z_w, z_s, z_x, out=z_y)
+
+    kt0 = kernel_times(hip, bonsai, [zcall] * n_t)
+    g_zero = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g_zero):
+        for _ in range(args.steps):
+            zcall()
+            zcall()
+    g_zero.replay()
+    torch.cuda.synchronize()
+    hip.record(e0, stream())
+    g_zero.replay()
+    hip.record(e1, stream())
+    torch.cuda.synchronize()
+    floor_step_us = hip.elapsed_ms(e0, e1) * 1e3 / args.steps
+    launch_floor = {"kernel_us": round(float(np.mean(kt0)) * 1e3, 3), "graph_step_us": round(floor_step_us, 3),
+                    "what": "the two decode calls of a step with K = 0 (each launches one kernel that zero-fills "
+                            "y), timed like the headline: per-launch events, and graph replay per step"}
+    roofline["launch_floor_us"] = launch_floor["kernel_us"]
+    log(f"launch floor: {launch_floor['kernel_us']:.2f} us per call, {floor_step_us:.2f} us per graph step "
+        f"(the headline step takes {ms * 1e3 / args.steps:.2f} us)")
+
     extra = {}
     if not args.headline_only:
         # LM head: N = 248320 vocabulary rows
@@ -494,6 +524,7 @@ def main() -> int:
         "roofline": roofline,
     }
     line["copy_probe"] = copy_probe
+    line["launch_floor"] = launch_floor
     line.update(extra)
     if not args.no_cpu_baseline:
         log("timing the CPU oracle")
