@@ -10,8 +10,9 @@ is issued), with inputs resident in HBM before the timed region starts.
 
 Beside it: the roofline of the dominant kernel (per-launch algorithmic bytes over the kernel's
 device duration, timed with HIP events recorded by hipExtLaunchKernel around each launch), the
-LM-head GEMV (N = 248320), the pp512 prefill GEMM (M = 512, N = 13824, K = 5120, TFLOP/s), the
-ternary decode GEMV (M = 1 and 8), a device copy probe, and the CPU oracle timed on the host.
+LM-head GEMV (N = 248320), the pp512 prefill GEMM (M = 512, N = 13824, K = 5120, TFLOP/s) for
+binary and ternary weights, the ternary decode GEMV (M = 1 and 8), a device copy probe, the
+launch floor of the decode step, and the CPU oracle timed on the host.
 
 Progress lines go to stderr.  Only the CPU-baseline leg touches the oracle.
 """
@@ -464,6 +465,24 @@ def main() -> int:
                                  "roofline": {"bound": "mfma", "achieved": round(tf, 2), "peak": PEAK_FP16_TFLOPS,
                                               "unit": "TFLOP/s", "frac": round(tf / PEAK_FP16_TFLOPS, 4)}}
         log(f"prefill gemm: {t4 * 1e3:.1f} us, {tf:.1f} TFLOP/s")
+        del ws, ss, w, s, x, y
+
+        # Ternary prefill GEMM at the same shape (2-bit codes)
+        w, s, x = (up(a) for a in synth.make_q2t(M4, N4, K))
+        ws = [w] + [w.clone() for _ in range(2)]
+        ss = [s] + [s.clone() for _ in range(2)]
+        y = torch.empty((M4, N4), dtype=torch.float32, device=dev)
+        bonsai.q2t_gemm(ws[0], ss[0], x, out=y)
+        kt6 = kernel_times(hip, bonsai, [lambda j=j: bonsai.q2t_gemm(ws[j % 3], ss[j % 3], x, out=y)
+                                         for j in range(30)])
+        t6 = float(np.mean(kt6))
+        tf6 = 2.0 * M4 * N4 * K / (t6 / 1e3) / 1e12
+        extra["ternary_prefill_gemm"] = {"shape": "M=512 N=13824 K=5120", "avg_kernel_us": round(t6 * 1e3, 2),
+                                         "TFLOPs": round(tf6, 2),
+                                         "roofline": {"bound": "mfma", "achieved": round(tf6, 2),
+                                                      "peak": PEAK_FP16_TFLOPS, "unit": "TFLOP/s",
+                                                      "frac": round(tf6 / PEAK_FP16_TFLOPS, 4)}}
+        log(f"ternary prefill gemm: {t6 * 1e3:.1f} us, {tf6:.1f} TFLOP/s")
         del ws, ss, w, s, x, y
 
         # Ternary decode GEMV, M = 1 and 8

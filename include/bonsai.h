@@ -80,6 +80,14 @@ bonsai_status bonsai_q1_gemm(const uint32_t *wbits, const uint16_t *scales, cons
 bonsai_status bonsai_q2t_gemv(const uint32_t *wcodes, const uint16_t *scales, const uint16_t *x,
                               float *y, int64_t M, int64_t N, int64_t K, void *hip_stream);
 
+/* Ternary prefill GEMM on 2-bit codes: y[M][N] = x[M][K] * W^T for any M >= 0, tuned for M = 512
+ * (the ternary article's cross-platform throughput table reports pp512 for this format).  The
+ * codes are expanded to binary16 operands 0 and +-2s, so the scales must satisfy |s| < 32752
+ * (2s finite in binary16); larger scales give non-finite results.  Otherwise as the other
+ * entry points. */
+bonsai_status bonsai_q2t_gemm(const uint32_t *wcodes, const uint16_t *scales, const uint16_t *x,
+                              float *y, int64_t M, int64_t N, int64_t K, void *hip_stream);
+
 /* Host-side executable layout spec: pure functions on host memory, no device, no allocation.
  * signs/trits are int8 [N][K] row-major; K must be a multiple of 32 (binary) or 16 (ternary).
  * pack rejects values outside the alphabet with BONSAI_ERR_VALUE (output then unspecified);

@@ -52,6 +52,8 @@ CONFIGS = {
     "C4": Config("C4", "q1_gemm", 512, 13824, 5120, "binary prefill GEMM, pp512"),
     "C5": Config("C5", "q2t_gemv", 1, 5120, 5120, "ternary decode GEMV, M=1"),
     "C5m8": Config("C5m8", "q2t_gemv", 8, 5120, 5120, "ternary decode GEMV, M=8"),
+    # beyond the five workloads: the ternary prefill at the binary prefill's shape (pp512)
+    "C6": Config("C6", "q2t_gemm", 512, 13824, 5120, "ternary prefill GEMM, pp512"),
 }
 
 

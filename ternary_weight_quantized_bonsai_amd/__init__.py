@@ -31,7 +31,7 @@ if not LIB_PATH.exists():
 _lib = ctypes.CDLL(str(LIB_PATH))
 _c_i64 = ctypes.c_int64
 _vp = ctypes.c_void_p
-for _name in ("bonsai_q1_gemv", "bonsai_q1_gemm", "bonsai_q2t_gemv"):
+for _name in ("bonsai_q1_gemv", "bonsai_q1_gemm", "bonsai_q2t_gemv", "bonsai_q2t_gemm"):
     _f = getattr(_lib, _name)
     _f.argtypes = [_vp, _vp, _vp, _vp, _c_i64, _c_i64, _c_i64, _vp]
     _f.restype = ctypes.c_int
@@ -122,6 +122,11 @@ def q1_gemm(wbits, scales, x, out=None):
 def q2t_gemv(wcodes, scales, x, out=None):
     """y[M, N] = x[M, K] W^T for ternary g128 weights on 2-bit codes, 1 <= M <= 8."""
     return _call("bonsai_q2t_gemv", wcodes, scales, x, out, 16)
+
+
+def q2t_gemm(wcodes, scales, x, out=None):
+    """y[M, N] = x[M, K] W^T for ternary g128 weights on 2-bit codes, any M (bonsai_q2t_gemm)."""
+    return _call("bonsai_q2t_gemm", wcodes, scales, x, out, 16)
 
 
 # ---------------------------------------------------------------------------------------

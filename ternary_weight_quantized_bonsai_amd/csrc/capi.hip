@@ -95,6 +95,13 @@ bonsai_status bonsai_q2t_gemv(const uint32_t *wcodes, const uint16_t *scales, co
                [&](int m, int n, int k, hipStream_t st) { return launch_q2t_gemv(wcodes, scales, x, y, m, n, k, st); });
 }
 
+bonsai_status bonsai_q2t_gemm(const uint32_t *wcodes, const uint16_t *scales, const uint16_t *x,
+                              float *y, int64_t M, int64_t N, int64_t K, void *hip_stream)
+{
+    return run(wcodes, scales, x, y, M, N, K, -1, hip_stream,
+               [&](int m, int n, int k, hipStream_t st) { return launch_q2t_gemm(wcodes, scales, x, y, m, n, k, st); });
+}
+
 bonsai_status bonsai_q1_pack(const int8_t *signs, int64_t N, int64_t K, uint32_t *wbits)
 {
     if (N < 0 || K < 0 || K % 32 != 0) return BONSAI_ERR_SHAPE;

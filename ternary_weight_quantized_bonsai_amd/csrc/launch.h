@@ -12,6 +12,8 @@ hipError_t launch_q2t_gemv(const uint32_t *wcodes, const uint16_t *scales, const
                            int M, int N, int K, hipStream_t stream);
 hipError_t launch_q1_gemm(const uint32_t *wbits, const uint16_t *scales, const uint16_t *x, float *y,
                           int M, int N, int K, hipStream_t stream);
+hipError_t launch_q2t_gemm(const uint32_t *wcodes, const uint16_t *scales, const uint16_t *x, float *y,
+                           int M, int N, int K, hipStream_t stream);
 // Small-M GEMV on the matrix cores (ternary M = 1..8, binary M = 2..8).
 hipError_t launch_gemv_mfma(bool ternary, const uint32_t *codes, const uint16_t *scales, const uint16_t *x,
                             float *y, int M, int N, int K, hipStream_t stream);

@@ -42,6 +42,7 @@
 #include <limits.h>
 
 #include <type_traits>
+#include <utility>
 
 #include "device.h"
 #include "launch.h"
@@ -52,8 +53,10 @@ namespace {
 constexpr int BM = 128, BN = 256, BK = 64;
 constexpr int NS = 4;                           // X stages in the LDS ring
 constexpr int XTILE = BM * BK * 2;              // 16 KB per stage
-constexpr int CH = 16;                          // K-steps per LDS chunk of sign words (1024 k)
-constexpr int WCH = BN * CH * BK / 8;           // 32 KB of sign words per chunk
+// K-steps per LDS chunk of codes: 1024 k of sign words or 512 k of ternary codes, 128 B per
+// column either way (8 cells of 16 bytes)
+template <bool TERN> constexpr int chunk_steps() { return TERN ? 8 : 16; }
+constexpr int WCH = BN * 128;                   // 32 KB of codes per chunk
 constexpr int SCH = BN * 32;                    // 8 KB of scales per chunk (room for one dword per scale)
 constexpr int LDS_BYTES = NS * XTILE + 2 * WCH + 2 * SCH;   // 144 KB
 
@@ -85,9 +88,47 @@ __device__ __forceinline__ half8_t expand8(uint32_t w, int s, int q, uint32_t cs
     return __builtin_bit_cast(half8_t, e);
 }
 
-// SMODE 16: one 16-byte scale copy per column and chunk (needs K % 1024 == 0); SMODE 2: one
-// 2-byte copy per column and group, landing in the low half of a dword.
-template <int SMODE>
+// Ternary: 8 halves of the k16 slice held by word w (16 codes, code j of k = j), k 8q .. 8q + 7,
+// times the scale.  Merging the word's half q with the same half shifted by one code puts codes
+// k and k + 1 16 bits apart, so one shift and one mask read a pair as binary16 (0 or +-2: code
+// 01 sets the top exponent bit, 11 also the sign); cs2 = (s, s) scales the pair exactly (2s is
+// finite for |s| < 32752), and the factor 2 comes off the fp32 sums.
+__device__ __forceinline__ half8_t expand8_tern(uint32_t w, int q, uint32_t cs2)
+{
+    const uint32_t lo = w >> (16 * q), hi = w >> (16 * q + 2);
+    const uint32_t v = (lo & 0xFFFFu) | (hi << 16);
+    u32x4 e;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const half2_t t = as_half2((v << (14 - 4 * i)) & 0xC000C000u);
+        e[i] = __builtin_bit_cast(uint32_t, t * as_half2(cs2));
+    }
+    return __builtin_bit_cast(half8_t, e);
+}
+
+// Scale copies of one chunk per column: binary SMODE 16, one 16-byte copy of the chunk's 8
+// scales (K % 1024 == 0), or SMODE 2, one 2-byte copy per group (low half of a dword); ternary
+// SMODE 4, one 4-byte copy per pair of the chunk's 4 groups (G even), or SMODE 2 per group.
+template <bool TERN, int SMODE> constexpr int scale_copies() { return TERN ? (SMODE == 4 ? 2 : 4) : (SMODE == 16 ? 1 : 8); }
+
+// Copies of the next chunk issued at mid-step j: binary, sign-word copy j (j < 8) and then the
+// scales at position 8 (SMODE 16) or 8 .. 15; ternary (8 steps per chunk), code copies 2j and
+// 2j + 1 (j < 4) and then scale copy j - 4.  A copy issued at mid-step j has landed by the wait
+// of mid-step j + 3, so every copy lands before the first read of what it brings: the next
+// chunk's cell 0 and first scales are read at the end of the chunk's last step.
+template <bool TERN, int SMODE> constexpr int copies_at(int j)
+{
+    return TERN ? (j < 4 ? 2 : (j - 4 < scale_copies<TERN, SMODE>() ? 1 : 0))
+                : (j < 8 ? 1 : 0) + (SMODE == 16 ? (j == 8 ? 1 : 0) : (j >= 8 ? 1 : 0));
+}
+
+template <int... J, class F>
+__device__ __forceinline__ void for_each_step(std::integer_sequence<int, J...>, F &&f)
+{
+    (f(std::integral_constant<int, J>{}), ...);
+}
+
+template <bool TERN, int SMODE>
 __global__ __launch_bounds__(256) void q1_gemm_kernel(const uint32_t *__restrict__ wbits,
                                                       const uint16_t *__restrict__ scales,
                                                       const uint16_t *__restrict__ x,
@@ -103,7 +144,9 @@ __global__ __launch_bounds__(256) void q1_gemm_kernel(const uint32_t *__restrict
     const int q = lane >> 5, l32 = lane & 31;
     const int tiles_n = (N + BN - 1) / BN;
     const int m0 = (blockIdx.x / tiles_n) * BM, n0 = (blockIdx.x % tiles_n) * BN;
-    const int G = K >> 7;                       // groups per row = 16-byte units of sign words per row
+    constexpr int CH = chunk_steps<TERN>();
+    const int G = K >> 7;                       // groups per row
+    const int U = TERN ? 2 * G : G;             // 16-byte units of codes per row
     const int KT = K / BK;
     const int nchunks = (KT + CH - 1) / CH;
 
@@ -126,7 +169,7 @@ __global__ __launch_bounds__(256) void q1_gemm_kernel(const uint32_t *__restrict
     for (int i = 0; i < 8; ++i) {
         const int c = 64 * wave + 8 * i + (lane >> 3);
         wu[i] = (lane & 7) ^ ((c >> 1) & 7);
-        wsrc[i] = reinterpret_cast<const u32x4 *>(wbits) + (size_t)min(n0 + c, N - 1) * G;
+        wsrc[i] = reinterpret_cast<const u32x4 *>(wbits) + (size_t)min(n0 + c, N - 1) * U;
     }
     const uint16_t *ssrc = scales + (size_t)min(n0 + 64 * wave + lane, N - 1) * G;
 
@@ -137,15 +180,19 @@ __global__ __launch_bounds__(256) void q1_gemm_kernel(const uint32_t *__restrict
                                              (lds_void_t *)(xs + slot * XTILE + (4 * wave + j) * 1024), 16, 0, 0);
     };
     auto issue_w = [&](int cc, int par, int i) {
-        __builtin_amdgcn_global_load_lds((glb_void_t *)(wsrc[i] + min(cc * 8 + wu[i], G - 1)),
+        __builtin_amdgcn_global_load_lds((glb_void_t *)(wsrc[i] + min(cc * 8 + wu[i], U - 1)),
                                          (lds_void_t *)(wls + par * WCH + (64 * wave + 8 * i) * 128), 16, 0, 0);
     };
+    constexpr int GPC = TERN ? 4 : 8;           // groups per chunk
     auto issue_s = [&](int cc, int par, int g) {
-        if (SMODE == 16)     // the chunk's 8 scales of column 64 wave + lane
+        if constexpr (!TERN && SMODE == 16)      // the chunk's 8 scales of column 64 wave + lane
             __builtin_amdgcn_global_load_lds((glb_void_t *)(ssrc + min(cc * 8, G - 8)),
                                              (lds_void_t *)(sls + par * SCH + (64 * wave) * 16), 16, 0, 0);
-        else                 // group g of the chunk, one dword per column
-            __builtin_amdgcn_global_load_lds((glb_void_t *)(ssrc + min(cc * 8 + g, G - 1)),
+        else if constexpr (TERN && SMODE == 4)   // groups 2g, 2g + 1 of the chunk, one dword per column
+            __builtin_amdgcn_global_load_lds((glb_void_t *)(ssrc + min(cc * GPC + 2 * g, G - 2)),
+                                             (lds_void_t *)(sls + par * SCH + (g * 256 + 64 * wave) * 4), 4, 0, 0);
+        else                                      // group g of the chunk, low half of a dword per column
+            __builtin_amdgcn_global_load_lds((glb_void_t *)(ssrc + min(cc * GPC + g, G - 1)),
                                              (lds_void_t *)(sls + par * SCH + (g * 256 + 64 * wave) * 4), 2, 0, 0);
     };
 
@@ -158,8 +205,10 @@ __global__ __launch_bounds__(256) void q1_gemm_kernel(const uint32_t *__restrict
             for (int i = 0; i < 16; ++i) acc[a][b][i] = 0.f;
 
     half8_t af[2][4], bf[2][2];                  // operands of the current / next k16 slice
-    uint32_t wcur[2][2], cs[2];                  // sign words and (-s, -s) of the step being expanded
-    uint32_t wnxt[2][2];                         // words of the following step (second half of a cell)
+    // code words of the step being expanded (binary: 2 words, the cell's other 2 saved for the
+    // next step; ternary: the cell's 4 words) and the scale pair, (-s, -s) binary or (s, s) ternary
+    uint32_t wcur[2][4], cs[2];
+    uint32_t wnxt[2][2];
     const uint32_t wls_base = (uint32_t)(uintptr_t)((__attribute__((address_space(3))) char *)wls);
     const uint32_t sls_base = (uint32_t)(uintptr_t)((__attribute__((address_space(3))) char *)sls);
 
@@ -172,16 +221,20 @@ __global__ __launch_bounds__(256) void q1_gemm_kernel(const uint32_t *__restrict
             af[buf][mt] = *reinterpret_cast<const half8_t *>(xb + 128 * r + 16 * (c ^ ((r >> 1) & 7)));
         }
     };
-    // cell u of the chunk in buffer par: both columns' words for steps 2u, 2u + 1 and group u's
-    // scales, waited for inside the block; the outputs are early-clobber so that no output
-    // register doubles as an address the block has yet to use
+    // cell u of the chunk in buffer par: both columns' words (binary: steps 2u, 2u + 1, group
+    // u; ternary: step u, group u / 2) and the group's scales, waited for inside the block; the
+    // outputs are early-clobber so that no output register doubles as an address the block has
+    // yet to use
     auto read_cell = [&](int par, int u) {
         uint32_t aw[2], as[2];
+        const int g = TERN ? u >> 1 : u;
 #pragma unroll
         for (int t = 0; t < 2; ++t) {
             const int c = 64 * wave + 32 * t + l32;
             aw[t] = wls_base + par * WCH + c * 128 + 16 * (u ^ ((c >> 1) & 7));
-            as[t] = sls_base + par * SCH + (SMODE == 16 ? c * 16 + 2 * u : (u * 256 + c) * 4);
+            if constexpr (!TERN && SMODE == 16) as[t] = sls_base + par * SCH + c * 16 + 2 * g;
+            else if constexpr (TERN && SMODE == 4) as[t] = sls_base + par * SCH + ((g >> 1) * 256 + c) * 4 + 2 * (g & 1);
+            else as[t] = sls_base + par * SCH + (g * 256 + c) * 4;
         }
         u32x4 w0, w1;
         uint32_t s0, s1;
@@ -190,14 +243,24 @@ __global__ __launch_bounds__(256) void q1_gemm_kernel(const uint32_t *__restrict
                      : "=&v"(w0), "=&v"(w1), "=&v"(s0), "=&v"(s1)   // early clobber: a load landing
                      : "v"(aw[0]), "v"(aw[1]), "v"(as[0]), "v"(as[1])  // must not overwrite a later
                      : "memory");                                      // load's address
-        wcur[0][0] = w0[0]; wcur[0][1] = w0[1]; wnxt[0][0] = w0[2]; wnxt[0][1] = w0[3];
-        wcur[1][0] = w1[0]; wcur[1][1] = w1[1]; wnxt[1][0] = w1[2]; wnxt[1][1] = w1[3];
-        cs[0] = (s0 | (s0 << 16)) ^ 0x80008000u;     // (-s, -s)
-        cs[1] = (s1 | (s1 << 16)) ^ 0x80008000u;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            wcur[0][e] = w0[e];
+            wcur[1][e] = w1[e];
+        }
+        if constexpr (!TERN) {
+            wnxt[0][0] = w0[2]; wnxt[0][1] = w0[3];
+            wnxt[1][0] = w1[2]; wnxt[1][1] = w1[3];
+        }
+        const uint32_t flip = TERN ? 0u : 0x80008000u;     // binary (-s, -s), ternary (s, s)
+        cs[0] = (s0 | (s0 << 16)) ^ flip;
+        cs[1] = (s1 | (s1 << 16)) ^ flip;
     };
-    // words of step j of the chunk in buffer par: a cell read at even j, else its saved half
+    // words of step j of the chunk in buffer par: ternary, cell j; binary, a cell read at even
+    // j, else its saved half
     auto read_w = [&](int par, int j) {
-        if ((j & 1) == 0) read_cell(par, j >> 1);
+        if (TERN) read_cell(par, j);
+        else if ((j & 1) == 0) read_cell(par, j >> 1);
         else {
 #pragma unroll
             for (int t = 0; t < 2; ++t) {
@@ -208,7 +271,8 @@ __global__ __launch_bounds__(256) void q1_gemm_kernel(const uint32_t *__restrict
     };
     auto make_b = [&](int s, int buf) {
 #pragma unroll
-        for (int t = 0; t < 2; ++t) bf[buf][t] = expand8(wcur[t][s >> 1], s, q, cs[t]);
+        for (int t = 0; t < 2; ++t)
+            bf[buf][t] = TERN ? expand8_tern(wcur[t][s], q, cs[t]) : expand8(wcur[t][s >> 1], s, q, cs[t]);
     };
     auto mfma8 = [&](int buf) {
 #pragma unroll
@@ -221,12 +285,8 @@ __global__ __launch_bounds__(256) void q1_gemm_kernel(const uint32_t *__restrict
     // prologue: chunk 0 and X stages 0 .. NS - 2
 #pragma unroll
     for (int i = 0; i < 8; ++i) issue_w(0, 0, i);
-    if (SMODE == 16) {
-        issue_s(0, 0, 0);
-    } else {
 #pragma unroll
-        for (int g = 0; g < 8; ++g) issue_s(0, 0, g);
-    }
+    for (int g = 0; g < scale_copies<TERN, SMODE>(); ++g) issue_s(0, 0, g);
 #pragma unroll
     for (int st = 0; st < NS - 1; ++st) issue_x(min(st, KT - 1), st);
     wait_vmcnt<4 * (NS - 2)>();                 // chunk 0 and stage 0 landed
@@ -235,8 +295,8 @@ __global__ __launch_bounds__(256) void q1_gemm_kernel(const uint32_t *__restrict
     read_a(0, 0, 0);
     make_b(0, 0);
 
-    // Mid-step m issues stage m + 3 and then that position's chunk copies for the next chunk:
-    // sign-word instruction m (m < 8), then the scales (position 8, or one group at 8 .. 15).
+    // Mid-step m issues stage m + 3 and then that position's chunk copies for the next chunk
+    // (copies_at).
     // Every chunk does so (the last one re-copies itself into the idle buffer), so the number
     // of copies issued after any stage is known at compile time.
     for (int cc = 0; cc < nchunks; ++cc) {
@@ -266,19 +326,28 @@ __global__ __launch_bounds__(256) void q1_gemm_kernel(const uint32_t *__restrict
             // Stage kt + 1 has landed once only the copies issued after it are outstanding:
             // mid-step kt - 2's chunk copies, then stage kt + 2 and mid-step kt - 1's.
             constexpr int jm2 = (j + CH - 2) % CH, jm1 = (j + CH - 1) % CH;
-            constexpr int pm2 = jm2 < 8 ? 1 : (SMODE == 16 ? (jm2 == 8 ? 1 : 0) : 1);
-            constexpr int pm1 = jm1 < 8 ? 1 : (SMODE == 16 ? (jm1 == 8 ? 1 : 0) : 1);
+            constexpr int pm2 = copies_at<TERN, SMODE>(jm2);
+            constexpr int pm1 = copies_at<TERN, SMODE>(jm1);
             if (j < 2 && cc == 0) {
                 if (j == 0) wait_vmcnt<4>();
-                else wait_vmcnt<4 + 1>();      // mid-step 0 issued stage 3, then sign-word copy 0
+                else wait_vmcnt<4 + copies_at<TERN, SMODE>(0)>();   // mid-step 0: stage 3, then its copies
             } else {
                 wait_vmcnt<pm2 + 4 + pm1>();
             }
             asm volatile("s_barrier" ::: "memory");
             issue_x(min(kt + NS - 1, KT - 1), (slot + NS - 1) % NS);
-            if (j < 8) issue_w(cn, par ^ 1, j);
-            else if (SMODE == 16) { if (j == 8) issue_s(cn, par ^ 1, 0); }
-            else issue_s(cn, par ^ 1, j - 8);
+            if constexpr (TERN) {
+                if constexpr (j < 4) {
+                    issue_w(cn, par ^ 1, 2 * j);
+                    issue_w(cn, par ^ 1, 2 * j + 1);
+                } else if constexpr (j - 4 < scale_copies<TERN, SMODE>()) {
+                    issue_s(cn, par ^ 1, j - 4);
+                }
+            } else {
+                if constexpr (j < 8) issue_w(cn, par ^ 1, j);
+                else if constexpr (SMODE == 16) { if constexpr (j == 8) issue_s(cn, par ^ 1, 0); }
+                else issue_s(cn, par ^ 1, j - 8);
+            }
             // slice 3, with the first operands of step kt + 1 fetched under it
             if (live) {
                 read_w(j == CH - 1 ? par ^ 1 : par, (j + 1) % CH);
@@ -294,22 +363,7 @@ __global__ __launch_bounds__(256) void q1_gemm_kernel(const uint32_t *__restrict
                 __builtin_amdgcn_sched_barrier(0);
             }
         };
-        step(std::integral_constant<int, 0>{});
-        step(std::integral_constant<int, 1>{});
-        step(std::integral_constant<int, 2>{});
-        step(std::integral_constant<int, 3>{});
-        step(std::integral_constant<int, 4>{});
-        step(std::integral_constant<int, 5>{});
-        step(std::integral_constant<int, 6>{});
-        step(std::integral_constant<int, 7>{});
-        step(std::integral_constant<int, 8>{});
-        step(std::integral_constant<int, 9>{});
-        step(std::integral_constant<int, 10>{});
-        step(std::integral_constant<int, 11>{});
-        step(std::integral_constant<int, 12>{});
-        step(std::integral_constant<int, 13>{});
-        step(std::integral_constant<int, 14>{});
-        step(std::integral_constant<int, 15>{});
+        for_each_step(std::make_integer_sequence<int, CH>{}, step);
     }
     wait_vmcnt<0>();                            // no copy into LDS outlives the workgroup
 
@@ -323,7 +377,7 @@ __global__ __launch_bounds__(256) void q1_gemm_kernel(const uint32_t *__restrict
 #pragma unroll
             for (int i = 0; i < 16; ++i) {
                 const int rowm = m0 + 32 * mt + 8 * (i >> 2) + 4 * q + (i & 3);
-                if (rowm < M) y[(size_t)rowm * N + col] = acc[mt][t][i];
+                if (rowm < M) y[(size_t)rowm * N + col] = TERN ? 0.5f * acc[mt][t][i] : acc[mt][t][i];
             }
         }
 }
@@ -336,8 +390,21 @@ hipError_t launch_q1_gemm(const uint32_t *wbits, const uint16_t *scales, const u
     const int64_t tiles = (int64_t)((N + BN - 1) / BN) * ((M + BM - 1) / BM);
     if (tiles > INT_MAX || K % 128 != 0 || K <= 0) return hipErrorInvalidValue;
     void *args[] = {&wbits, &scales, &x, &y, &M, &N, &K};
-    const void *fn = (K % 1024 == 0) ? reinterpret_cast<const void *>(&q1_gemm_kernel<16>)
-                                     : reinterpret_cast<const void *>(&q1_gemm_kernel<2>);
+    const void *fn = (K % 1024 == 0) ? reinterpret_cast<const void *>(&q1_gemm_kernel<false, 16>)
+                                     : reinterpret_cast<const void *>(&q1_gemm_kernel<false, 2>);
+    return launch_kernel(fn, dim3((unsigned)tiles), dim3(256), args, 0, stream);
+}
+
+// Ternary prefill ("Ternary Bonsai 27B" article, cross-platform throughput: pp512) on the
+// same tiles, 2-bit codes expanded to 0 / +-2s operands.
+hipError_t launch_q2t_gemm(const uint32_t *wcodes, const uint16_t *scales, const uint16_t *x, float *y,
+                           int M, int N, int K, hipStream_t stream)
+{
+    const int64_t tiles = (int64_t)((N + BN - 1) / BN) * ((M + BM - 1) / BM);
+    if (tiles > INT_MAX || K % 128 != 0 || K <= 0) return hipErrorInvalidValue;
+    void *args[] = {&wcodes, &scales, &x, &y, &M, &N, &K};
+    const void *fn = ((K / 128) % 2 == 0) ? reinterpret_cast<const void *>(&q1_gemm_kernel<true, 4>)
+                                          : reinterpret_cast<const void *>(&q1_gemm_kernel<true, 2>);
     return launch_kernel(fn, dim3((unsigned)tiles), dim3(256), args, 0, stream);
 }
 

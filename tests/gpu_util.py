@@ -31,7 +31,8 @@ def call(kind: str, w: np.ndarray, s: np.ndarray, x: np.ndarray, out=None):
     """Run one entry point on device copies of (w, s, x); returns the float32 result on the host."""
     import ternary_weight_quantized_bonsai_amd as bonsai
     torch, _ = torch_dev()
-    fn = {"q1_gemv": bonsai.q1_gemv, "q1_gemm": bonsai.q1_gemm, "q2t_gemv": bonsai.q2t_gemv}[kind]
+    fn = {"q1_gemv": bonsai.q1_gemv, "q1_gemm": bonsai.q1_gemm, "q2t_gemv": bonsai.q2t_gemv,
+          "q2t_gemm": bonsai.q2t_gemm}[kind]
     note(f"{kind} M={x.shape[0]} N={w.shape[0]} K={x.shape[1]}")
     y = fn(to_dev(w), to_dev(s), to_dev(x), out=out)
     torch.cuda.synchronize()

@@ -18,7 +18,7 @@ def declared_functions():
 
 def test_header_declares_the_boundary():
     names = declared_functions()
-    for want in ("bonsai_q1_gemv", "bonsai_q1_gemm", "bonsai_q2t_gemv", "bonsai_q1_pack",
+    for want in ("bonsai_q1_gemv", "bonsai_q1_gemm", "bonsai_q2t_gemv", "bonsai_q2t_gemm", "bonsai_q1_pack",
                  "bonsai_q1_unpack", "bonsai_q2t_pack", "bonsai_q2t_unpack", "bonsai_status_str",
                  "bonsai_last_device_error", "bonsai_time_next_launch"):
         assert want in names
@@ -110,7 +110,7 @@ def test_pack_rejects_values_and_shapes():
 
 
 # ---- GPU entry points: host-side validation only (nothing is launched) ------------------
-GPU_FNS = ["bonsai_q1_gemv", "bonsai_q1_gemm", "bonsai_q2t_gemv"]
+GPU_FNS = ["bonsai_q1_gemv", "bonsai_q1_gemm", "bonsai_q2t_gemv", "bonsai_q2t_gemm"]
 FAKE = 0x7F0000000000          # aligned, never dereferenced: every case below fails validation
 
 
@@ -141,7 +141,8 @@ def test_gemv_rejects_m_above_8(fn):
     assert f(FAKE, FAKE, FAKE, FAKE, 9, 64, 128, None) == bonsai.ERR_SHAPE
 
 
-def test_gemm_accepts_large_m_in_validation_only():
+@pytest.mark.parametrize("fn", ["bonsai_q1_gemm", "bonsai_q2t_gemm"])
+def test_gemm_accepts_large_m_in_validation_only(fn):
     # M = 2^30 + 1 is rejected; nothing is launched for it
-    f = bonsai.raw().bonsai_q1_gemm
+    f = getattr(bonsai.raw(), fn)
     assert f(FAKE, FAKE, FAKE, FAKE, (1 << 30) + 1, 64, 128, None) == bonsai.ERR_SHAPE

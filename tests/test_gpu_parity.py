@@ -14,7 +14,7 @@ from gpu_util import assert_close, call, exact, note, ref, to_dev, torch_dev
 
 pytestmark = pytest.mark.gpu
 
-KINDS = ["q1_gemv", "q1_gemm", "q2t_gemv"]
+KINDS = ["q1_gemv", "q1_gemm", "q2t_gemv", "q2t_gemm"]
 
 
 def make(kind, M, N, K, seed=0, tag=None):
@@ -67,15 +67,16 @@ def test_config_c3_popcount_all_rows():
     assert np.array_equal(y[0], (2 * pop - c.K).astype(np.float32))
 
 
-def test_config_c4_prefill_sampled(orc):
-    c = synth.CONFIGS["C4"]
+@pytest.mark.parametrize("name", ["C4", "C6"])
+def test_config_prefill_sampled(name, orc):
+    c = synth.CONFIGS[name]
     w, s, x = make(c.kind, c.M, c.N, c.K)
     y = call(c.kind, w, s, x)
     rng = np.random.default_rng(1)
     ms = np.unique(np.concatenate([np.arange(8), np.arange(120, 136), np.arange(c.M - 8, c.M)]))
     ns = np.unique(np.concatenate([np.arange(64), np.arange(c.N - 64, c.N), rng.choice(c.N, 128, replace=False)]))
     yref, a = ref(c.kind, orc, w, s, x, m_idx=ms, n_idx=ns)
-    assert_close(y[np.ix_(ms, ns)], yref, a, "C4 sampled")
+    assert_close(y[np.ix_(ms, ns)], yref, a, f"{name} sampled")
 
 
 # ---- integer-valued inputs at full shapes: bit-exact -------------------------------------
@@ -96,7 +97,7 @@ def test_integer_inputs_bit_exact_full(name, orc):
     assert np.array_equal(y, ye)
 
 
-@pytest.mark.parametrize("name", ["C3", "C4"])
+@pytest.mark.parametrize("name", ["C3", "C4", "C6"])
 def test_integer_inputs_bit_exact_sampled(name, orc):
     c = synth.CONFIGS[name]
     w, s, x = integer_inputs(c.kind, c.M, c.N, c.K, 8)
@@ -131,12 +132,14 @@ def test_q2t_gemv_onehot_every_field(orc):
         assert np.array_equal(y, W[:, k0:k0 + 8].T), k0
 
 
-def test_q1_gemm_identity_gives_dequantized_weights(orc):
+@pytest.mark.parametrize("kind", ["q1_gemm", "q2t_gemm"])
+def test_gemm_identity_gives_dequantized_weights(kind, orc):
     N, K = 300, 512
-    w, s, _ = make("q1_gemm", 1, N, K, 5, "identity")
+    w, s, _ = make(kind, 1, N, K, 5, f"identity/{kind}")
     x = np.where(np.eye(K, dtype=bool), 0x3C00, 0).astype(np.uint16)
-    y = call("q1_gemm", w, s, x)
-    assert np.array_equal(y, orc.q1_dequant(w, s, K).astype(np.float32).T)
+    y = call(kind, w, s, x)
+    deq = orc.q1_dequant if kind.startswith("q1") else orc.q2t_dequant
+    assert np.array_equal(y, deq(w, s, K).astype(np.float32).T)
 
 
 # ---- ragged and edge shapes ---------------------------------------------------------------
@@ -152,6 +155,9 @@ EDGE = {
                  (1, 130, 131072), (4, 4097, 640)],
     "q1_gemm": [(1, 1, 128), (17, 100, 256), (130, 257, 384), (128, 128, 512), (256, 384, 1024),
                 (5, 3000, 640), (300, 70, 2048), (16, 40, 131072), (64, 300, 1152), (200, 520, 3200)],
+    # ternary prefill: 512-k chunks, odd G (2-byte scale copies), K not a multiple of 512
+    "q2t_gemm": [(1, 1, 128), (17, 100, 256), (130, 257, 384), (128, 128, 512), (256, 384, 1024),
+                 (5, 3000, 640), (300, 70, 2048), (16, 40, 131072), (64, 300, 1152), (200, 520, 3200)],
 }
 
 
@@ -185,7 +191,7 @@ def raw_call(kind, w_t, s_t, x_t, y_ptr, M, N, K):
 
 
 @pytest.mark.parametrize("kind,M,N,K", [("q1_gemv", 3, 1001, 640), ("q2t_gemv", 8, 333, 384),
-                                        ("q1_gemm", 131, 259, 512)])
+                                        ("q1_gemm", 131, 259, 512), ("q2t_gemm", 131, 259, 640)])
 def test_poison_and_guard_band(kind, M, N, K, orc):
     torch, dev = torch_dev()
     w, s, x = make(kind, M, N, K, 21, f"poison/{kind}")
@@ -216,7 +222,7 @@ def test_empty_products_and_k0(kind):
 
 
 # ---- determinism, symmetry, cross-kernel consistency --------------------------------------
-@pytest.mark.parametrize("name", ["C2a", "C4", "C5m8"])
+@pytest.mark.parametrize("name", ["C2a", "C4", "C5m8", "C6"])
 def test_bitwise_deterministic(name):
     c = synth.CONFIGS[name]
     w, s, x = make(c.kind, c.M, c.N, c.K)
@@ -224,14 +230,14 @@ def test_bitwise_deterministic(name):
 
 
 @pytest.mark.parametrize("kind,M,N,K", [("q1_gemv", 2, 2000, 5120), ("q1_gemm", 96, 700, 1024),
-                                        ("q2t_gemv", 8, 1500, 2048)])
+                                        ("q2t_gemv", 8, 1500, 2048), ("q2t_gemm", 96, 700, 1024)])
 def test_metamorphic(kind, M, N, K, orc):
     w, s, x = make(kind, M, N, K, 31, f"meta/{kind}")
     y = call(kind, w, s, x)
     yneg = call(kind, w, s, x ^ np.uint16(0x8000))                                # y(-x) = -y(x)
-    if kind == "q1_gemm":
+    if kind.endswith("gemm"):
         # The MFMA's fp32 accumulation is not sign-symmetric bit for bit (observed on gfx950),
-        # so for the matrix-core kernel the identity holds within the acceptance bound.
+        # so for the matrix-core GEMMs the identity holds within the acceptance bound.
         yref, a = ref(kind, orc, w, s, x)
         assert_close(-yneg, yref, a, "negated x")
     else:
