@@ -21,6 +21,10 @@
 // FMA per output straight from the binary16 scale, so the operands stay exact small integers
 // and every product is exact; the ternary factor 2 comes off the sums once at the end.
 //
+// Rows of x beyond 16 take more column blocks: blockIdx.y selects rows 16 y .. 16 y + 15 of x
+// and of the output, so a skinny product (a few dozen rows of x, as in checking several draft
+// tokens at once) runs as that many 16-column passes over the same weight tiles.
+//
 // Work split.  A workgroup owns R = 16 RT weight rows; its waves take 4-group slices of K.
 // Each slice's codes (R rows x 4 groups), scales and x (M rows x 512 k) are copied straight
 // into the wave's LDS (direct global->LDS loads, whole lines), the wave's partial sums of the
@@ -75,6 +79,10 @@ __global__ __launch_bounds__(sm_max_waves(RT) * 64) void gemv_mfma_kernel(const 
     constexpr int R = 16 * RT;
     constexpr int TILE = R * L::row_bytes;
     extern __shared__ u32x4 lds[];
+    // this workgroup's block of 16 rows of x and y
+    x += (size_t)16 * blockIdx.y * K;
+    y += (size_t)16 * blockIdx.y * N;
+    M = min(16, M - 16 * (int)blockIdx.y);
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int nw = blockDim.x >> 6;
@@ -265,11 +273,13 @@ template <bool TERN, int RT>
 hipError_t launch_rt(const uint32_t *codes, const uint16_t *scales, const uint16_t *x, float *y,
                      int M, int N, int K, hipStream_t stream)
 {
-    const int nw = sm_waves<TERN>(RT, M, K);
+    const int mb = M < 16 ? M : 16;                 // rows of x per workgroup
+    const int nw = sm_waves<TERN>(RT, mb, K);
     if (nw < 1) return hipErrorInvalidValue;
-    const size_t lds = (size_t)nw * sm_wave_bytes<TERN>(RT, M) + (size_t)nw * M * 16 * RT * 4;
+    const size_t lds = (size_t)nw * sm_wave_bytes<TERN>(RT, mb) + (size_t)nw * mb * 16 * RT * 4;
     const int64_t blocks = ((int64_t)N + 16 * RT - 1) / (16 * RT);
-    if (blocks > INT_MAX) return hipErrorInvalidValue;
+    const int64_t yblocks = ((int64_t)M + 15) / 16;
+    if (blocks > INT_MAX || yblocks > 65535) return hipErrorInvalidValue;
     const void *fn = (K / 128) % 2 == 0 ? reinterpret_cast<const void *>(&gemv_mfma_kernel<TERN, RT, true>)
                                         : reinterpret_cast<const void *>(&gemv_mfma_kernel<TERN, RT, false>);
     static const bool attr =
@@ -279,7 +289,7 @@ hipError_t launch_rt(const uint32_t *codes, const uint16_t *scales, const uint16
                             hipFuncAttributeMaxDynamicSharedMemorySize, kLdsPerCu) == hipSuccess;
     if (!attr) return hipErrorInvalidValue;
     void *args[] = {&codes, &scales, &x, &y, &M, &N, &K};
-    return launch_kernel(fn, dim3((unsigned)blocks), dim3(64 * nw), args, lds, stream);
+    return launch_kernel(fn, dim3((unsigned)blocks, (unsigned)yblocks), dim3(64 * nw), args, lds, stream);
 }
 
 template <bool TERN>
@@ -291,14 +301,15 @@ hipError_t launch_sm(const uint32_t *codes, const uint16_t *scales, const uint16
     // needs the fewest rounds of the chip's 256 CUs, given what the LDS and the 32 wave slots
     // of a CU hold, and among those the smallest tile (the most workgroups).
     constexpr int kCus = 256, kWavesPerCu = 32;
+    const int mb = M < 16 ? M : 16;
     auto rounds = [&](int rt) -> int64_t {
-        const int nw = sm_waves<TERN>(rt, M, K);
+        const int nw = sm_waves<TERN>(rt, mb, K);
         if (nw < 1) return INT64_MAX;
-        const int64_t lds = (int64_t)nw * sm_wave_bytes<TERN>(rt, M) + (int64_t)nw * M * 16 * rt * 4;
+        const int64_t lds = (int64_t)nw * sm_wave_bytes<TERN>(rt, mb) + (int64_t)nw * mb * 16 * rt * 4;
         int64_t per_cu = kLdsPerCu / lds;
         if (per_cu > kWavesPerCu / nw) per_cu = kWavesPerCu / nw;
         if (per_cu < 1) return INT64_MAX;
-        const int64_t blocks = ((int64_t)N + 16 * rt - 1) / (16 * rt);
+        const int64_t blocks = (((int64_t)N + 16 * rt - 1) / (16 * rt)) * (((int64_t)M + 15) / 16);
         return (blocks + per_cu * kCus - 1) / (per_cu * kCus);
     };
     const int64_t r1 = rounds(1), r2 = rounds(2), r4 = rounds(4);
@@ -309,9 +320,11 @@ hipError_t launch_sm(const uint32_t *codes, const uint16_t *scales, const uint16
 
 }  // namespace
 
+// Any M >= 1 (16 rows of x per column block).
 hipError_t launch_gemv_mfma(bool ternary, const uint32_t *codes, const uint16_t *scales, const uint16_t *x,
                             float *y, int M, int N, int K, hipStream_t stream)
 {
+    if (M < 1) return hipErrorInvalidValue;
     return ternary ? launch_sm<true>(codes, scales, x, y, M, N, K, stream)
                    : launch_sm<false>(codes, scales, x, y, M, N, K, stream);
 }

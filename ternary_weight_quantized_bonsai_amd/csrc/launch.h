@@ -14,7 +14,8 @@ hipError_t launch_q1_gemm(const uint32_t *wbits, const uint16_t *scales, const u
                           int M, int N, int K, hipStream_t stream);
 hipError_t launch_q2t_gemm(const uint32_t *wcodes, const uint16_t *scales, const uint16_t *x, float *y,
                            int M, int N, int K, hipStream_t stream);
-// Small-M GEMV on the matrix cores (ternary M = 1..8, binary M = 2..8).
+// Small-M products on the matrix cores: 16 rows of x per column block, any M >= 1 (the GEMV
+// entry points use it for ternary M = 1..8 and binary M = 2..8, the GEMMs for small M).
 hipError_t launch_gemv_mfma(bool ternary, const uint32_t *codes, const uint16_t *scales, const uint16_t *x,
                             float *y, int M, int N, int K, hipStream_t stream);
 hipError_t launch_fill_zero(float *y, int64_t count, hipStream_t stream);

@@ -384,9 +384,17 @@ __global__ __launch_bounds__(256) void q1_gemm_kernel(const uint32_t *__restrict
 
 }  // namespace
 
+// Up to this many rows of x the small-M kernel (16 rows of x per pass over the weights) beats
+// the 128 x 256 tiles, which leave most CUs idle there (N = 13824 makes 54 tiles per 128 rows
+// of x).  Measured at N = 13824, K = 5120: 10 us against 51 us at M = 16, 35 against 51 at
+// M = 64; the two meet near M = 96 (binary) and 72 (ternary).
+constexpr int kSmallM = 80;
+
 hipError_t launch_q1_gemm(const uint32_t *wbits, const uint16_t *scales, const uint16_t *x, float *y,
                           int M, int N, int K, hipStream_t stream)
 {
+    if (M == 1) return launch_q1_gemv(wbits, scales, x, y, M, N, K, stream);
+    if (M <= kSmallM) return launch_gemv_mfma(false, wbits, scales, x, y, M, N, K, stream);
     const int64_t tiles = (int64_t)((N + BN - 1) / BN) * ((M + BM - 1) / BM);
     if (tiles > INT_MAX || K % 128 != 0 || K <= 0) return hipErrorInvalidValue;
     void *args[] = {&wbits, &scales, &x, &y, &M, &N, &K};
@@ -400,6 +408,7 @@ hipError_t launch_q1_gemm(const uint32_t *wbits, const uint16_t *scales, const u
 hipError_t launch_q2t_gemm(const uint32_t *wcodes, const uint16_t *scales, const uint16_t *x, float *y,
                            int M, int N, int K, hipStream_t stream)
 {
+    if (M <= kSmallM) return launch_gemv_mfma(true, wcodes, scales, x, y, M, N, K, stream);
     const int64_t tiles = (int64_t)((N + BN - 1) / BN) * ((M + BM - 1) / BM);
     if (tiles > INT_MAX || K % 128 != 0 || K <= 0) return hipErrorInvalidValue;
     void *args[] = {&wcodes, &scales, &x, &y, &M, &N, &K};

@@ -132,14 +132,16 @@ def test_q2t_gemv_onehot_every_field(orc):
         assert np.array_equal(y, W[:, k0:k0 + 8].T), k0
 
 
-@pytest.mark.parametrize("kind", ["q1_gemm", "q2t_gemm"])
-def test_gemm_identity_gives_dequantized_weights(kind, orc):
+@pytest.mark.parametrize("kind,M", [("q1_gemm", 512), ("q2t_gemm", 512), ("q1_gemm", 70), ("q2t_gemm", 70)])
+def test_gemm_identity_gives_dequantized_weights(kind, M, orc):
+    """x = the first M rows of the identity: y = the first M columns of the dequantized W^T (the
+    128 x 256 tiles at M = 512; the small-M kernel, five 16-row blocks, at M = 70)."""
     N, K = 300, 512
     w, s, _ = make(kind, 1, N, K, 5, f"identity/{kind}")
-    x = np.where(np.eye(K, dtype=bool), 0x3C00, 0).astype(np.uint16)
+    x = np.where(np.eye(K, dtype=bool), 0x3C00, 0).astype(np.uint16)[:M]
     y = call(kind, w, s, x)
     deq = orc.q1_dequant if kind.startswith("q1") else orc.q2t_dequant
-    assert np.array_equal(y, deq(w, s, K).astype(np.float32).T)
+    assert np.array_equal(y, deq(w, s, K).astype(np.float32).T[:M])
 
 
 # ---- ragged and edge shapes ---------------------------------------------------------------
@@ -153,11 +155,14 @@ EDGE = {
                 (1, 40000, 256), (1, 17000, 6144), (1, 16500, 8192)],
     "q2t_gemv": [(1, 1, 128), (1, 63, 256), (2, 65, 384), (8, 1000, 1152), (7, 777, 2048),
                  (1, 130, 131072), (4, 4097, 640)],
+    # M <= 80 runs the small-M kernel in 16-row blocks of x (ragged last block), above it the tiles
     "q1_gemm": [(1, 1, 128), (17, 100, 256), (130, 257, 384), (128, 128, 512), (256, 384, 1024),
-                (5, 3000, 640), (300, 70, 2048), (16, 40, 131072), (64, 300, 1152), (200, 520, 3200)],
+                (5, 3000, 640), (300, 70, 2048), (16, 40, 131072), (64, 300, 1152), (200, 520, 3200),
+                (33, 2000, 1024), (80, 777, 640), (81, 777, 640)],
     # ternary prefill: 512-k chunks, odd G (2-byte scale copies), K not a multiple of 512
     "q2t_gemm": [(1, 1, 128), (17, 100, 256), (130, 257, 384), (128, 128, 512), (256, 384, 1024),
-                 (5, 3000, 640), (300, 70, 2048), (16, 40, 131072), (64, 300, 1152), (200, 520, 3200)],
+                 (5, 3000, 640), (300, 70, 2048), (16, 40, 131072), (64, 300, 1152), (200, 520, 3200),
+                 (33, 2000, 1024), (80, 777, 640), (81, 777, 640)],
 }
 
 
