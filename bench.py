@@ -485,6 +485,27 @@ def main() -> int:
         log(f"ternary prefill gemm: {t6 * 1e3:.1f} us, {tf6:.1f} TFLOP/s")
         del ws, ss, w, s, x, y
 
+        # The GEMM entry point at a few rows of x (several draft tokens checked at once): the
+        # small-M kernel, 16 rows of x per pass over the weights
+        small = {}
+        w, s, _ = (up(a) for a in synth.make_q1(1, N4, K))
+        R6 = max(3, math.ceil(ROTATE_BYTES / q1_bytes(N4, K)))
+        ws = [w] + [w.clone() for _ in range(R6 - 1)]
+        ss = [s] + [s.clone() for _ in range(R6 - 1)]
+        for M6 in (16, 64):
+            x = up(synth.make_q1(M6, N4, K)[2])
+            y = torch.empty((M6, N4), dtype=torch.float32, device=dev)
+            bonsai.q1_gemm(ws[0], ss[0], x, out=y)
+            kt6 = kernel_times(hip, bonsai, [lambda j=j: bonsai.q1_gemm(ws[j % R6], ss[j % R6], x, out=y)
+                                             for j in range(R6)])
+            t6 = float(np.mean(kt6))
+            small[f"M{M6}"] = {"avg_kernel_us": round(t6 * 1e3, 2),
+                               "TFLOPs": round(2.0 * M6 * N4 * K / (t6 / 1e3) / 1e12, 2),
+                               "packed_weight_GBps": round(q1_bytes(N4, K) / (t6 / 1e3) / 1e9, 1)}
+            log(f"small-M gemm M={M6}: {t6 * 1e3:.2f} us")
+        extra["small_m_gemm"] = {"shape": "N=13824 K=5120, binary", **small}
+        del ws, ss, w, s, x, y
+
         # Ternary decode GEMV, M = 1 and 8
         N5 = 5120
         tern = {}
