@@ -88,6 +88,14 @@ bonsai_status bonsai_q2t_gemv(const uint32_t *wcodes, const uint16_t *scales, co
 bonsai_status bonsai_q2t_gemm(const uint32_t *wcodes, const uint16_t *scales, const uint16_t *x,
                               float *y, int64_t M, int64_t N, int64_t K, void *hip_stream);
 
+/* Binary embedding gather: out[i][k] = W[ids[i]][k] (+-s, exact in binary16) for i < n_ids,
+ * from a binary g128 table wbits [V][K/32], scales [V][K/128].  The model card's highlights
+ * count the embeddings among the binary weights.  ids: int64 device array; out: binary16
+ * [n_ids][K] device array.  An id outside [0, V) gives a row of zeros (nothing outside the
+ * table is read).  n_ids == 0 or K == 0 is a no-op; otherwise as the other GPU entry points. */
+bonsai_status bonsai_q1_embed(const uint32_t *wbits, const uint16_t *scales, const int64_t *ids,
+                              uint16_t *out, int64_t n_ids, int64_t V, int64_t K, void *hip_stream);
+
 /* Host-side executable layout spec: pure functions on host memory, no device, no allocation.
  * signs/trits are int8 [N][K] row-major; K must be a multiple of 32 (binary) or 16 (ternary).
  * pack rejects values outside the alphabet with BONSAI_ERR_VALUE (output then unspecified);

@@ -39,6 +39,8 @@ for _name in ("bonsai_q1_pack", "bonsai_q1_unpack", "bonsai_q2t_pack", "bonsai_q
     _f = getattr(_lib, _name)
     _f.argtypes = [_vp, _c_i64, _c_i64, _vp]
     _f.restype = ctypes.c_int
+_lib.bonsai_q1_embed.argtypes = [_vp, _vp, _vp, _vp, _c_i64, _c_i64, _c_i64, _vp]
+_lib.bonsai_q1_embed.restype = ctypes.c_int
 _lib.bonsai_time_next_launch.argtypes = [_vp, _vp]
 _lib.bonsai_time_next_launch.restype = ctypes.c_int
 _lib.bonsai_last_device_error.argtypes = []
@@ -127,6 +129,32 @@ def q2t_gemv(wcodes, scales, x, out=None):
 def q2t_gemm(wcodes, scales, x, out=None):
     """y[M, N] = x[M, K] W^T for ternary g128 weights on 2-bit codes, any M (bonsai_q2t_gemm)."""
     return _call("bonsai_q2t_gemm", wcodes, scales, x, out, 16)
+
+
+def q1_embed(wbits, scales, ids, out=None):
+    """out[i, :] = dequantized row ids[i] of a binary g128 table (binary16, exact); ids outside
+    [0, V) give zero rows (bonsai_q1_embed)."""
+    import torch
+
+    if wbits.dtype not in (torch.int32, torch.uint32) or scales.dtype not in (torch.float16, torch.int16, torch.uint16):
+        raise TypeError("wbits must be int32/uint32 and scales float16/int16/uint16")
+    if ids.dtype != torch.int64:
+        raise TypeError("ids must be int64")
+    for name, t in (("wbits", wbits), ("scales", scales), ("ids", ids)):
+        if not t.is_cuda or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous device tensor")
+    V, K = wbits.shape[0], wbits.shape[1] * 32
+    if tuple(scales.shape) != (V, K // 128):
+        raise ValueError(f"inconsistent shapes wbits {tuple(wbits.shape)}, scales {tuple(scales.shape)}")
+    n = ids.numel()
+    if out is None:
+        out = torch.empty((n, K), dtype=torch.float16, device=ids.device)
+    elif out.dtype not in (torch.float16, torch.int16) or tuple(out.shape) != (n, K) or not out.is_contiguous():
+        raise ValueError("out must be a contiguous float16 [n_ids, K] tensor")
+    stream = torch.cuda.current_stream(ids.device).cuda_stream
+    _check("bonsai_q1_embed", _lib.bonsai_q1_embed(wbits.data_ptr(), scales.data_ptr(), ids.data_ptr(),
+                                                   out.data_ptr(), n, V, K, stream))
+    return out
 
 
 # ---------------------------------------------------------------------------------------

@@ -102,6 +102,21 @@ bonsai_status bonsai_q2t_gemm(const uint32_t *wcodes, const uint16_t *scales, co
                [&](int m, int n, int k, hipStream_t st) { return launch_q2t_gemm(wcodes, scales, x, y, m, n, k, st); });
 }
 
+bonsai_status bonsai_q1_embed(const uint32_t *wbits, const uint16_t *scales, const int64_t *ids,
+                              uint16_t *out, int64_t n_ids, int64_t V, int64_t K, void *hip_stream)
+{
+    if (n_ids < 0 || V < 0 || K < 0 || K % 128 != 0 || K > BONSAI_MAX_K || n_ids > (1 << 30) || V > (1 << 30))
+        return BONSAI_ERR_SHAPE;
+    if (n_ids == 0 || K == 0) return BONSAI_OK;
+    if (!ids || !out || (V > 0 && (!wbits || !scales))) return BONSAI_ERR_NULL;
+    if (!aligned16(ids) || !aligned16(out) || (V > 0 && (!aligned16(wbits) || !aligned16(scales))))
+        return BONSAI_ERR_ALIGN;
+    const hipError_t e = launch_q1_embed(wbits, scales, ids, out, n_ids, V, (int)K, static_cast<hipStream_t>(hip_stream));
+    if (e == hipSuccess) return BONSAI_OK;
+    g_last_device_error = hipGetErrorName(e);
+    return BONSAI_ERR_DEVICE;
+}
+
 bonsai_status bonsai_q1_pack(const int8_t *signs, int64_t N, int64_t K, uint32_t *wbits)
 {
     if (N < 0 || K < 0 || K % 32 != 0) return BONSAI_ERR_SHAPE;

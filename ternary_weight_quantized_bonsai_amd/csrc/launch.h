@@ -19,6 +19,8 @@ hipError_t launch_q2t_gemm(const uint32_t *wcodes, const uint16_t *scales, const
 hipError_t launch_gemv_mfma(bool ternary, const uint32_t *codes, const uint16_t *scales, const uint16_t *x,
                             float *y, int M, int N, int K, hipStream_t stream);
 hipError_t launch_fill_zero(float *y, int64_t count, hipStream_t stream);
+hipError_t launch_q1_embed(const uint32_t *wbits, const uint16_t *scales, const int64_t *ids, uint16_t *out,
+                           int64_t n_ids, int64_t V, int K, hipStream_t stream);
 
 // Every kernel launch of the library goes through here: a plain hipLaunchKernel, or, when the
 // caller armed the timing hook on this thread, hipExtLaunchKernel with the caller's events.

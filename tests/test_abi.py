@@ -146,3 +146,18 @@ def test_gemm_accepts_large_m_in_validation_only(fn):
     # M = 2^30 + 1 is rejected; nothing is launched for it
     f = getattr(bonsai.raw(), fn)
     assert f(FAKE, FAKE, FAKE, FAKE, (1 << 30) + 1, 64, 128, None) == bonsai.ERR_SHAPE
+
+
+def test_embed_validation():
+    f = bonsai.raw().bonsai_q1_embed
+    p = FAKE
+    assert f(p, p, p, p, 0, 10, 128, None) == bonsai.OK              # no ids: no-op
+    assert f(None, None, None, None, 4, 10, 0, None) == bonsai.OK    # K = 0: no-op
+    assert f(p, p, None, p, 4, 10, 128, None) == bonsai.ERR_NULL
+    assert f(p, p, p, None, 4, 10, 128, None) == bonsai.ERR_NULL
+    assert f(None, p, p, p, 4, 10, 128, None) == bonsai.ERR_NULL
+    assert f(p, p, p, p, 4, 10, 100, None) == bonsai.ERR_SHAPE
+    assert f(p, p, p, p, -1, 10, 128, None) == bonsai.ERR_SHAPE
+    assert f(p, p, p, p, 4, -1, 128, None) == bonsai.ERR_SHAPE
+    assert f(p, p, p + 8, p, 4, 10, 128, None) == bonsai.ERR_ALIGN
+    assert f(p, p, p, p + 2, 4, 10, 128, None) == bonsai.ERR_ALIGN

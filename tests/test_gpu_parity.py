@@ -264,3 +264,39 @@ def test_gemm_matches_gemv_on_the_same_rows(orc):
     assert_close(yg, yref, a, "gemm")
     assert_close(yv, yref, a, "gemv")
     assert_close(yg, yv.astype(np.float64), 2 * a, "gemm vs gemv")
+
+
+# ---- embedding gather ---------------------------------------------------------------------
+def _embed(w, s, ids):
+    import ternary_weight_quantized_bonsai_amd as bonsai
+    torch, dev = torch_dev()
+    note(f"q1_embed n={ids.size} V={w.shape[0]} K={w.shape[1] * 32}")
+    out = bonsai.q1_embed(to_dev(w), to_dev(s), torch.from_numpy(ids).to(dev))
+    torch.cuda.synchronize()
+    return out.cpu().numpy().view(np.uint16)
+
+
+def _embed_ref(orc, w, s, ids, K):
+    V = w.shape[0]
+    ref = np.zeros((ids.size, K), np.uint16)
+    for i, r in enumerate(ids):
+        if 0 <= r < V:
+            ref[i] = orc.q1_dequant(w, s, K, int(r), int(r) + 1)[0].astype(np.float16).view(np.uint16)
+    return ref
+
+
+def test_embed_gather_bit_exact(orc):
+    """Rows of +-s exactly (binary16), odd G, ids out of range give zero rows."""
+    V, K = 1000, 640
+    w, s, _ = make("q1_gemv", 1, V, K, 51, "embed")
+    rng = np.random.default_rng(5)
+    ids = np.concatenate([[0, V - 1, -1, V, 1 << 40], rng.integers(0, V, 300)]).astype(np.int64)
+    assert np.array_equal(_embed(w, s, ids), _embed_ref(orc, w, s, ids, K))
+
+
+def test_embed_gather_vocab_shape(orc):
+    """The LM-head table shape (V = 248320, K = 5120), 512 sampled ids."""
+    V, K = 248320, 5120
+    w, s, _ = make("q1_gemv", 1, V, K, 0, f"{V}x{K}")
+    ids = np.random.default_rng(6).integers(0, V, 512).astype(np.int64)
+    assert np.array_equal(_embed(w, s, ids), _embed_ref(orc, w, s, ids, K))
