@@ -8,7 +8,8 @@ The arithmetic lives in ``bonsai_oracle.c`` (plain C, double precision, natural
 k order); this module compiles it with gcc and wraps it with ctypes and numpy.
 Every function follows the definition on the "1-bit Bonsai 27B" model card
 (section "Weight representation: Binary g128": sign bit 0 -> -scale,
-1 -> +scale, 128 consecutive weights per FP16 scale) and, for ternary weights,
+1 -> +scale, 128 consecutive weights per FP16 scale), for MLX's affine 1-bit form
+(section "MLX packaging": scale * bit + bias per group), and, for ternary weights,
 the "Ternary Bonsai 27B" article ({-1, 0, +1} x FP16 group scale on 2-bit
 storage; the 2-bit code 00 -> 0, 01 -> +1, 11 -> -1 is this library's reading).
 
@@ -81,6 +82,11 @@ class Oracle:
             f = getattr(lib, fn)
             f.argtypes = _MM_ARGS + [_dp]
             f.restype = ctypes.c_int
+        lib.bo_q1a_dequant.argtypes = [_u32p, _u16p, _u16p, ctypes.c_int64, ctypes.c_int64,
+                                       ctypes.c_int64, ctypes.c_int64, _dp]
+        lib.bo_q1a_dequant.restype = ctypes.c_int
+        lib.bo_q1a_matmul.argtypes = [_u32p, _u16p, _u16p] + _MM_ARGS[2:] + [_dp]
+        lib.bo_q1a_matmul.restype = ctypes.c_int
         for fn in ("bo_q1_exact", "bo_q2t_exact"):
             f = getattr(lib, fn)
             f.argtypes = _MM_ARGS
@@ -112,8 +118,22 @@ class Oracle:
         return self._dequant("bo_q2t_dequant", wcodes, scales, K, n0,
                              wcodes.shape[0] if n1 is None else n1)
 
+    def q1a_dequant(self, wbits, scales, biases, K, n0=0, n1=None):
+        """Dense double rows of the affine 1-bit matrix: w = scale * bit + bias per group."""
+        wbits = np.ascontiguousarray(wbits, dtype=np.uint32)
+        scales = np.ascontiguousarray(scales, dtype=np.uint16)
+        biases = np.ascontiguousarray(biases, dtype=np.uint16)
+        N = wbits.shape[0]
+        n1 = N if n1 is None else n1
+        W = np.empty((n1 - n0, K), dtype=np.float64)
+        rc = self._lib.bo_q1a_dequant(_ptr(wbits, _u32p), _ptr(scales, _u16p), _ptr(biases, _u16p),
+                                      N, K, n0, n1, _ptr(W, _dp))
+        if rc:
+            raise OracleError("bo_q1a_dequant", rc)
+        return W
+
     # -- matmul ------------------------------------------------------------------------------
-    def _mm(self, fn, words, scales, x, K, m_idx, n_idx, with_abs):
+    def _mm(self, fn, words, scales, x, K, m_idx, n_idx, with_abs, biases=None):
         words = np.ascontiguousarray(words, dtype=np.uint32)
         scales = np.ascontiguousarray(scales, dtype=np.uint16)
         x = np.ascontiguousarray(x, dtype=np.uint16)
@@ -126,6 +146,9 @@ class Oracle:
         args = [_ptr(words, _u32p), _ptr(scales, _u16p), _ptr(x, _u16p), M, N, K,
                 None if mi is None else _ptr(mi, _i64p), mc,
                 None if ni is None else _ptr(ni, _i64p), nc, _ptr(y, _dp)]
+        if biases is not None:
+            biases = np.ascontiguousarray(biases, dtype=np.uint16)
+            args.insert(2, _ptr(biases, _u16p))
         a = None
         if with_abs is not None:
             a = np.empty_like(y)
@@ -141,6 +164,10 @@ class Oracle:
 
     def q2t_matmul(self, wcodes, scales, x, K, m_idx=None, n_idx=None):
         return self._mm("bo_q2t_matmul", wcodes, scales, x, K, m_idx, n_idx, True)
+
+    def q1a_matmul(self, wbits, scales, biases, x, K, m_idx=None, n_idx=None):
+        """(y, a) for affine 1-bit weights (MLX's scale-and-bias form, model card 'MLX packaging')."""
+        return self._mm("bo_q1a_matmul", wbits, scales, x, K, m_idx, n_idx, True, biases=biases)
 
     def q1_exact(self, wbits, scales, x, K, m_idx=None, n_idx=None):
         """y computed exactly (128-bit fixed point), rounded once to double."""

@@ -14,6 +14,10 @@
  * Binary g128"): each weight is one sign bit, bit 0 stands for -scale and bit 1
  * for +scale, and every 128 consecutive weights share one FP16 scale.
  *
+ * Affine 1-bit weights (model card, "MLX packaging"): MLX's grouped low-bit format keeps a
+ * scale a and a bias b per group of 128, and a 1-bit weight is a * q + b for its bit q; the
+ * binary weights are packed there as a = 2 s, b = -s, which gives back +-s.
+ *
  * Ternary weights ("Ternary Bonsai 27B" article, sections on the ternary format
  * and on its limitations): weights are {-1, 0, +1} times a per-128 FP16 scale,
  * held today in 2-bit storage.  The pages do not give the 2-bit code; the code
@@ -73,6 +77,16 @@ static double q1_weight(const uint32_t *wbits, const uint16_t *scales, int64_t K
     return bit ? s : -s;
 }
 
+/* Affine 1-bit weight (n,k): a * q + b with q the bit and (a, b) the group's scale and bias. */
+static double q1a_weight(const uint32_t *wbits, const uint16_t *scales, const uint16_t *biases, int64_t K,
+                         int64_t n, int64_t k)
+{
+    const uint32_t word = wbits[n * (K / 32) + k / 32];
+    const double q = (double)((word >> (k % 32)) & 1u);
+    const int64_t g = n * (K / 128) + k / 128;
+    return bo_f16_to_f64(scales[g]) * q + bo_f16_to_f64(biases[g]);
+}
+
 /* Ternary code of weight (n,k): 0 -> 0, 1 -> +1, 3 -> -1, 2 -> reserved (returns 0 on success). */
 static int q2t_trit(const uint32_t *wcodes, int64_t K, int64_t n, int64_t k, int *t)
 {
@@ -97,6 +111,16 @@ int bo_q1_dequant(const uint32_t *wbits, const uint16_t *scales, int64_t N, int6
     return BO_OK;
 }
 
+int bo_q1a_dequant(const uint32_t *wbits, const uint16_t *scales, const uint16_t *biases, int64_t N, int64_t K,
+                   int64_t n0, int64_t n1, double *W)
+{
+    if (!shape_ok(0, N, K) || n0 < 0 || n1 > N || n0 > n1) return BO_ERR_SHAPE;
+    for (int64_t n = n0; n < n1; ++n)
+        for (int64_t k = 0; k < K; ++k)
+            W[(n - n0) * K + k] = q1a_weight(wbits, scales, biases, K, n, k);
+    return BO_OK;
+}
+
 int bo_q2t_dequant(const uint32_t *wcodes, const uint16_t *scales, int64_t N, int64_t K,
                    int64_t n0, int64_t n1, double *W)
 {
@@ -113,8 +137,9 @@ int bo_q2t_dequant(const uint32_t *wcodes, const uint16_t *scales, int64_t N, in
 /* The selected (m, n) entries of y = x W^T and of a = |x| |W|^T.
  * m_idx / n_idx list the rows of x and of W to evaluate (NULL: all of them, in order);
  * y and a are [m_cnt][n_cnt] row-major. */
-static int matmul(int ternary, const uint32_t *words, const uint16_t *scales, const uint16_t *x,
-                  int64_t M, int64_t N, int64_t K,
+/* form: 0 binary, 1 ternary, 2 affine 1-bit (biases used only there) */
+static int matmul(int form, const uint32_t *words, const uint16_t *scales, const uint16_t *biases,
+                  const uint16_t *x, int64_t M, int64_t N, int64_t K,
                   const int64_t *m_idx, int64_t m_cnt, const int64_t *n_idx, int64_t n_cnt,
                   double *y, double *a)
 {
@@ -131,8 +156,9 @@ static int matmul(int ternary, const uint32_t *words, const uint16_t *scales, co
     int rc = BO_OK;
     for (int64_t j = 0; j < n_cnt && rc == BO_OK; ++j) {
         const int64_t n = n_idx ? n_idx[j] : j;
-        rc = ternary ? bo_q2t_dequant(words, scales, N, K, n, n + 1, wrow)
-                     : bo_q1_dequant(words, scales, N, K, n, n + 1, wrow);
+        rc = form == 1 ? bo_q2t_dequant(words, scales, N, K, n, n + 1, wrow)
+           : form == 2 ? bo_q1a_dequant(words, scales, biases, N, K, n, n + 1, wrow)
+                       : bo_q1_dequant(words, scales, N, K, n, n + 1, wrow);
         for (int64_t i = 0; i < m_cnt && rc == BO_OK; ++i) {
             const int64_t m = m_idx ? m_idx[i] : i;
             double acc = 0.0, mag = 0.0;
@@ -154,7 +180,15 @@ int bo_q1_matmul(const uint32_t *wbits, const uint16_t *scales, const uint16_t *
                  const int64_t *m_idx, int64_t m_cnt, const int64_t *n_idx, int64_t n_cnt,
                  double *y, double *a)
 {
-    return matmul(0, wbits, scales, x, M, N, K, m_idx, m_cnt, n_idx, n_cnt, y, a);
+    return matmul(0, wbits, scales, NULL, x, M, N, K, m_idx, m_cnt, n_idx, n_cnt, y, a);
+}
+
+int bo_q1a_matmul(const uint32_t *wbits, const uint16_t *scales, const uint16_t *biases, const uint16_t *x,
+                  int64_t M, int64_t N, int64_t K,
+                  const int64_t *m_idx, int64_t m_cnt, const int64_t *n_idx, int64_t n_cnt,
+                  double *y, double *a)
+{
+    return matmul(2, wbits, scales, biases, x, M, N, K, m_idx, m_cnt, n_idx, n_cnt, y, a);
 }
 
 int bo_q2t_matmul(const uint32_t *wcodes, const uint16_t *scales, const uint16_t *x,
@@ -162,7 +196,7 @@ int bo_q2t_matmul(const uint32_t *wcodes, const uint16_t *scales, const uint16_t
                   const int64_t *m_idx, int64_t m_cnt, const int64_t *n_idx, int64_t n_cnt,
                   double *y, double *a)
 {
-    return matmul(1, wcodes, scales, x, M, N, K, m_idx, m_cnt, n_idx, n_cnt, y, a);
+    return matmul(1, wcodes, scales, NULL, x, M, N, K, m_idx, m_cnt, n_idx, n_cnt, y, a);
 }
 
 /* ---- exact fixed-point cross-check ------------------------------------------------------- */

@@ -155,6 +155,59 @@ def pin_mlx_identity(o):
     assert np.array_equal(o.q1_dequant(w, s, K), mlx)
 
 
+def pin_affine_forms(o):
+    """Affine 1-bit weights (model card, 'MLX packaging': a scale and a bias per group of 128,
+    weight = scale * bit + bias).  Fixed outside the oracle by: the native sign form re-encoded
+    as (2 s, -s), which must reproduce the binary oracle exactly; one-hot bit probes read through
+    the byte view with distinct scales and biases per group; a zero scale, where y reduces to
+    the bias times the group sums of x; and Python integer brute force on integer data."""
+    # (2 s, -s): same weights, same sums, same magnitudes as the native binary form
+    M, N, K = 3, 5, 640
+    w, s, x = synth.make_q1(M, N, K, 21, "pin/affine")
+    a2 = _f16(2.0 * _lib_f16(s))
+    bneg = s ^ np.uint16(0x8000)
+    assert np.array_equal(o.q1a_dequant(w, a2, bneg, K), o.q1_dequant(w, s, K))
+    y1, m1 = o.q1_matmul(w, s, x, K)
+    ya, ma = o.q1a_matmul(w, a2, bneg, x, K)
+    assert np.array_equal(ya, y1) and np.array_equal(ma, m1)
+
+    # one-hot bits: only weight (n, k) takes scale + bias, every other weight its group's bias
+    N, K = 2, 384
+    sc = _f16([[3.0, 5.0, 7.0], [11.0, 13.0, 17.0]])
+    bi = _f16([[-0.5, -0.25, -2.0], [-4.0, 0.75, 1.5]])
+    for (n, k) in [(0, 0), (0, 31), (0, 32), (0, 200), (1, 127), (1, 128), (1, 383)]:
+        words = np.zeros((N, K // 32), dtype=np.uint32)
+        words[n].view(np.uint8)[k // 8] = np.uint8(1 << (k % 8))
+        assert _sign_bit(words, n, k) == 1
+        W = o.q1a_dequant(words, sc, bi, K)
+        want = np.repeat(_lib_f16(bi), 128, axis=1)
+        want[n, k] += _lib_f16(sc)[n, k // 128]
+        assert np.array_equal(W, want), (n, k)
+
+    # zero scale: y[m][n] = sum over groups of bias(n, g) * (sum of x over the group)
+    M, N, K = 2, 3, 512
+    w, s, x = synth.make_q1(M, N, K, 22, "pin/affine0")
+    b = synth.scales_f16(N, K // 128, 23, "pin/affine0b")
+    y, _ = o.q1a_matmul(w, np.zeros_like(s), b, x, K)
+    gx = _lib_f16(x).reshape(M, K // 128, 128).sum(axis=2)            # [M, G]
+    want = gx @ _lib_f16(b).T                                           # [M, N]
+    assert np.allclose(y, want, rtol=1e-12, atol=1e-12)
+
+    # integer data: exact from Python integers through the byte view
+    N, K = 3, 256
+    rng = np.random.default_rng(24)
+    w = synth.sign_words(N, K // 32, 24, "pin/affineint")
+    av = rng.integers(-6, 7, (N, K // 128))
+    bv = rng.integers(-6, 7, (N, K // 128))
+    xv = rng.integers(-8, 9, (2, K))
+    y, _ = o.q1a_matmul(w, _f16(av), _f16(bv), _f16(xv), K)
+    for m in range(2):
+        for n in range(N):
+            want = sum((int(av[n, k // 128]) * _sign_bit(w, n, k) + int(bv[n, k // 128])) * int(xv[m, k])
+                       for k in range(K))
+            assert y[m, n] == want, (m, n)
+
+
 def pin_metamorphic(o):
     """y(-x) = -y(x), y(2s) = 2 y(s) and y(~signs) = -y(signs), all exactly."""
     M, N, K = 3, 9, 768
@@ -280,7 +333,7 @@ def pin_storage_figures(o):
 
 ALL_PINS = [
     pin_f16_decoder, pin_all_ones_all_zero, pin_popcount, pin_onehot, pin_byte_patterns,
-    pin_exact_vs_double, pin_mlx_identity, pin_metamorphic, pin_ternary_zero_and_mask,
+    pin_exact_vs_double, pin_mlx_identity, pin_affine_forms, pin_metamorphic, pin_ternary_zero_and_mask,
     pin_ternary_counts_and_onehot, pin_reserved_and_shapes, pin_golden_hand_cases,
     pin_storage_figures,
 ]

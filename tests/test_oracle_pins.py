@@ -37,6 +37,13 @@ MUTANTS = {
                               "case 1: *t = -1; return 0;\n    case 3: *t = 1;"),
     "ternary_field_order": ("(word >> (2 * (k % 16))) & 3u;", "(word >> (30 - 2 * (k % 16))) & 3u;"),
     "ternary_reserved_as_zero": ("default: return BO_ERR_CODE;", "default: *t = 0; return 0;"),
+    "affine_bias_dropped": ("* q + bo_f16_to_f64(biases[g]);", "* q;"),
+    "affine_scale_bias_swapped": ("return bo_f16_to_f64(scales[g]) * q + bo_f16_to_f64(biases[g]);",
+                                  "return bo_f16_to_f64(biases[g]) * q + bo_f16_to_f64(scales[g]);"),
+    "affine_bit_inverted": ("const double q = (double)((word >> (k % 32)) & 1u);",
+                            "const double q = (double)(((~word) >> (k % 32)) & 1u);"),
+    "affine_group_of_64": ("const int64_t g = n * (K / 128) + k / 128;",
+                           "const int64_t g = n * (K / 128) + (k / 64) % (K / 128);"),
     "f16_bias_off_by_one": ("ldexp((double)(1024 + f), e - 25)", "ldexp((double)(1024 + f), e - 24)"),
     "f16_subnormal_wrong": ("ldexp((double)f, -24)", "ldexp((double)f, -25)"),
     "f16_implicit_bit_dropped": ("ldexp((double)(1024 + f), e - 25)", "ldexp((double)f, e - 25)"),
