@@ -55,7 +55,8 @@ typedef enum {
     BONSAI_ERR_NULL = 1,    /* a required pointer is NULL                                   */
     BONSAI_ERR_SHAPE = 2,   /* M, N or K negative or out of range, or K % 128 != 0           */
     BONSAI_ERR_ALIGN = 3,   /* a device pointer is not 16-byte aligned                       */
-    BONSAI_ERR_VALUE = 4,   /* pack input outside {-1,+1} (binary) or {-1,0,+1} (ternary)    */
+    BONSAI_ERR_VALUE = 4,   /* pack input outside {-1,+1} (binary) or {-1,0,+1} (ternary);
+                               an affine conversion whose result is not exact (see below)    */
     BONSAI_ERR_CODE = 5,    /* unpack met the reserved ternary field value 2                 */
     BONSAI_ERR_DEVICE = 6   /* the HIP runtime refused the launch                            */
 } bonsai_status;
@@ -95,6 +96,29 @@ bonsai_status bonsai_q2t_gemm(const uint32_t *wcodes, const uint16_t *scales, co
  * table is read).  n_ids == 0 or K == 0 is a no-op; otherwise as the other GPU entry points. */
 bonsai_status bonsai_q1_embed(const uint32_t *wbits, const uint16_t *scales, const int64_t *ids,
                               uint16_t *out, int64_t n_ids, int64_t V, int64_t K, void *hip_stream);
+
+/* Affine 1-bit matmul: y[M][N] = x[M][K] * W^T with W[n][k] = a * q + b, q the bit of W[n][k] in
+ * the binary layout above and (a, b) = (mlx_scales, biases)[n][k / 128], binary16 [N][K/128]
+ * each.  This is MLX's grouped low-bit format at one bit (model card, "MLX packaging": one
+ * scale and one bias per group of 128; the binary weights travel in it as a = 2s, b = -s).
+ * Any M >= 0 (16 rows of x per pass of the small-M matrix-core kernel; built for decode and
+ * short M).  The sum is taken as a * sum(q x) + b * sum(x) per group in float32, so the
+ * accuracy bound is 1e-3 * sum_k (|a q x| + |b x|) + 1e-6, which for a = 2s, b = -s is at most
+ * three times the binary entry points' bound.  Otherwise as the other GPU entry points;
+ * biases is a device pointer like mlx_scales. */
+bonsai_status bonsai_q1a_matmul(const uint32_t *wbits, const uint16_t *mlx_scales, const uint16_t *biases,
+                                const uint16_t *x, float *y, int64_t M, int64_t N, int64_t K, void *hip_stream);
+
+/* Host conversions between the binary scales and MLX's (scale, bias) pairs for the same sign
+ * words (model card, "MLX packaging"), bit-exact, on host arrays of n_groups binary16 values:
+ * to_affine writes a = 2s and b = -s (BONSAI_ERR_VALUE if 2s is not finite: |s| > 32752,
+ * inf or NaN); from_affine writes s = -b and returns BONSAI_ERR_VALUE unless a == 2s exactly
+ * for every group (i.e. unless the affine weights are exactly +-s).  On an error the outputs
+ * are unspecified.  n_groups == 0 is a no-op. */
+bonsai_status bonsai_q1_to_affine(const uint16_t *scales, int64_t n_groups, uint16_t *mlx_scales,
+                                  uint16_t *mlx_biases);
+bonsai_status bonsai_q1_from_affine(const uint16_t *mlx_scales, const uint16_t *mlx_biases, int64_t n_groups,
+                                    uint16_t *scales);
 
 /* Host-side executable layout spec: pure functions on host memory, no device, no allocation.
  * signs/trits are int8 [N][K] row-major; K must be a multiple of 32 (binary) or 16 (ternary).

@@ -13,6 +13,8 @@ returned in its storage form:
 * scales       - IEEE binary16 bit patterns (uint16) of |N(0, 0.02)| + 1e-3,
                  rounded to nearest-even by numpy's float16 conversion.
 * activations  - IEEE binary16 bit patterns (uint16) of N(0, 1).
+* biases       - IEEE binary16 bit patterns (uint16) of N(0, 0.02), for the
+                 affine (scale, bias) form of the binary words.
 
 The workload shapes are those of the model card ("1-bit Bonsai 27B",
 model-overview table and the config summary on the Bonsai-27B article):
@@ -28,7 +30,7 @@ import numpy as np
 
 __all__ = [
     "Config", "CONFIGS", "rng_for", "sign_words", "trit_words", "scales_f16",
-    "activations_f16", "make_q1", "make_q2t", "digest",
+    "activations_f16", "biases_f16", "make_q1", "make_q2t", "make_q1a", "digest",
 ]
 
 
@@ -96,6 +98,12 @@ def activations_f16(m: int, k: int, seed: int, tag: str) -> np.ndarray:
     return rng.standard_normal(size=(m, k)).astype(np.float16).view(np.uint16)
 
 
+def biases_f16(n_rows: int, n_groups: int, seed: int, tag: str) -> np.ndarray:
+    """uint16 [n_rows, n_groups]: binary16 bits of N(0, 0.02) (either sign)."""
+    rng = rng_for(seed, tag + "/biases")
+    return (rng.standard_normal(size=(n_rows, n_groups)) * 0.02).astype(np.float16).view(np.uint16)
+
+
 def make_q1(M: int, N: int, K: int, seed: int = 0, tag: str | None = None):
     """(sign words [N, K/32], scales [N, K/128], x [M, K]) for a binary matmul."""
     tag = tag or f"{N}x{K}"
@@ -108,6 +116,13 @@ def make_q2t(M: int, N: int, K: int, seed: int = 0, tag: str | None = None):
     tag = tag or f"t{N}x{K}"
     return (trit_words(N, K // 16, seed, tag), scales_f16(N, K // 128, seed, tag),
             activations_f16(M, K, seed, f"{tag}/M{M}"))
+
+
+def make_q1a(M: int, N: int, K: int, seed: int = 0, tag: str | None = None):
+    """(sign words, scales, biases [N, K/128], x) for an affine 1-bit matmul."""
+    tag = tag or f"a{N}x{K}"
+    w, s, x = make_q1(M, N, K, seed, tag)
+    return w, s, biases_f16(N, K // 128, seed, tag), x
 
 
 def digest(buf: np.ndarray) -> str:

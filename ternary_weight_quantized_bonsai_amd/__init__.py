@@ -39,6 +39,12 @@ for _name in ("bonsai_q1_pack", "bonsai_q1_unpack", "bonsai_q2t_pack", "bonsai_q
     _f = getattr(_lib, _name)
     _f.argtypes = [_vp, _c_i64, _c_i64, _vp]
     _f.restype = ctypes.c_int
+_lib.bonsai_q1a_matmul.argtypes = [_vp, _vp, _vp, _vp, _vp, _c_i64, _c_i64, _c_i64, _vp]
+_lib.bonsai_q1a_matmul.restype = ctypes.c_int
+_lib.bonsai_q1_to_affine.argtypes = [_vp, _c_i64, _vp, _vp]
+_lib.bonsai_q1_to_affine.restype = ctypes.c_int
+_lib.bonsai_q1_from_affine.argtypes = [_vp, _vp, _c_i64, _vp]
+_lib.bonsai_q1_from_affine.restype = ctypes.c_int
 _lib.bonsai_q1_embed.argtypes = [_vp, _vp, _vp, _vp, _c_i64, _c_i64, _c_i64, _vp]
 _lib.bonsai_q1_embed.restype = ctypes.c_int
 _lib.bonsai_time_next_launch.argtypes = [_vp, _vp]
@@ -131,6 +137,20 @@ def q2t_gemm(wcodes, scales, x, out=None):
     return _call("bonsai_q2t_gemm", wcodes, scales, x, out, 16)
 
 
+def q1a_matmul(wbits, mlx_scales, biases, x, out=None):
+    """y[M, N] = x[M, K] W^T for affine 1-bit weights W = a q + b per group of 128 (MLX's 1-bit
+    form of the binary words; bonsai_q1a_matmul), any M."""
+    import torch
+
+    M, N, K, out, stream = _dev_args(wbits, mlx_scales, x, out, 32)
+    if biases.dtype not in (torch.float16, torch.int16, torch.uint16) or not biases.is_cuda \
+            or not biases.is_contiguous() or tuple(biases.shape) != tuple(mlx_scales.shape):
+        raise ValueError("biases must be a contiguous binary16 device tensor shaped like the scales")
+    _check("bonsai_q1a_matmul", _lib.bonsai_q1a_matmul(wbits.data_ptr(), mlx_scales.data_ptr(), biases.data_ptr(),
+                                                       x.data_ptr(), out.data_ptr(), M, N, K, stream))
+    return out
+
+
 def q1_embed(wbits, scales, ids, out=None):
     """out[i, :] = dequantized row ids[i] of a binary g128 table (binary16, exact); ids outside
     [0, V) give zero rows (bonsai_q1_embed)."""
@@ -165,6 +185,24 @@ def _host(a, dtype):
     if a.dtype != dtype:
         raise TypeError(f"expected {np.dtype(dtype)}, got {a.dtype}")
     return a
+
+
+def q1_to_affine(scales: np.ndarray):
+    """Binary scales (binary16 bits) -> MLX (scale, bias) = (2 s, -s), bit-exact (bonsai_q1_to_affine)."""
+    s = _host(scales, np.uint16)
+    a, b = np.empty_like(s), np.empty_like(s)
+    _check("bonsai_q1_to_affine", _lib.bonsai_q1_to_affine(s.ctypes.data, s.size, a.ctypes.data, b.ctypes.data))
+    return a, b
+
+
+def q1_from_affine(mlx_scales: np.ndarray, biases: np.ndarray) -> np.ndarray:
+    """MLX (scale, bias) with scale == -2 bias exactly -> binary scales (bonsai_q1_from_affine)."""
+    a, b = _host(mlx_scales, np.uint16), _host(biases, np.uint16)
+    if a.shape != b.shape:
+        raise ValueError("scales and biases must have the same shape")
+    s = np.empty_like(a)
+    _check("bonsai_q1_from_affine", _lib.bonsai_q1_from_affine(a.ctypes.data, b.ctypes.data, a.size, s.ctypes.data))
+    return s
 
 
 def q1_pack(signs: np.ndarray) -> np.ndarray:

@@ -36,6 +36,17 @@ bonsai_status check_gpu_args(const void *w, const void *s, const void *x, const 
     return BONSAI_OK;
 }
 
+// 2 s in binary16, exactly (an exponent step, or a shift of a subnormal's fraction, which
+// carries into the exponent by itself); false when 2 s is not finite or s is inf / NaN
+bool f16_twice(uint16_t s, uint16_t *out)
+{
+    const uint16_t sign = s & 0x8000u, mag = s & 0x7FFFu;
+    const unsigned e = mag >> 10;
+    if (e >= 30) return false;
+    *out = (uint16_t)(sign | (e == 0 ? mag << 1 : mag + 0x400u));
+    return true;
+}
+
 template <typename Launch>
 bonsai_status run(const void *w, const void *s, const void *x, float *y, int64_t M, int64_t N,
                   int64_t K, int64_t max_m, void *stream, Launch launch)
@@ -100,6 +111,46 @@ bonsai_status bonsai_q2t_gemm(const uint32_t *wcodes, const uint16_t *scales, co
 {
     return run(wcodes, scales, x, y, M, N, K, -1, hip_stream,
                [&](int m, int n, int k, hipStream_t st) { return launch_q2t_gemm(wcodes, scales, x, y, m, n, k, st); });
+}
+
+bonsai_status bonsai_q1a_matmul(const uint32_t *wbits, const uint16_t *scales, const uint16_t *biases,
+                                const uint16_t *x, float *y, int64_t M, int64_t N, int64_t K, void *hip_stream)
+{
+    if (M > 0 && N > 0 && K > 0 && K % 128 == 0 && K <= BONSAI_MAX_K && N <= (1 << 30) && M <= (1 << 30)) {
+        if (!biases) return BONSAI_ERR_NULL;
+        if (!aligned16(biases)) return BONSAI_ERR_ALIGN;
+    }
+    return run(wbits, scales, x, y, M, N, K, -1, hip_stream, [&](int m, int n, int k, hipStream_t st) {
+        return launch_q1a_matmul(wbits, scales, biases, x, y, m, n, k, st);
+    });
+}
+
+bonsai_status bonsai_q1_to_affine(const uint16_t *scales, int64_t n_groups, uint16_t *mlx_scales,
+                                  uint16_t *mlx_biases)
+{
+    if (n_groups < 0) return BONSAI_ERR_SHAPE;
+    if (n_groups == 0) return BONSAI_OK;
+    if (!scales || !mlx_scales || !mlx_biases) return BONSAI_ERR_NULL;
+    for (int64_t g = 0; g < n_groups; ++g) {
+        if (!f16_twice(scales[g], &mlx_scales[g])) return BONSAI_ERR_VALUE;
+        mlx_biases[g] = (uint16_t)(scales[g] ^ 0x8000u);
+    }
+    return BONSAI_OK;
+}
+
+bonsai_status bonsai_q1_from_affine(const uint16_t *mlx_scales, const uint16_t *mlx_biases, int64_t n_groups,
+                                    uint16_t *scales)
+{
+    if (n_groups < 0) return BONSAI_ERR_SHAPE;
+    if (n_groups == 0) return BONSAI_OK;
+    if (!scales || !mlx_scales || !mlx_biases) return BONSAI_ERR_NULL;
+    for (int64_t g = 0; g < n_groups; ++g) {
+        const uint16_t s = (uint16_t)(mlx_biases[g] ^ 0x8000u);
+        uint16_t twice;
+        if (!f16_twice(s, &twice) || twice != mlx_scales[g]) return BONSAI_ERR_VALUE;
+        scales[g] = s;
+    }
+    return BONSAI_OK;
 }
 
 bonsai_status bonsai_q1_embed(const uint32_t *wbits, const uint16_t *scales, const int64_t *ids,
@@ -198,7 +249,7 @@ const char *bonsai_status_str(bonsai_status s)
     case BONSAI_ERR_NULL: return "a required pointer is NULL";
     case BONSAI_ERR_SHAPE: return "M, N or K out of range, or K not a multiple of 128";
     case BONSAI_ERR_ALIGN: return "a device pointer is not 16-byte aligned";
-    case BONSAI_ERR_VALUE: return "pack input outside the weight alphabet";
+    case BONSAI_ERR_VALUE: return "input outside the weight alphabet, or not an exact binary-weight scale/bias pair";
     case BONSAI_ERR_CODE: return "reserved ternary code 0b10";
     case BONSAI_ERR_DEVICE: return "HIP launch failed";
     }

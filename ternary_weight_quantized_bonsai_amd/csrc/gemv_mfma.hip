@@ -15,11 +15,21 @@
 //   ternary the block is two words of 16 codes: pair i of quarter q is fields j = 2q + (i % 2)
 //           and j + 8 of word i / 2; (w << (14 - 2j)) & 0xC000C000 reads codes 00, 01, 11 as
 //           0, +2, -2 (the exponent MSB is the code's low bit, the sign its high bit).
+//   affine  binary words again, but the operand is the bit itself, q 2^-7 (binary16 0x2000 or 0):
+//           rotate the word so that bit 4q+i lands on bit 13, mask with 0x20002000.
 // B holds x at the same k.  Column j of D depends on column j of B alone, so the lanes of the
 // columns past M read row M - 1 again (a broadcast) and those columns are never stored.
 // The group scale multiplies each group's four chained MFMAs afterwards, one mixed-precision
 // FMA per output straight from the binary16 scale, so the operands stay exact small integers
 // and every product is exact; the ternary factor 2 comes off the sums once at the end.
+//
+// Affine weights (MLX's 1-bit form: a scale a and a bias b per group, weight a q + b for the bit
+// q; "1-bit Bonsai 27B" model card, "MLX packaging") split each group's sum into a times the
+// q-weighted sum D and b times the plain sum X of x over the group.  X does not depend on the
+// weight row: each lane adds up its quarter's 32 halves of the group with v_dot2 against (1, 1)
+// on the B operand it already holds, and two lane exchanges (quarters 16 and 32 lanes apart)
+// complete the column's sum.  The operand's 2^-7 comes off at the end with the bias term scaled
+// to match: acc = sum_g a_g D_g + b_g X_g 2^-7, y = 128 acc.
 //
 // Rows of x beyond 16 take more column blocks: blockIdx.y selects rows 16 y .. 16 y + 15 of x
 // and of the output, so a skinny product (a few dozen rows of x, as in checking several draft
@@ -49,6 +59,7 @@ constexpr int kSmScaleBytes = 64 * kSmGroups * 4;   // room for one dword per (r
 
 template <bool TERN>
 struct SmLayout {
+    // (affine weights use the binary layout; their biases take a second scale-sized region)
     static constexpr int cell = TERN ? 32 : 16;           // bytes per (row, group)
     static constexpr int row_bytes = kSmGroups * cell;     // bytes per row and slice
     static constexpr int lanes_per_row = row_bytes / 16;
@@ -58,23 +69,26 @@ struct SmLayout {
     static constexpr int xstride = 1024 + (TERN ? 16 : 32);
 };
 
-// LDS bytes of one wave: codes, scales and the M rows of x
-template <bool TERN>
+// LDS bytes of one wave: codes, scales (and biases) and the M rows of x
+template <bool TERN, bool AFF>
 constexpr int sm_wave_bytes(int rt, int m)
 {
-    return 16 * rt * SmLayout<TERN>::row_bytes + kSmScaleBytes + m * SmLayout<TERN>::xstride;
+    return 16 * rt * SmLayout<TERN>::row_bytes + (AFF ? 2 : 1) * kSmScaleBytes + m * SmLayout<TERN>::xstride;
 }
 
 // four row tiles per wave need more than the 128 VGPRs that 16 waves per workgroup leave
 constexpr int sm_max_waves(int rt) { return rt >= 4 ? 12 : kSmMaxWaves; }
 
-// PAIRS: the group count is even, so a row's scales of groups 2p, 2p + 1 are one aligned dword
-template <bool TERN, int RT, bool PAIRS>
+// PAIRS: the group count is even, so a row's scales of groups 2p, 2p + 1 are one aligned dword.
+// AFF: affine 1-bit weights (binary words, scales and biases); biases is unused otherwise.
+template <bool TERN, bool AFF, int RT, bool PAIRS>
 __global__ __launch_bounds__(sm_max_waves(RT) * 64) void gemv_mfma_kernel(const uint32_t *__restrict__ codes,
                                                                      const uint16_t *__restrict__ scales,
+                                                                     const uint16_t *__restrict__ biases,
                                                                      const uint16_t *__restrict__ x,
                                                                      float *__restrict__ y, int M, int N, int K)
 {
+    static_assert(!(TERN && AFF), "affine weights are binary words");
     using L = SmLayout<TERN>;
     constexpr int R = 16 * RT;
     constexpr int TILE = R * L::row_bytes;
@@ -89,11 +103,12 @@ __global__ __launch_bounds__(sm_max_waves(RT) * 64) void gemv_mfma_kernel(const 
     const int G = K >> 7;
     const int ns = (G + kSmGroups - 1) / kSmGroups;       // slices of K
     const int n0 = blockIdx.x * R;
-    const int wbytes = sm_wave_bytes<TERN>(RT, M);
+    const int wbytes = sm_wave_bytes<TERN, AFF>(RT, M);
     char *const mine = reinterpret_cast<char *>(lds) + wave * wbytes;
     char *const tile = mine;
     char *const sc = mine + TILE;
-    char *const xs = sc + kSmScaleBytes;
+    char *const bc = sc + kSmScaleBytes;                  // biases (affine only), laid out as sc
+    char *const xs = sc + (AFF ? 2 : 1) * kSmScaleBytes;
     float *const red = reinterpret_cast<float *>(reinterpret_cast<char *>(lds) + nw * wbytes);
     const int q = lane >> 4, i16 = lane & 15;
     const int units = G * (L::cell / 16);                  // 16-byte units per weight row
@@ -122,19 +137,24 @@ __global__ __launch_bounds__(sm_max_waves(RT) * 64) void gemv_mfma_kernel(const 
         // scales: the scale of (row r, group u) is half u of the 8 bytes at sc + 8 r (PAIRS:
         // one 4-byte copy per row and pair of groups), or the low half of the dword at
         // sc + 16 r + 4 u (one 2-byte copy per row and group)
-        if constexpr (PAIRS) {
 #pragma unroll
-            for (int k = 0; k < (2 * R + 63) / 64; ++k) {
-                const int e = 64 * k + lane, r = min(e >> 1, R - 1), p = e & 1;
-                __builtin_amdgcn_global_load_lds((glb_void_t *)(scales + (size_t)min(n0 + r, N - 1) * G + min(g0 + 2 * p, G - 2)),
-                                                 (lds_void_t *)(sc + 256 * k), 4, 0, 0);
-            }
-        } else {
+        for (int which = 0; which < (AFF ? 2 : 1); ++which) {
+            const uint16_t *const src = which ? biases : scales;
+            char *const dst = which ? bc : sc;
+            if constexpr (PAIRS) {
 #pragma unroll
-            for (int k = 0; k < (4 * R + 63) / 64; ++k) {
-                const int e = 64 * k + lane, r = min(e >> 2, R - 1), u = e & 3;
-                __builtin_amdgcn_global_load_lds((glb_void_t *)(scales + (size_t)min(n0 + r, N - 1) * G + min(g0 + u, gl)),
-                                                 (lds_void_t *)(sc + 256 * k), 2, 0, 0);
+                for (int k = 0; k < (2 * R + 63) / 64; ++k) {
+                    const int e = 64 * k + lane, r = min(e >> 1, R - 1), p = e & 1;
+                    __builtin_amdgcn_global_load_lds((glb_void_t *)(src + (size_t)min(n0 + r, N - 1) * G + min(g0 + 2 * p, G - 2)),
+                                                     (lds_void_t *)(dst + 256 * k), 4, 0, 0);
+                }
+            } else {
+#pragma unroll
+                for (int k = 0; k < (4 * R + 63) / 64; ++k) {
+                    const int e = 64 * k + lane, r = min(e >> 2, R - 1), u = e & 3;
+                    __builtin_amdgcn_global_load_lds((glb_void_t *)(src + (size_t)min(n0 + r, N - 1) * G + min(g0 + u, gl)),
+                                                     (lds_void_t *)(dst + 256 * k), 2, 0, 0);
+                }
             }
         }
         // x: row m, k = 128 g0 .. 128 g0 + 511 (clamped inside K; past-K groups count 0)
@@ -143,31 +163,41 @@ __global__ __launch_bounds__(sm_max_waves(RT) * 64) void gemv_mfma_kernel(const 
                                              (lds_void_t *)(xs + m * L::xstride), 16, 0, 0);
         vm_wait<0>();                                     // this wave's slice landed
         if (g1 - g0 < kSmGroups) {
-            // groups past K (last slice only) hold clamped copies: their scales become zero
+            // groups past K (last slice only) hold clamped copies: their scales (and biases)
+            // become zero
             for (int e = lane; e < R * kSmGroups; e += 64) {
                 const int r = e >> 2, u = e & 3;
-                if (g0 + u >= g1) *reinterpret_cast<uint16_t *>(sc + (PAIRS ? 8 * r + 2 * u : 16 * r + 4 * u)) = 0;
+                const int off = PAIRS ? 8 * r + 2 * u : 16 * r + 4 * u;
+                if (g0 + u >= g1) {
+                    *reinterpret_cast<uint16_t *>(sc + off) = 0;
+                    if constexpr (AFF) *reinterpret_cast<uint16_t *>(bc + off) = 0;
+                }
             }
         }
         // the scales of this lane's D rows 16 t + 4 q + r, all four groups: the binary16 of
         // group u is half u % 2 of sp[t][r][u / 2] (PAIRS) or the low half of sp[t][r][u]
         constexpr int SW = PAIRS ? 2 : 4;
-        uint32_t sp[RT][4][SW];
+        constexpr int NB = AFF ? 2 : 1;
+        uint32_t sp[NB][RT][4][SW];                       // [0] scales, [1] biases
 #pragma unroll
-        for (int t = 0; t < RT; ++t)
+        for (int b = 0; b < NB; ++b)
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int row = 16 * t + 4 * q + r;
-                if constexpr (PAIRS) {
-                    const uint2 v = *reinterpret_cast<const uint2 *>(sc + 8 * row);
-                    sp[t][r][0] = v.x;
-                    sp[t][r][1] = v.y;
-                } else {
-                    const u32x4 v = *reinterpret_cast<const u32x4 *>(sc + 16 * row);
+            for (int t = 0; t < RT; ++t)
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) sp[t][r][e] = v[e];
+                for (int r = 0; r < 4; ++r) {
+                    const int row = 16 * t + 4 * q + r;
+                    const char *const base = b ? bc : sc;
+                    if constexpr (PAIRS) {
+                        const uint2 v = *reinterpret_cast<const uint2 *>(base + 8 * row);
+                        sp[b][t][r][0] = v.x;
+                        sp[b][t][r][1] = v.y;
+                    } else {
+                        const u32x4 v = *reinterpret_cast<const u32x4 *>(base + 16 * row);
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) sp[b][t][r][e] = v[e];
+                    }
                 }
-            }
+        float xq[kSmGroups];                              // affine: this quarter's part of X per group
 
 #pragma unroll
         for (int u = 0; u < kSmGroups; ++u) {
@@ -211,10 +241,22 @@ __global__ __launch_bounds__(sm_max_waves(RT) * 64) void gemv_mfma_kernel(const 
                     bv[3] = pack_hi(xa.y, xb.y);
                 }
                 const half8_t bf = __builtin_bit_cast(half8_t, bv);
+                if constexpr (AFF) {
+                    const half2_t one2 = {(_Float16)1.0f, (_Float16)1.0f};
+                    float xs4 = kb == 0 ? 0.f : xq[u];
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) xs4 = __builtin_amdgcn_fdot2(as_half2(bv[e]), one2, xs4, false);
+                    xq[u] = xs4;
+                }
 #pragma unroll
                 for (int t = 0; t < RT; ++t) {
                     u32x4 av;
-                    if constexpr (TERN) {
+                    if constexpr (AFF) {
+                        const uint32_t w = wd[t][kb];
+#pragma unroll
+                        for (int i = 0; i < 4; ++i)   // rotate bit 4q + i (and 16 above it) onto bit 13
+                            av[i] = __builtin_amdgcn_alignbit(w, w, (uint32_t)(4 * q + i + 19)) & 0x20002000u;
+                    } else if constexpr (TERN) {
 #pragma unroll
                         for (int i = 0; i < 4; ++i) {
                             const uint32_t w = wd[t][2 * kb + (i >> 1)];
@@ -233,9 +275,24 @@ __global__ __launch_bounds__(sm_max_waves(RT) * 64) void gemv_mfma_kernel(const 
             for (int t = 0; t < RT; ++t)
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
-                    const half2_t h = as_half2(sp[t][r][PAIRS ? u >> 1 : u]);
+                    const half2_t h = as_half2(sp[0][t][r][PAIRS ? u >> 1 : u]);
                     acc[t][r] = fmaf((float)h[PAIRS ? u & 1 : 0], d[t][r], acc[t][r]);
                 }
+        }
+        if constexpr (AFF) {
+            // the bias term: X of column i16 is the sum of the four quarters' parts
+#pragma unroll
+            for (int u = 0; u < kSmGroups; ++u) {
+                float xg = xq[u] + __shfl_xor(xq[u], 16);
+                xg = (xg + __shfl_xor(xg, 32)) * 0x1p-7f;
+#pragma unroll
+                for (int t = 0; t < RT; ++t)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        const half2_t h = as_half2(sp[NB - 1][t][r][PAIRS ? u >> 1 : u]);
+                        acc[t][r] = fmaf((float)h[PAIRS ? u & 1 : 0], xg, acc[t][r]);
+                    }
+            }
         }
         lgkm_wait0();                                     // LDS reads done before the next slice's copies
     }
@@ -245,7 +302,7 @@ __global__ __launch_bounds__(sm_max_waves(RT) * 64) void gemv_mfma_kernel(const 
 #pragma unroll
         for (int t = 0; t < RT; ++t)
 #pragma unroll
-            for (int r = 0; r < 4; ++r) red[(wave * M + i16) * R + 16 * t + 4 * q + r] = TERN ? 0.5f * acc[t][r] : acc[t][r];
+            for (int r = 0; r < 4; ++r) red[(wave * M + i16) * R + 16 * t + 4 * q + r] = TERN ? 0.5f * acc[t][r] : AFF ? 128.f * acc[t][r] : acc[t][r];
     }
     __syncthreads();
     for (int o = threadIdx.x; o < M * R; o += blockDim.x) {
@@ -259,42 +316,42 @@ __global__ __launch_bounds__(sm_max_waves(RT) * 64) void gemv_mfma_kernel(const 
 constexpr int kLdsPerCu = 160 * 1024;
 
 // waves of a workgroup: one per slice of K, at most 16 and as many as the LDS holds
-template <bool TERN>
+template <bool TERN, bool AFF>
 int sm_waves(int rt, int M, int K)
 {
     const int ns = (K / 128 + kSmGroups - 1) / kSmGroups;
-    const int per_wave = sm_wave_bytes<TERN>(rt, M) + M * 16 * rt * 4;
+    const int per_wave = sm_wave_bytes<TERN, AFF>(rt, M) + M * 16 * rt * 4;
     int nw = ns < sm_max_waves(rt) ? ns : sm_max_waves(rt);
     if (nw > kLdsPerCu / per_wave) nw = kLdsPerCu / per_wave;
     return nw;
 }
 
-template <bool TERN, int RT>
-hipError_t launch_rt(const uint32_t *codes, const uint16_t *scales, const uint16_t *x, float *y,
-                     int M, int N, int K, hipStream_t stream)
+template <bool TERN, bool AFF, int RT>
+hipError_t launch_rt(const uint32_t *codes, const uint16_t *scales, const uint16_t *biases, const uint16_t *x,
+                     float *y, int M, int N, int K, hipStream_t stream)
 {
     const int mb = M < 16 ? M : 16;                 // rows of x per workgroup
-    const int nw = sm_waves<TERN>(RT, mb, K);
+    const int nw = sm_waves<TERN, AFF>(RT, mb, K);
     if (nw < 1) return hipErrorInvalidValue;
-    const size_t lds = (size_t)nw * sm_wave_bytes<TERN>(RT, mb) + (size_t)nw * mb * 16 * RT * 4;
+    const size_t lds = (size_t)nw * sm_wave_bytes<TERN, AFF>(RT, mb) + (size_t)nw * mb * 16 * RT * 4;
     const int64_t blocks = ((int64_t)N + 16 * RT - 1) / (16 * RT);
     const int64_t yblocks = ((int64_t)M + 15) / 16;
     if (blocks > INT_MAX || yblocks > 65535) return hipErrorInvalidValue;
-    const void *fn = (K / 128) % 2 == 0 ? reinterpret_cast<const void *>(&gemv_mfma_kernel<TERN, RT, true>)
-                                        : reinterpret_cast<const void *>(&gemv_mfma_kernel<TERN, RT, false>);
+    const void *fn = (K / 128) % 2 == 0 ? reinterpret_cast<const void *>(&gemv_mfma_kernel<TERN, AFF, RT, true>)
+                                        : reinterpret_cast<const void *>(&gemv_mfma_kernel<TERN, AFF, RT, false>);
     static const bool attr =
-        hipFuncSetAttribute(reinterpret_cast<const void *>(&gemv_mfma_kernel<TERN, RT, true>),
+        hipFuncSetAttribute(reinterpret_cast<const void *>(&gemv_mfma_kernel<TERN, AFF, RT, true>),
                             hipFuncAttributeMaxDynamicSharedMemorySize, kLdsPerCu) == hipSuccess &&
-        hipFuncSetAttribute(reinterpret_cast<const void *>(&gemv_mfma_kernel<TERN, RT, false>),
+        hipFuncSetAttribute(reinterpret_cast<const void *>(&gemv_mfma_kernel<TERN, AFF, RT, false>),
                             hipFuncAttributeMaxDynamicSharedMemorySize, kLdsPerCu) == hipSuccess;
     if (!attr) return hipErrorInvalidValue;
-    void *args[] = {&codes, &scales, &x, &y, &M, &N, &K};
+    void *args[] = {&codes, &scales, &biases, &x, &y, &M, &N, &K};
     return launch_kernel(fn, dim3((unsigned)blocks, (unsigned)yblocks), dim3(64 * nw), args, lds, stream);
 }
 
-template <bool TERN>
-hipError_t launch_sm(const uint32_t *codes, const uint16_t *scales, const uint16_t *x, float *y,
-                     int M, int N, int K, hipStream_t stream)
+template <bool TERN, bool AFF = false>
+hipError_t launch_sm(const uint32_t *codes, const uint16_t *scales, const uint16_t *biases, const uint16_t *x,
+                     float *y, int M, int N, int K, hipStream_t stream)
 {
     // Every wave loads its slice at once and then computes, so a second round of workgroups
     // on a CU pays the load latency again: take the row tile (16, 32 or 64 rows) whose grid
@@ -303,9 +360,11 @@ hipError_t launch_sm(const uint32_t *codes, const uint16_t *scales, const uint16
     constexpr int kCus = 256, kWavesPerCu = 32;
     const int mb = M < 16 ? M : 16;
     auto rounds = [&](int rt) -> int64_t {
-        const int nw = sm_waves<TERN>(rt, mb, K);
+        // the affine kernel keeps scales and biases in registers: no four-tile variant
+        if (AFF && rt == 4) return INT64_MAX;
+        const int nw = sm_waves<TERN, AFF>(rt, mb, K);
         if (nw < 1) return INT64_MAX;
-        const int64_t lds = (int64_t)nw * sm_wave_bytes<TERN>(rt, mb) + (int64_t)nw * mb * 16 * rt * 4;
+        const int64_t lds = (int64_t)nw * sm_wave_bytes<TERN, AFF>(rt, mb) + (int64_t)nw * mb * 16 * rt * 4;
         int64_t per_cu = kLdsPerCu / lds;
         if (per_cu > kWavesPerCu / nw) per_cu = kWavesPerCu / nw;
         if (per_cu < 1) return INT64_MAX;
@@ -313,9 +372,10 @@ hipError_t launch_sm(const uint32_t *codes, const uint16_t *scales, const uint16
         return (blocks + per_cu * kCus - 1) / (per_cu * kCus);
     };
     const int64_t r1 = rounds(1), r2 = rounds(2), r4 = rounds(4);
-    if (r1 <= r2 && r1 <= r4) return launch_rt<TERN, 1>(codes, scales, x, y, M, N, K, stream);
-    if (r2 <= r4) return launch_rt<TERN, 2>(codes, scales, x, y, M, N, K, stream);
-    return launch_rt<TERN, 4>(codes, scales, x, y, M, N, K, stream);
+    if (r1 <= r2 && r1 <= r4) return launch_rt<TERN, AFF, 1>(codes, scales, biases, x, y, M, N, K, stream);
+    if (r2 <= r4) return launch_rt<TERN, AFF, 2>(codes, scales, biases, x, y, M, N, K, stream);
+    if constexpr (AFF) return hipErrorInvalidValue;
+    else return launch_rt<TERN, AFF, 4>(codes, scales, biases, x, y, M, N, K, stream);
 }
 
 }  // namespace
@@ -325,8 +385,16 @@ hipError_t launch_gemv_mfma(bool ternary, const uint32_t *codes, const uint16_t 
                             float *y, int M, int N, int K, hipStream_t stream)
 {
     if (M < 1) return hipErrorInvalidValue;
-    return ternary ? launch_sm<true>(codes, scales, x, y, M, N, K, stream)
-                   : launch_sm<false>(codes, scales, x, y, M, N, K, stream);
+    return ternary ? launch_sm<true>(codes, scales, nullptr, x, y, M, N, K, stream)
+                   : launch_sm<false>(codes, scales, nullptr, x, y, M, N, K, stream);
+}
+
+// Affine 1-bit weights (MLX's scale-and-bias form of the binary words), any M >= 1.
+hipError_t launch_q1a_matmul(const uint32_t *wbits, const uint16_t *scales, const uint16_t *biases,
+                             const uint16_t *x, float *y, int M, int N, int K, hipStream_t stream)
+{
+    if (M < 1) return hipErrorInvalidValue;
+    return launch_sm<false, true>(wbits, scales, biases, x, y, M, N, K, stream);
 }
 
 // Ternary weights ("Ternary Bonsai 27B" article, ternary format: {-1, 0, +1} times the FP16
@@ -335,7 +403,7 @@ hipError_t launch_q2t_gemv(const uint32_t *wcodes, const uint16_t *scales, const
                            int M, int N, int K, hipStream_t stream)
 {
     if (M < 1 || M > 8) return hipErrorInvalidValue;
-    return launch_sm<true>(wcodes, scales, x, y, M, N, K, stream);
+    return launch_sm<true>(wcodes, scales, nullptr, x, y, M, N, K, stream);
 }
 
 }  // namespace bonsai

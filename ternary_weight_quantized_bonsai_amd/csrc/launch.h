@@ -18,6 +18,9 @@ hipError_t launch_q2t_gemm(const uint32_t *wcodes, const uint16_t *scales, const
 // entry points use it for ternary M = 1..8 and binary M = 2..8, the GEMMs for small M).
 hipError_t launch_gemv_mfma(bool ternary, const uint32_t *codes, const uint16_t *scales, const uint16_t *x,
                             float *y, int M, int N, int K, hipStream_t stream);
+// Affine 1-bit weights (binary words with a binary16 scale and bias per group), any M >= 1.
+hipError_t launch_q1a_matmul(const uint32_t *wbits, const uint16_t *scales, const uint16_t *biases,
+                             const uint16_t *x, float *y, int M, int N, int K, hipStream_t stream);
 hipError_t launch_fill_zero(float *y, int64_t count, hipStream_t stream);
 hipError_t launch_q1_embed(const uint32_t *wbits, const uint16_t *scales, const int64_t *ids, uint16_t *out,
                            int64_t n_ids, int64_t V, int K, hipStream_t stream);

@@ -148,6 +148,60 @@ def test_gemm_accepts_large_m_in_validation_only(fn):
     assert f(FAKE, FAKE, FAKE, FAKE, (1 << 30) + 1, 64, 128, None) == bonsai.ERR_SHAPE
 
 
+def test_affine_matmul_validation():
+    f = bonsai.raw().bonsai_q1a_matmul
+    p = FAKE
+    assert f(p, p, None, p, p, 1, 64, 128, None) == bonsai.ERR_NULL
+    assert f(p, p, p + 2, p, p, 1, 64, 128, None) == bonsai.ERR_ALIGN
+    assert f(None, p, p, p, p, 1, 64, 128, None) == bonsai.ERR_NULL
+    assert f(p, p, p, p, None, 1, 64, 128, None) == bonsai.ERR_NULL
+    assert f(p, p, p, p, p, 1, 64, 100, None) == bonsai.ERR_SHAPE
+    assert f(p, p, p, p, p, -1, 64, 128, None) == bonsai.ERR_SHAPE
+    assert f(p, p, p, p + 8, p, 1, 64, 128, None) == bonsai.ERR_ALIGN
+    assert f(None, None, None, None, None, 0, 64, 128, None) == bonsai.OK
+    assert f(None, None, None, None, None, 3, 0, 128, None) == bonsai.OK
+
+
+def test_affine_conversion_every_f16_pattern():
+    """to_affine gives (2 s, -s) exactly for every binary16 s whose double is finite, rejects
+    the rest, and from_affine takes each pair back to the same bits."""
+    s = np.arange(1 << 16, dtype=np.uint16)
+    sv = s.view(np.float16).astype(np.float64)
+    with np.errstate(over="ignore", invalid="ignore"):
+        ok = np.isfinite(sv) & np.isfinite((2.0 * sv).astype(np.float16).astype(np.float64))
+    good = s[ok]
+    a, b = bonsai.q1_to_affine(good)
+    gv = good.view(np.float16).astype(np.float64)
+    assert np.array_equal(a.view(np.float16).astype(np.float64), 2.0 * gv)       # exact doubling
+    assert np.array_equal(np.signbit(a.view(np.float16)), np.signbit(good.view(np.float16)))
+    assert np.array_equal(b, good ^ np.uint16(0x8000))
+    assert np.array_equal(bonsai.q1_from_affine(a, b), good)
+    for bad in s[~ok]:                    # |s| >= 32768, inf, NaN
+        with pytest.raises(bonsai.BonsaiError):
+            bonsai.q1_to_affine(np.array([bad], np.uint16))
+
+
+def test_affine_from_rejects_non_binary_pairs():
+    s = np.array([0x3C00, 0x2E66, 0x0001, 0x8400], np.uint16)
+    a, b = bonsai.q1_to_affine(s)
+    for i in range(s.size):
+        for bad_a, bad_b in ((a[i] ^ np.uint16(1), b[i]), (a[i], b[i] ^ np.uint16(1)), (a[i], b[i] ^ np.uint16(0x8000))):
+            aa, bb = a.copy(), b.copy()
+            aa[i], bb[i] = bad_a, bad_b
+            with pytest.raises(bonsai.BonsaiError):
+                bonsai.q1_from_affine(aa, bb)
+    assert bonsai.q1_from_affine(a[:0], b[:0]).size == 0
+
+
+def test_affine_conversion_gives_the_binary_weights(orc):
+    """The converted pairs dequantize (oracle, affine form) to the native binary weights."""
+    import synth
+    N, K = 7, 640
+    w, s, _ = synth.make_q1(1, N, K, 3, "abi/affine")
+    a, b = bonsai.q1_to_affine(s)
+    assert np.array_equal(orc.q1a_dequant(w, a, b, K), orc.q1_dequant(w, s, K))
+
+
 def test_embed_validation():
     f = bonsai.raw().bonsai_q1_embed
     p = FAKE

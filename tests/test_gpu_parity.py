@@ -266,6 +266,96 @@ def test_gemm_matches_gemv_on_the_same_rows(orc):
     assert_close(yg, yv.astype(np.float64), 2 * a, "gemm vs gemv")
 
 
+# ---- affine 1-bit (MLX's scale-and-bias form) ------------------------------------------------
+def _affine(w, a, b, x):
+    import ternary_weight_quantized_bonsai_amd as bonsai
+    torch, _ = torch_dev()
+    note(f"q1a_matmul M={x.shape[0]} N={w.shape[0]} K={x.shape[1]}")
+    y = bonsai.q1a_matmul(to_dev(w), to_dev(a), to_dev(b), to_dev(x))
+    torch.cuda.synchronize()
+    return y.cpu().numpy()
+
+
+def _affine_magnitude(orc, w, a, b, x, m_idx=None, n_idx=None):
+    """sum_k |a q x| + |b x|: the size of the two terms the kernel sums separately (oracle)."""
+    K = x.shape[1]
+    zero = np.zeros_like(a)
+    _, mq = orc.q1a_matmul(w, a, zero, x, K, m_idx, n_idx)
+    _, mb = orc.q1a_matmul(w, zero, b, x, K, m_idx, n_idx)
+    return mq + mb
+
+
+AFFINE_SHAPES = [(1, 256, 512), (1, 300, 640), (2, 1000, 1152), (8, 2000, 1024), (16, 777, 640),
+                 (17, 500, 1152), (33, 130, 384), (80, 300, 896), (1, 5, 128)]
+
+
+@pytest.mark.parametrize("M,N,K", AFFINE_SHAPES)
+def test_affine_matmul_vs_oracle(M, N, K, orc):
+    w, a, b, x = synth.make_q1a(M, N, K, 61, f"aff{N}x{K}")
+    y = _affine(w, a, b, x)
+    yref, _ = orc.q1a_matmul(w, a, b, x, K)
+    assert_close(y, yref, _affine_magnitude(orc, w, a, b, x), f"q1a M={M} N={N} K={K}")
+
+
+@pytest.mark.parametrize("M,N,K", [(1, 5120, 5120), (8, 13824, 5120)])
+def test_affine_matmul_decode_shapes_sampled(M, N, K, orc):
+    w, a, b, x = synth.make_q1a(M, N, K, 0, f"aff{N}x{K}")
+    y = _affine(w, a, b, x)
+    rng = np.random.default_rng(62)
+    n_idx = np.unique(np.concatenate([[0, N - 1], rng.integers(0, N, 300)]))
+    yref, _ = orc.q1a_matmul(w, a, b, x, K, None, n_idx)
+    assert_close(y[:, n_idx], yref, _affine_magnitude(orc, w, a, b, x, None, n_idx), "q1a sampled")
+
+
+@pytest.mark.parametrize("M,N,K", [(1, 5120, 5120), (5, 700, 896), (24, 300, 640)])
+def test_affine_bonsai_packing_matches_binary(M, N, K, orc):
+    """The binary weights carried as (2 s, -s) give the binary product (model card, 'MLX packaging')."""
+    import ternary_weight_quantized_bonsai_amd as bonsai
+    w, s, x = synth.make_q1(M, N, K, 63, f"affpk{N}x{K}")
+    a, b = bonsai.q1_to_affine(s)
+    y = _affine(w, a, b, x)
+    yref, mag = orc.q1_matmul(w, s, x, K)
+    assert_close(y, yref, 3 * mag, "q1a as binary")
+
+
+@pytest.mark.parametrize("M,N,K", [(1, 300, 640), (7, 260, 1024), (20, 129, 384)])
+def test_affine_integer_inputs_bit_exact(M, N, K, orc):
+    """Small integer x, scales and biases: every partial sum is exact in float32, so the kernel
+    must equal the exact result bit for bit."""
+    rng = np.random.default_rng(64 + M)
+    w = synth.sign_words(N, K // 32, 64, f"affint{N}x{K}")
+    f16 = lambda v: v.astype(np.float16).view(np.uint16)
+    a = f16(rng.integers(-4, 5, (N, K // 128)))
+    b = f16(rng.integers(-4, 5, (N, K // 128)))
+    x = f16(rng.integers(-8, 9, (M, K)))
+    y = _affine(w, a, b, x)
+    yref, _ = orc.q1a_matmul(w, a, b, x, K)
+    assert np.array_equal(y.astype(np.float64), yref)
+
+
+def test_affine_poison_guard_and_empty(orc):
+    """Only y[:M, :N] is written; M = 0 / N = 0 are no-ops; K = 0 writes zeros."""
+    import ternary_weight_quantized_bonsai_amd as bonsai
+    torch, dev = torch_dev()
+    M, N, K = 9, 131, 640
+    w, a, b, x = synth.make_q1a(M, N, K, 65, "affpoison")
+    buf = torch.full((M * N + 64,), float("nan"), dtype=torch.float32, device=dev)
+    wd, ad, bd, xd = to_dev(w), to_dev(a), to_dev(b), to_dev(x)
+    note(f"q1a_matmul poison M={M} N={N} K={K}")
+    st = bonsai.raw().bonsai_q1a_matmul(wd.data_ptr(), ad.data_ptr(), bd.data_ptr(), xd.data_ptr(),
+                                        buf.data_ptr(), M, N, K, torch.cuda.current_stream().cuda_stream)
+    torch.cuda.synchronize()
+    assert st == bonsai.OK
+    host = buf.cpu().numpy()
+    yref, _ = orc.q1a_matmul(w, a, b, x, K)
+    assert_close(host[:M * N].reshape(M, N), yref, _affine_magnitude(orc, w, a, b, x), "q1a poison")
+    assert np.isnan(host[M * N:]).all()
+    out = torch.full((3, 5), 7.0, dtype=torch.float32, device=dev)
+    assert bonsai.raw().bonsai_q1a_matmul(0, 0, 0, 0, out.data_ptr(), 3, 5, 0, None) == bonsai.OK
+    torch.cuda.synchronize()
+    assert (out.cpu().numpy() == 0).all()
+
+
 # ---- embedding gather ---------------------------------------------------------------------
 def _embed(w, s, ids):
     import ternary_weight_quantized_bonsai_amd as bonsai
