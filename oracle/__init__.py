@@ -87,6 +87,12 @@ class Oracle:
         lib.bo_q1a_dequant.restype = ctypes.c_int
         lib.bo_q1a_matmul.argtypes = [_u32p, _u16p, _u16p] + _MM_ARGS[2:] + [_dp]
         lib.bo_q1a_matmul.restype = ctypes.c_int
+        _u8p = ctypes.POINTER(ctypes.c_uint8)
+        lib.bo_t5_dequant.argtypes = [_u8p, _u16p, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
+                                      ctypes.c_int64, _dp]
+        lib.bo_t5_dequant.restype = ctypes.c_int
+        lib.bo_t5_matmul.argtypes = [_u8p] + _MM_ARGS[1:] + [_dp]
+        lib.bo_t5_matmul.restype = ctypes.c_int
         for fn in ("bo_q1_exact", "bo_q2t_exact"):
             f = getattr(lib, fn)
             f.argtypes = _MM_ARGS
@@ -98,12 +104,12 @@ class Oracle:
         return self._lib.bo_f16_to_f64(int(bits) & 0xFFFF)
 
     # -- dense dequantisation --------------------------------------------------------------
-    def _dequant(self, fn, words, scales, K, n0, n1):
-        words = np.ascontiguousarray(words, dtype=np.uint32)
+    def _dequant(self, fn, words, scales, K, n0, n1, wtype=np.uint32, wptr=_u32p):
+        words = np.ascontiguousarray(words, dtype=wtype)
         scales = np.ascontiguousarray(scales, dtype=np.uint16)
         N = words.shape[0]
         W = np.empty((n1 - n0, K), dtype=np.float64)
-        rc = getattr(self._lib, fn)(_ptr(words, _u32p), _ptr(scales, _u16p), N, K, n0, n1,
+        rc = getattr(self._lib, fn)(_ptr(words, wptr), _ptr(scales, _u16p), N, K, n0, n1,
                                     _ptr(W, _dp))
         if rc:
             raise OracleError(fn, rc)
@@ -117,6 +123,11 @@ class Oracle:
     def q2t_dequant(self, wcodes, scales, K, n0=0, n1=None):
         return self._dequant("bo_q2t_dequant", wcodes, scales, K, n0,
                              wcodes.shape[0] if n1 is None else n1)
+
+    def t5_dequant(self, codes, scales, K, n0=0, n1=None):
+        """Dense double rows of the base-3 ternary matrix (five trits per byte)."""
+        return self._dequant("bo_t5_dequant", codes, scales, K, n0,
+                             codes.shape[0] if n1 is None else n1, np.uint8, ctypes.POINTER(ctypes.c_uint8))
 
     def q1a_dequant(self, wbits, scales, biases, K, n0=0, n1=None):
         """Dense double rows of the affine 1-bit matrix: w = scale * bit + bias per group."""
@@ -133,8 +144,9 @@ class Oracle:
         return W
 
     # -- matmul ------------------------------------------------------------------------------
-    def _mm(self, fn, words, scales, x, K, m_idx, n_idx, with_abs, biases=None):
-        words = np.ascontiguousarray(words, dtype=np.uint32)
+    def _mm(self, fn, words, scales, x, K, m_idx, n_idx, with_abs, biases=None, wtype=np.uint32,
+            wptr=_u32p):
+        words = np.ascontiguousarray(words, dtype=wtype)
         scales = np.ascontiguousarray(scales, dtype=np.uint16)
         x = np.ascontiguousarray(x, dtype=np.uint16)
         M, N = x.shape[0], words.shape[0]
@@ -143,7 +155,7 @@ class Oracle:
         mc = M if mi is None else mi.size
         nc = N if ni is None else ni.size
         y = np.empty((mc, nc), dtype=np.float64)
-        args = [_ptr(words, _u32p), _ptr(scales, _u16p), _ptr(x, _u16p), M, N, K,
+        args = [_ptr(words, wptr), _ptr(scales, _u16p), _ptr(x, _u16p), M, N, K,
                 None if mi is None else _ptr(mi, _i64p), mc,
                 None if ni is None else _ptr(ni, _i64p), nc, _ptr(y, _dp)]
         if biases is not None:
@@ -164,6 +176,11 @@ class Oracle:
 
     def q2t_matmul(self, wcodes, scales, x, K, m_idx=None, n_idx=None):
         return self._mm("bo_q2t_matmul", wcodes, scales, x, K, m_idx, n_idx, True)
+
+    def t5_matmul(self, codes, scales, x, K, m_idx=None, n_idx=None):
+        """(y, a) for base-3 ternary weights (five trits per byte)."""
+        return self._mm("bo_t5_matmul", codes, scales, x, K, m_idx, n_idx, True, wtype=np.uint8,
+                        wptr=ctypes.POINTER(ctypes.c_uint8))
 
     def q1a_matmul(self, wbits, scales, biases, x, K, m_idx=None, n_idx=None):
         """(y, a) for affine 1-bit weights (MLX's scale-and-bias form, model card 'MLX packaging')."""
@@ -199,10 +216,12 @@ def tolerance(a: np.ndarray) -> np.ndarray:
 # Bits per weight of each storage form, from the pages: one sign bit plus a 16-bit
 # scale shared by 128 weights (model card, "Weight representation" and "Memory
 # requirement"); 2-bit ternary codes plus the same scale (ternary article, limitations);
-# MLX's scale-plus-bias packing of the binary weights (model card, "MLX packaging").
+# MLX's scale-plus-bias packing of the binary weights (model card, "MLX packaging");
+# this library's base-3 ternary layout, five trits per byte plus the same scale (its own
+# layout: the ternary article gives only the log2(3) + 16/128 bound it approaches).
 def bits_per_weight(form: str) -> float:
     return {"q1": 1 + 16 / 128, "q2t": 2 + 16 / 128, "mlx_affine_1bit": 1 + 32 / 128,
-            "fp16": 16.0}[form]
+            "t5": 8 / 5 + 16 / 128, "fp16": 16.0}[form]
 
 
 def packed_bytes(form: str, N: int, K: int) -> int:
@@ -213,4 +232,6 @@ def packed_bytes(form: str, N: int, K: int) -> int:
         return N * K // 8 + 2 * N * (K // 128)
     if form == "q2t":
         return N * K // 4 + 2 * N * (K // 128)
+    if form == "t5":
+        return N * 32 * ((K + 159) // 160) + 2 * N * (K // 128)
     raise ValueError(form)

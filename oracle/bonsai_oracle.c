@@ -23,10 +23,19 @@
  * held today in 2-bit storage.  The pages do not give the 2-bit code; the code
  * used here is 00 -> 0, 01 -> +1, 11 -> -1, with 10 reserved (rejected).
  *
+ * Base-3 ternary weights (the same {-1, 0, +1} x scale, at the native density the ternary
+ * article's limitations section anticipates: log2(3) bits per weight in theory).  The pages give
+ * no layout; this library's is five trits per byte, described under "Storage" below.
+ *
  * Storage (the pages are silent on bit order; this is the chosen layout):
  *   sign words  uint32 [N][K/32]: weight (n,k) is bit (k mod 32) of word k/32 of row n.
  *   trit words  uint32 [N][K/16]: weight (n,k) is the 2-bit field whose low bit is
  *               bit 2*(k mod 16) of word k/16 of row n.
+ *   base-3      uint8 [N][32 * ceil(K/160)]: a row is a run of 32-byte superblocks of 160
+ *               weights.  Byte c (0..31) of superblock b holds the five weights
+ *               k = 160 b + c + 32 i, i = 0..4, as the base-3 number sum_i d_i 3^i with digit
+ *               d = w mod 3 (0 -> 0, 1 -> +1, 2 -> -1).  Bytes 243..255 are reserved (rejected);
+ *               weights past K are zero digits.
  *   scales      IEEE binary16 bit patterns [N][K/128]; weight (n,k) uses scale k/128.
  *   x           IEEE binary16 bit patterns [M][K].
  *
@@ -100,6 +109,22 @@ static int q2t_trit(const uint32_t *wcodes, int64_t K, int64_t n, int64_t k, int
     }
 }
 
+/* Base-3 trit of weight (n,k): digit i of byte c of superblock b, where k = 160 b + 32 i + c. */
+static int t5_trit(const uint8_t *codes, int64_t K, int64_t n, int64_t k, int *t)
+{
+    const int64_t row_bytes = 32 * ((K + 159) / 160);
+    const int64_t b = k / 160, i = (k % 160) / 32, c = k % 32;
+    const unsigned v = codes[n * row_bytes + 32 * b + c];
+    if (v >= 243) return BO_ERR_CODE;
+    unsigned place = 1;
+    for (int64_t j = 0; j < i; ++j) place *= 3;
+    switch ((v / place) % 3) {
+    case 0: *t = 0; return 0;
+    case 1: *t = 1; return 0;
+    default: *t = -1; return 0;
+    }
+}
+
 /* Dense dequantisation of rows [n0, n1) into W (row-major, K doubles per row). */
 int bo_q1_dequant(const uint32_t *wbits, const uint16_t *scales, int64_t N, int64_t K,
                   int64_t n0, int64_t n1, double *W)
@@ -134,11 +159,24 @@ int bo_q2t_dequant(const uint32_t *wcodes, const uint16_t *scales, int64_t N, in
     return BO_OK;
 }
 
+int bo_t5_dequant(const uint8_t *codes, const uint16_t *scales, int64_t N, int64_t K,
+                  int64_t n0, int64_t n1, double *W)
+{
+    if (!shape_ok(0, N, K) || n0 < 0 || n1 > N || n0 > n1) return BO_ERR_SHAPE;
+    for (int64_t n = n0; n < n1; ++n)
+        for (int64_t k = 0; k < K; ++k) {
+            int t;
+            if (t5_trit(codes, K, n, k, &t)) return BO_ERR_CODE;
+            W[(n - n0) * K + k] = t * bo_f16_to_f64(scales[n * (K / 128) + k / 128]);
+        }
+    return BO_OK;
+}
+
 /* The selected (m, n) entries of y = x W^T and of a = |x| |W|^T.
  * m_idx / n_idx list the rows of x and of W to evaluate (NULL: all of them, in order);
  * y and a are [m_cnt][n_cnt] row-major. */
-/* form: 0 binary, 1 ternary, 2 affine 1-bit (biases used only there) */
-static int matmul(int form, const uint32_t *words, const uint16_t *scales, const uint16_t *biases,
+/* form: 0 binary, 1 ternary, 2 affine 1-bit (biases used only there), 3 base-3 ternary */
+static int matmul(int form, const void *words, const uint16_t *scales, const uint16_t *biases,
                   const uint16_t *x, int64_t M, int64_t N, int64_t K,
                   const int64_t *m_idx, int64_t m_cnt, const int64_t *n_idx, int64_t n_cnt,
                   double *y, double *a)
@@ -158,6 +196,7 @@ static int matmul(int form, const uint32_t *words, const uint16_t *scales, const
         const int64_t n = n_idx ? n_idx[j] : j;
         rc = form == 1 ? bo_q2t_dequant(words, scales, N, K, n, n + 1, wrow)
            : form == 2 ? bo_q1a_dequant(words, scales, biases, N, K, n, n + 1, wrow)
+           : form == 3 ? bo_t5_dequant(words, scales, N, K, n, n + 1, wrow)
                        : bo_q1_dequant(words, scales, N, K, n, n + 1, wrow);
         for (int64_t i = 0; i < m_cnt && rc == BO_OK; ++i) {
             const int64_t m = m_idx ? m_idx[i] : i;
@@ -189,6 +228,14 @@ int bo_q1a_matmul(const uint32_t *wbits, const uint16_t *scales, const uint16_t 
                   double *y, double *a)
 {
     return matmul(2, wbits, scales, biases, x, M, N, K, m_idx, m_cnt, n_idx, n_cnt, y, a);
+}
+
+int bo_t5_matmul(const uint8_t *codes, const uint16_t *scales, const uint16_t *x,
+                 int64_t M, int64_t N, int64_t K,
+                 const int64_t *m_idx, int64_t m_cnt, const int64_t *n_idx, int64_t n_cnt,
+                 double *y, double *a)
+{
+    return matmul(3, codes, scales, NULL, x, M, N, K, m_idx, m_cnt, n_idx, n_cnt, y, a);
 }
 
 int bo_q2t_matmul(const uint32_t *wcodes, const uint16_t *scales, const uint16_t *x,

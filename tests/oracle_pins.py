@@ -208,6 +208,74 @@ def pin_affine_forms(o):
             assert y[m, n] == want, (m, n)
 
 
+def _t5_pack(trits: np.ndarray) -> np.ndarray:
+    """Base-3 layout from its definition: byte c of superblock b is sum_i (w mod 3) 3^i over
+    the weights k = 160 b + c + 32 i (zero past K)."""
+    N, K = trits.shape
+    SB = -(-K // 160)
+    out = np.zeros((N, 32 * SB), dtype=np.uint8)
+    for n in range(N):
+        for b in range(SB):
+            for c in range(32):
+                v = 0
+                for i in range(5):
+                    k = 160 * b + c + 32 * i
+                    v += (int(trits[n, k]) % 3 if k < K else 0) * 3 ** i
+                out[n, 32 * b + c] = v
+    return out
+
+
+def pin_t5_forms(o):
+    """Base-3 ternary (five trits per byte).  Fixed outside the oracle by: the same trits read
+    from 2-bit words through the byte view, packed from the layout's definition, must give
+    exactly the 2-bit oracle's weights and products; one-hot digits at every byte and digit of
+    two superblocks and a ragged third; reserved bytes; the density bound of the pages."""
+    for (N, K, seed) in [(3, 640, 31), (2, 1152, 32), (4, 384, 33)]:
+        words = synth.trit_words(N, K // 16, seed, f"pin/t5/{K}")
+        trits = np.array([[_trit(words, n, k) for k in range(K)] for n in range(N)])
+        codes = _t5_pack(trits)
+        s = synth.scales_f16(N, K // 128, seed, f"pin/t5/{K}")
+        assert np.array_equal(o.t5_dequant(codes, s, K), o.q2t_dequant(words, s, K)), K
+        x = synth.activations_f16(2, K, seed, f"pin/t5/{K}")
+        yt, at = o.t5_matmul(codes, s, x, K)
+        yq, aq = o.q2t_matmul(words, s, x, K)
+        assert np.array_equal(yt, yq) and np.array_equal(at, aq), K
+
+    # one-hot digits: byte c of superblock b = 3^i (digit 1, +1) or 2 3^i (digit 2, -1)
+    N, K = 1, 384                                  # superblocks 0, 1 whole, 2 holds k 320..383
+    s = _f16([[3.0, 5.0, 7.0]])
+    sv = _lib_f16(s)[0]
+    for b in range(3):
+        for c in range(32):
+            for i in range(5):
+                k = 160 * b + c + 32 * i
+                for digit, sign in ((1, 1.0), (2, -1.0)):
+                    codes = np.zeros((N, 96), dtype=np.uint8)
+                    codes[0, 32 * b + c] = digit * 3 ** i
+                    want = np.zeros((N, K))
+                    if k < K:
+                        want[0, k] = sign * sv[k // 128]
+                    assert np.array_equal(o.t5_dequant(codes, s, K), want), (b, c, i, digit)
+
+    # reserved bytes 243..255 are refused; every byte below them decodes
+    for v in (243, 250, 255):
+        codes = np.zeros((1, 32), dtype=np.uint8)
+        codes[0, 5] = v
+        try:
+            o.t5_dequant(codes, _f16([[1.0]]), 128)
+        except oracle_mod.OracleError as e:
+            assert e.rc == oracle_mod.ERR_CODE
+        else:
+            raise AssertionError(f"reserved byte {v} accepted")
+    o.t5_dequant(np.full((1, 32), 242, np.uint8), _f16([[1.0]]), 128)
+
+    # density: at or above the pages' log2(3) + 16/128 bound, within 1 % of it
+    ideal = math.log2(3) + 16 / 128
+    bpw = oracle_mod.bits_per_weight("t5")
+    assert ideal <= bpw <= 1.01 * ideal
+    assert oracle_mod.packed_bytes("t5", 5120, 5120) * 8 / (5120 * 5120) == bpw
+
+
 def pin_metamorphic(o):
     """y(-x) = -y(x), y(2s) = 2 y(s) and y(~signs) = -y(signs), all exactly."""
     M, N, K = 3, 9, 768
@@ -333,7 +401,7 @@ def pin_storage_figures(o):
 
 ALL_PINS = [
     pin_f16_decoder, pin_all_ones_all_zero, pin_popcount, pin_onehot, pin_byte_patterns,
-    pin_exact_vs_double, pin_mlx_identity, pin_affine_forms, pin_metamorphic, pin_ternary_zero_and_mask,
+    pin_exact_vs_double, pin_mlx_identity, pin_affine_forms, pin_t5_forms, pin_metamorphic, pin_ternary_zero_and_mask,
     pin_ternary_counts_and_onehot, pin_reserved_and_shapes, pin_golden_hand_cases,
     pin_storage_figures,
 ]

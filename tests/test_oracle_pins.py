@@ -44,6 +44,15 @@ MUTANTS = {
                             "const double q = (double)(((~word) >> (k % 32)) & 1u);"),
     "affine_group_of_64": ("const int64_t g = n * (K / 128) + k / 128;",
                            "const int64_t g = n * (K / 128) + (k / 64) % (K / 128);"),
+    "t5_digit_order_reversed": ("for (int64_t j = 0; j < i; ++j) place *= 3;",
+                                "for (int64_t j = 0; j < 4 - i; ++j) place *= 3;"),
+    "t5_five_consecutive_k": ("const int64_t b = k / 160, i = (k % 160) / 32, c = k % 32;",
+                              "const int64_t b = k / 160, i = (k % 160) % 5, c = (k % 160) / 5;"),
+    "t5_digit_two_as_plus": ("    case 1: *t = 1; return 0;\n    default: *t = -1; return 0;",
+                             "    case 1: *t = -1; return 0;\n    default: *t = 1; return 0;"),
+    "t5_superblock_stride": ("codes[n * row_bytes + 32 * b + c]", "codes[n * row_bytes + 30 * b + c]"),
+    "t5_row_bytes_floor": ("32 * ((K + 159) / 160)", "32 * (K / 160)"),
+    "t5_reserved_accepted": ("if (v >= 243) return BO_ERR_CODE;", "if (v > 255) return BO_ERR_CODE;"),
     "f16_bias_off_by_one": ("ldexp((double)(1024 + f), e - 25)", "ldexp((double)(1024 + f), e - 24)"),
     "f16_subnormal_wrong": ("ldexp((double)f, -24)", "ldexp((double)f, -25)"),
     "f16_implicit_bit_dropped": ("ldexp((double)(1024 + f), e - 25)", "ldexp((double)f, e - 25)"),
