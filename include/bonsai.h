@@ -57,7 +57,8 @@ typedef enum {
     BONSAI_ERR_ALIGN = 3,   /* a device pointer is not 16-byte aligned                       */
     BONSAI_ERR_VALUE = 4,   /* pack input outside {-1,+1} (binary) or {-1,0,+1} (ternary);
                                an affine conversion whose result is not exact (see below)    */
-    BONSAI_ERR_CODE = 5,    /* unpack met the reserved ternary field value 2                 */
+    BONSAI_ERR_CODE = 5,    /* unpack met a reserved ternary code (2-bit field value 2; base-3
+                               byte 243..255, or a nonzero weight in a base-3 row's padding)  */
     BONSAI_ERR_DEVICE = 6   /* the HIP runtime refused the launch                            */
 } bonsai_status;
 
@@ -96,6 +97,26 @@ bonsai_status bonsai_q2t_gemm(const uint32_t *wcodes, const uint16_t *scales, co
  * table is read).  n_ids == 0 or K == 0 is a no-op; otherwise as the other GPU entry points. */
 bonsai_status bonsai_q1_embed(const uint32_t *wbits, const uint16_t *scales, const int64_t *ids,
                               uint16_t *out, int64_t n_ids, int64_t V, int64_t K, void *hip_stream);
+
+/* Base-3 ternary weights ("t5"): the ternary weights at near their native density.  The ternary
+ * article's limitations section puts the information content at log2(3) ~ 1.585 bits per weight
+ * (about 1.71 with the scales) against the 2.125 of today's 2-bit storage, and gives no layout;
+ * this one is the library's own.
+ *   codes : uint8 [N][32 * ceil(K/160)], row-major: each row is a run of 32-byte superblocks of
+ *           160 weights.  Byte c (0..31) of superblock b holds W[n][k] for k = 160 b + c + 32 i,
+ *           i = 0..4, as the base-3 number sum_i d_i 3^i with d = W mod 3 (0 -> 0, 1 -> +1,
+ *           2 -> -1).  Positions k >= K hold zero weights.  Bytes 243..255 are reserved: never
+ *           produced by the packer, rejected by the unpacker, unspecified on the GPU.
+ *   scales, x, y : as for the other layouts.  1.6 bits per weight (1.725 with the scales).
+ * bonsai_t5_matmul: y[M][N] = x[M][K] * W^T for any M >= 0 (16 rows of x per pass of a small-M
+ * matrix-core kernel; built for decode).  Otherwise as the other GPU entry points.
+ * bonsai_t5_pack / bonsai_t5_unpack: host functions as the other packers, for any K >= 0;
+ * trits are int8 [N][K] in {-1, 0, +1}.  unpack also rejects (BONSAI_ERR_CODE) a nonzero
+ * weight in a row's padding past K. */
+bonsai_status bonsai_t5_matmul(const uint8_t *codes, const uint16_t *scales, const uint16_t *x,
+                               float *y, int64_t M, int64_t N, int64_t K, void *hip_stream);
+bonsai_status bonsai_t5_pack(const int8_t *trits, int64_t N, int64_t K, uint8_t *codes);
+bonsai_status bonsai_t5_unpack(const uint8_t *codes, int64_t N, int64_t K, int8_t *trits);
 
 /* Affine 1-bit matmul: y[M][N] = x[M][K] * W^T with W[n][k] = a * q + b, q the bit of W[n][k] in
  * the binary layout above and (a, b) = (mlx_scales, biases)[n][k / 128], binary16 [N][K/128]

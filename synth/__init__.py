@@ -30,7 +30,8 @@ import numpy as np
 
 __all__ = [
     "Config", "CONFIGS", "rng_for", "sign_words", "trit_words", "scales_f16",
-    "activations_f16", "biases_f16", "make_q1", "make_q2t", "make_q1a", "digest",
+    "activations_f16", "biases_f16", "trits_i8", "make_q1", "make_q2t", "make_q1a", "make_t5_trits",
+    "digest",
 ]
 
 
@@ -104,6 +105,13 @@ def biases_f16(n_rows: int, n_groups: int, seed: int, tag: str) -> np.ndarray:
     return (rng.standard_normal(size=(n_rows, n_groups)) * 0.02).astype(np.float16).view(np.uint16)
 
 
+def trits_i8(n_rows: int, k: int, seed: int, tag: str, p_zero: float = 0.4, p_plus: float = 0.3) -> np.ndarray:
+    """int8 [n_rows, k]: each entry independently 0 (p_zero), +1 (p_plus) or -1."""
+    rng = rng_for(seed, tag + "/trits8")
+    u = rng.random(size=(n_rows, k))
+    return np.where(u < 1.0 - p_zero - p_plus, -1, np.where(u < 1.0 - p_zero, 1, 0)).astype(np.int8)
+
+
 def make_q1(M: int, N: int, K: int, seed: int = 0, tag: str | None = None):
     """(sign words [N, K/32], scales [N, K/128], x [M, K]) for a binary matmul."""
     tag = tag or f"{N}x{K}"
@@ -123,6 +131,14 @@ def make_q1a(M: int, N: int, K: int, seed: int = 0, tag: str | None = None):
     tag = tag or f"a{N}x{K}"
     w, s, x = make_q1(M, N, K, seed, tag)
     return w, s, biases_f16(N, K // 128, seed, tag), x
+
+
+def make_t5_trits(M: int, N: int, K: int, seed: int = 0, tag: str | None = None):
+    """(trits int8 [N, K], scales [N, K/128], x [M, K]) for a ternary matmul in any layout; the
+    caller packs the trits (the packers hold the layouts, this module holds none)."""
+    tag = tag or f"t5{N}x{K}"
+    return (trits_i8(N, K, seed, tag), scales_f16(N, K // 128, seed, tag),
+            activations_f16(M, K, seed, f"{tag}/M{M}"))
 
 
 def digest(buf: np.ndarray) -> str:

@@ -39,6 +39,12 @@ for _name in ("bonsai_q1_pack", "bonsai_q1_unpack", "bonsai_q2t_pack", "bonsai_q
     _f = getattr(_lib, _name)
     _f.argtypes = [_vp, _c_i64, _c_i64, _vp]
     _f.restype = ctypes.c_int
+_lib.bonsai_t5_matmul.argtypes = [_vp, _vp, _vp, _vp, _c_i64, _c_i64, _c_i64, _vp]
+_lib.bonsai_t5_matmul.restype = ctypes.c_int
+for _name in ("bonsai_t5_pack", "bonsai_t5_unpack"):
+    _f = getattr(_lib, _name)
+    _f.argtypes = [_vp, _c_i64, _c_i64, _vp]
+    _f.restype = ctypes.c_int
 _lib.bonsai_q1a_matmul.argtypes = [_vp, _vp, _vp, _vp, _vp, _c_i64, _c_i64, _c_i64, _vp]
 _lib.bonsai_q1a_matmul.restype = ctypes.c_int
 _lib.bonsai_q1_to_affine.argtypes = [_vp, _c_i64, _vp, _vp]
@@ -137,6 +143,38 @@ def q2t_gemm(wcodes, scales, x, out=None):
     return _call("bonsai_q2t_gemm", wcodes, scales, x, out, 16)
 
 
+def t5_row_bytes(K: int) -> int:
+    """Bytes per row of the base-3 ternary layout: 32-byte superblocks of 160 weights."""
+    return 32 * ((K + 159) // 160)
+
+
+def t5_matmul(codes, scales, x, out=None):
+    """y[M, N] = x[M, K] W^T for base-3 ternary weights (five trits per byte; bonsai_t5_matmul),
+    any M.  codes: uint8 [N, 32 ceil(K/160)]."""
+    import torch
+
+    if codes.dtype not in (torch.uint8, torch.int8) or codes.dim() != 2:
+        raise TypeError("codes must be a 2-D uint8 tensor")
+    if scales.dtype not in (torch.float16, torch.int16, torch.uint16) or x.dtype not in (torch.float16, torch.int16, torch.uint16):
+        raise TypeError("scales and x must be binary16 tensors")
+    for name, t in (("codes", codes), ("scales", scales), ("x", x)):
+        if not t.is_cuda or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous device tensor")
+    M, K = x.shape
+    N = codes.shape[0]
+    if codes.shape[1] != t5_row_bytes(K) or tuple(scales.shape) != (N, K // 128):
+        raise ValueError(f"inconsistent shapes codes {tuple(codes.shape)}, scales {tuple(scales.shape)}, "
+                         f"x {tuple(x.shape)}")
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.float32, device=x.device)
+    elif out.dtype != torch.float32 or tuple(out.shape) != (M, N) or not out.is_contiguous():
+        raise ValueError("out must be a contiguous float32 [M, N] tensor")
+    stream = torch.cuda.current_stream(x.device).cuda_stream
+    _check("bonsai_t5_matmul", _lib.bonsai_t5_matmul(codes.data_ptr(), scales.data_ptr(), x.data_ptr(),
+                                                     out.data_ptr(), M, N, K, stream))
+    return out
+
+
 def q1a_matmul(wbits, mlx_scales, biases, x, out=None):
     """y[M, N] = x[M, K] W^T for affine 1-bit weights W = a q + b per group of 128 (MLX's 1-bit
     form of the binary words; bonsai_q1a_matmul), any M."""
@@ -203,6 +241,25 @@ def q1_from_affine(mlx_scales: np.ndarray, biases: np.ndarray) -> np.ndarray:
     s = np.empty_like(a)
     _check("bonsai_q1_from_affine", _lib.bonsai_q1_from_affine(a.ctypes.data, b.ctypes.data, a.size, s.ctypes.data))
     return s
+
+
+def t5_pack(trits: np.ndarray) -> np.ndarray:
+    """int8 trits [N, K] in {-1, 0, +1} -> base-3 bytes [N, 32 ceil(K/160)] (bonsai_t5_pack)."""
+    t = _host(trits, np.int8)
+    N, K = t.shape
+    out = np.zeros((N, t5_row_bytes(K)), dtype=np.uint8)
+    _check("bonsai_t5_pack", _lib.bonsai_t5_pack(t.ctypes.data, N, K, out.ctypes.data))
+    return out
+
+
+def t5_unpack(codes: np.ndarray, K: int) -> np.ndarray:
+    c = _host(codes, np.uint8)
+    N = c.shape[0]
+    if c.shape[1] != t5_row_bytes(K):
+        raise ValueError("codes must be [N, 32 ceil(K/160)]")
+    out = np.empty((N, K), dtype=np.int8)
+    _check("bonsai_t5_unpack", _lib.bonsai_t5_unpack(c.ctypes.data, N, K, out.ctypes.data))
+    return out
 
 
 def q1_pack(signs: np.ndarray) -> np.ndarray:

@@ -125,6 +125,59 @@ bonsai_status bonsai_q1a_matmul(const uint32_t *wbits, const uint16_t *scales, c
     });
 }
 
+bonsai_status bonsai_t5_matmul(const uint8_t *codes, const uint16_t *scales, const uint16_t *x,
+                               float *y, int64_t M, int64_t N, int64_t K, void *hip_stream)
+{
+    return run(codes, scales, x, y, M, N, K, -1, hip_stream,
+               [&](int m, int n, int k, hipStream_t st) { return launch_t5_matmul(codes, scales, x, y, m, n, k, st); });
+}
+
+bonsai_status bonsai_t5_pack(const int8_t *trits, int64_t N, int64_t K, uint8_t *codes)
+{
+    if (N < 0 || K < 0) return BONSAI_ERR_SHAPE;
+    if (N == 0 || K == 0) return BONSAI_OK;
+    if (!trits || !codes) return BONSAI_ERR_NULL;
+    const int64_t sb = (K + 159) / 160;
+    for (int64_t n = 0; n < N; ++n)
+        for (int64_t b = 0; b < sb; ++b)
+            for (int c = 0; c < 32; ++c) {
+                unsigned v = 0, place = 1;
+                for (int i = 0; i < 5; ++i, place *= 3) {
+                    const int64_t k = 160 * b + c + 32 * i;
+                    if (k >= K) continue;
+                    const int8_t t = trits[n * K + k];
+                    if (t < -1 || t > 1) return BONSAI_ERR_VALUE;
+                    v += (unsigned)(t < 0 ? 2 : t) * place;
+                }
+                codes[n * 32 * sb + 32 * b + c] = (uint8_t)v;
+            }
+    return BONSAI_OK;
+}
+
+bonsai_status bonsai_t5_unpack(const uint8_t *codes, int64_t N, int64_t K, int8_t *trits)
+{
+    if (N < 0 || K < 0) return BONSAI_ERR_SHAPE;
+    if (N == 0 || K == 0) return BONSAI_OK;
+    if (!trits || !codes) return BONSAI_ERR_NULL;
+    const int64_t sb = (K + 159) / 160;
+    for (int64_t n = 0; n < N; ++n)
+        for (int64_t b = 0; b < sb; ++b)
+            for (int c = 0; c < 32; ++c) {
+                unsigned v = codes[n * 32 * sb + 32 * b + c];
+                if (v >= 243) return BONSAI_ERR_CODE;
+                for (int i = 0; i < 5; ++i, v /= 3) {
+                    const int64_t k = 160 * b + c + 32 * i;
+                    const int d = (int)(v % 3);
+                    if (k >= K) {
+                        if (d != 0) return BONSAI_ERR_CODE;      // padding must hold zero weights
+                        continue;
+                    }
+                    trits[n * K + k] = (int8_t)(d == 2 ? -1 : d);
+                }
+            }
+    return BONSAI_OK;
+}
+
 bonsai_status bonsai_q1_to_affine(const uint16_t *scales, int64_t n_groups, uint16_t *mlx_scales,
                                   uint16_t *mlx_biases)
 {
@@ -250,7 +303,7 @@ const char *bonsai_status_str(bonsai_status s)
     case BONSAI_ERR_SHAPE: return "M, N or K out of range, or K not a multiple of 128";
     case BONSAI_ERR_ALIGN: return "a device pointer is not 16-byte aligned";
     case BONSAI_ERR_VALUE: return "input outside the weight alphabet, or not an exact binary-weight scale/bias pair";
-    case BONSAI_ERR_CODE: return "reserved ternary code 0b10";
+    case BONSAI_ERR_CODE: return "reserved ternary code (2-bit field 0b10, base-3 byte above 242 or nonzero padding)";
     case BONSAI_ERR_DEVICE: return "HIP launch failed";
     }
     return "unknown status";

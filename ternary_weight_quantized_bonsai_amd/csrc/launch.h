@@ -21,6 +21,9 @@ hipError_t launch_gemv_mfma(bool ternary, const uint32_t *codes, const uint16_t 
 // Affine 1-bit weights (binary words with a binary16 scale and bias per group), any M >= 1.
 hipError_t launch_q1a_matmul(const uint32_t *wbits, const uint16_t *scales, const uint16_t *biases,
                              const uint16_t *x, float *y, int M, int N, int K, hipStream_t stream);
+// Base-3 ternary weights (five trits per byte, 32-byte superblocks of 160 k), any M >= 1.
+hipError_t launch_t5_matmul(const uint8_t *codes, const uint16_t *scales, const uint16_t *x, float *y,
+                            int M, int N, int K, hipStream_t stream);
 hipError_t launch_fill_zero(float *y, int64_t count, hipStream_t stream);
 hipError_t launch_q1_embed(const uint32_t *wbits, const uint16_t *scales, const int64_t *ids, uint16_t *out,
                            int64_t n_ids, int64_t V, int K, hipStream_t stream);

@@ -1,0 +1,268 @@
+// t5_gemv.hip -- small-M matmul on base-3 ternary weights (five trits per byte), matrix cores.
+//
+// Ternary weights ({-1, 0, +1} x the FP16 group scale; "Ternary Bonsai 27B" article, ternary
+// format) need log2(3) bits each; the article's limitations section notes that the current
+// release stores them in 2 bits and that native-density storage is still to come.  This
+// library's base-3 layout gets within 1 % of that bound: a row is a run of 32-byte superblocks
+// of 160 weights, and byte c of a superblock holds the weights k = c + 32 i (i = 0..4) as the
+// base-3 number sum_i d_i 3^i with d = w mod 3.  That is 1.6 bits per weight, 1.725 with the
+// scales, against 2.125 for the 2-bit codes.
+//
+// Why this order.  v_mfma_f32_16x16x32_f16 takes 32 k per instruction; a lane (row i = lane %
+// 16, quarter q = lane / 16) supplies 8 of them.  With digit i of byte c standing for k = c +
+// 32 i, digit i of bytes 8q .. 8q + 7 of a superblock are exactly k = 32 i + 8q .. 32 i + 8q + 7:
+// one MFMA per digit, and the lane's B operand is 8 consecutive halves of x, one 16-byte LDS
+// read with no repacking.
+//
+// Decoding.  A 256-entry table in LDS maps a byte to its five digits as 2-bit ternary codes
+// (00 -> 0, 01 -> +1, 11 -> -1) at fields 0..4 of both halves of a word.  One v_bfi_b32 joins
+// the low half of byte 2m's entry and the high half of byte 2m + 1's, so that digit i of the two
+// bytes sits at fields i and i + 8; (word << (14 - 2i)) & 0xC000C000 then gives the binary16
+// pair (2 t, 2 t') exactly (the exponent MSB is the code's low bit, the sign its high bit), and
+// the factor 2 comes off once at the end.  Bytes 243..255 are reserved: the table maps them to
+// zero weights, and results on them are unspecified.
+//
+// Work split (as the small-M kernel for the other layouts).  A workgroup owns 16 RT weight rows
+// and one block of 16 rows of x; its waves take slices of 640 k (four superblocks, five groups):
+// the slice's codes, scales and x arrive by direct global->LDS copies, each 32-k block's MFMAs
+// chain within their group of 128 k and the group scale is applied to the sums once per group;
+// the waves' partial sums meet in LDS and are added in a fixed order.
+#include <limits.h>
+
+#include "device.h"
+#include "launch.h"
+
+namespace bonsai {
+namespace {
+
+typedef float float4_v __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(1))) const void glb_void_t;
+
+constexpr int kT5SbPerSlice = 4;                     // superblocks of 160 k per slice
+constexpr int kT5GroupsPerSlice = 5;                 // groups of 128 k per slice (640 k)
+constexpr int kT5SliceBytes = 32 * kT5SbPerSlice;    // code bytes per row and slice
+constexpr int kT5XStride = 2 * 640 + 16;             // LDS bytes per row of x (640 k + pad)
+constexpr int kT5LutBytes = 256 * 4;
+constexpr int kT5MaxWaves = 16;
+constexpr int kLdsPerCu = 160 * 1024;
+
+constexpr int t5_scale_bytes(int rt) { return (5 * 16 * rt + 63) / 64 * 256; }
+
+// LDS bytes of one wave: codes, scales and the M rows of x
+constexpr int t5_wave_bytes(int rt, int m) { return 16 * rt * kT5SliceBytes + t5_scale_bytes(rt) + m * kT5XStride; }
+
+template <int RT>
+__global__ __launch_bounds__(kT5MaxWaves * 64) void t5_gemv_kernel(const uint8_t *__restrict__ codes,
+                                                                  const uint16_t *__restrict__ scales,
+                                                                  const uint16_t *__restrict__ x,
+                                                                  float *__restrict__ y, int M, int N, int K)
+{
+    constexpr int R = 16 * RT;
+    constexpr int TILE = R * kT5SliceBytes;
+    constexpr int SCB = t5_scale_bytes(RT);
+    extern __shared__ u32x4 lds[];
+    x += (size_t)16 * blockIdx.y * K;
+    y += (size_t)16 * blockIdx.y * N;
+    M = min(16, M - 16 * (int)blockIdx.y);
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int nw = blockDim.x >> 6;
+    const int G = K >> 7;
+    const int SB = (K + 159) / 160;                   // superblocks per row
+    const int units = 2 * SB;                         // 16-byte units per row
+    const int ns = (SB + kT5SbPerSlice - 1) / kT5SbPerSlice;
+    const int n0 = blockIdx.x * R;
+    const int wbytes = t5_wave_bytes(RT, M);
+    uint32_t *const lut = reinterpret_cast<uint32_t *>(lds);
+    char *const mine = reinterpret_cast<char *>(lds) + kT5LutBytes + wave * wbytes;
+    char *const tile = mine;
+    char *const sc = mine + TILE;
+    char *const xs = sc + SCB;
+    float *const red = reinterpret_cast<float *>(reinterpret_cast<char *>(lds) + kT5LutBytes + nw * wbytes);
+    const int q = lane >> 4, i16 = lane & 15;
+    const u32x4 *xg = reinterpret_cast<const u32x4 *>(x);
+    const int xunits = K >> 3;                        // 16-byte units per row of x
+
+    // the byte -> codes table: digit i of v at fields i (low half) and i + 8 (high half)
+    for (int v = threadIdx.x; v < 256; v += blockDim.x) {
+        uint32_t c = 0;
+        if (v < 243) {
+            int r = v;
+#pragma unroll
+            for (int i = 0; i < 5; ++i) {
+                const int d = r % 3;
+                r /= 3;
+                c |= (d == 0 ? 0u : d == 1 ? 1u : 3u) << (2 * i);
+            }
+        }
+        lut[v] = c | (c << 16);
+    }
+    __syncthreads();
+
+    float4_v acc[RT];
+#pragma unroll
+    for (int t = 0; t < RT; ++t) acc[t] = float4_v{0.f, 0.f, 0.f, 0.f};
+    const float4_v zero4 = float4_v{0.f, 0.f, 0.f, 0.f};
+
+    for (int s = wave; s < ns; s += nw) {
+        const int g0 = kT5GroupsPerSlice * s;
+        // codes: copy k covers rows 8 k + lane / 8; the 16-byte unit c of row r lands in slot
+        // c ^ (r & 7) of the row's 128 bytes (clamped inside the row: past-K groups count 0)
+#pragma unroll
+        for (int k = 0; k < TILE / 1024; ++k) {
+            const int r = 8 * k + (lane >> 3);
+            const int c = (lane & 7) ^ (r & 7);
+            const int unit = min(2 * kT5SbPerSlice * s + c, units - 1);
+            __builtin_amdgcn_global_load_lds(
+                (glb_void_t *)(codes + (size_t)min(n0 + r, N - 1) * (32 * SB) + 16 * unit),
+                (lds_void_t *)(tile + k * 1024), 16, 0, 0);
+        }
+        // scales: entry e = 5 r + u (row r, group u of the slice) is the low half of the dword
+        // at sc + 4 e (one 2-byte copy per entry)
+#pragma unroll
+        for (int k = 0; k < SCB / 256; ++k) {
+            const int e = 64 * k + lane, r = min(e / 5, R - 1), u = e % 5;
+            __builtin_amdgcn_global_load_lds(
+                (glb_void_t *)(scales + (size_t)min(n0 + r, N - 1) * G + min(g0 + u, G - 1)),
+                (lds_void_t *)(sc + 256 * k), 2, 0, 0);
+        }
+        // x: row m, k = 640 s .. 640 s + 639 (80 units; clamped inside K)
+        for (int m = 0; m < M; ++m) {
+            const u32x4 *row = xg + (size_t)m * xunits;
+            __builtin_amdgcn_global_load_lds((glb_void_t *)(row + min(80 * s + lane, xunits - 1)),
+                                             (lds_void_t *)(xs + m * kT5XStride), 16, 0, 0);
+            if (lane < 16)
+                __builtin_amdgcn_global_load_lds((glb_void_t *)(row + min(80 * s + 64 + lane, xunits - 1)),
+                                                 (lds_void_t *)(xs + m * kT5XStride + 1024), 16, 0, 0);
+        }
+        vm_wait<0>();                                     // this wave's slice landed
+        if (g0 + kT5GroupsPerSlice > G) {
+            // groups past K (last slice only) hold clamped copies: their scales become zero
+            for (int e = lane; e < 5 * R; e += 64)
+                if (g0 + e % 5 >= G) *reinterpret_cast<uint16_t *>(sc + 4 * e) = 0;
+        }
+
+        const char *xrow = xs + min(i16, M - 1) * kT5XStride;   // row i16 of x (M - 1 past M)
+        float4_v d[RT];
+#pragma unroll
+        for (int sb = 0; sb < kT5SbPerSlice; ++sb) {
+            // this lane's 8 bytes (8q .. 8q + 7) of superblock sb in each row tile, joined in
+            // pairs: wv[t][m] holds bytes 2m (fields 0..4) and 2m + 1 (fields 8..12)
+            uint32_t wv[RT][4];
+#pragma unroll
+            for (int t = 0; t < RT; ++t) {
+                const int r = 16 * t + i16;
+                const int slot = (2 * sb + (q >> 1)) ^ (r & 7);
+                const uint2 b8 = *reinterpret_cast<const uint2 *>(tile + kT5SliceBytes * r + 16 * slot + 8 * (q & 1));
+#pragma unroll
+                for (int m = 0; m < 4; ++m) {
+                    const uint32_t w = m < 2 ? b8.x : b8.y;
+                    const uint32_t lo = lut[(w >> (16 * (m & 1))) & 0xFFu];
+                    const uint32_t hi = lut[(w >> (16 * (m & 1) + 8)) & 0xFFu];
+                    wv[t][m] = (lo & 0x0000FFFFu) | (hi & 0xFFFF0000u);     // v_bfi_b32
+                }
+            }
+#pragma unroll
+            for (int i = 0; i < 5; ++i) {
+                const int blk = 5 * sb + i;                   // 32-k block of the slice
+                const int u = blk >> 2;                       // its group in the slice
+                const u32x4 bv = *reinterpret_cast<const u32x4 *>(xrow + 64 * blk + 16 * q);
+                const half8_t bf = __builtin_bit_cast(half8_t, bv);
+#pragma unroll
+                for (int t = 0; t < RT; ++t) {
+                    u32x4 av;
+#pragma unroll
+                    for (int m = 0; m < 4; ++m) av[m] = (wv[t][m] << (14 - 2 * i)) & 0xC000C000u;
+                    d[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8_t, av), bf,
+                                                                  (blk & 3) == 0 ? zero4 : d[t], 0, 0, 0);
+                }
+                if ((blk & 3) == 3) {
+                    // group u complete: D rows 16 t + 4 q + r take their scale
+#pragma unroll
+                    for (int t = 0; t < RT; ++t)
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) {
+                            const int row = 16 * t + 4 * q + r;
+                            const uint16_t sv = *reinterpret_cast<const uint16_t *>(sc + 4 * (5 * row + u));
+                            acc[t][r] = fmaf(f16_bits_to_f32(sv), d[t][r], acc[t][r]);
+                        }
+                }
+            }
+        }
+        lgkm_wait0();                                     // LDS reads done before the next slice's copies
+    }
+
+    // D rows 16 t + 4 q + r, column i16: the wave's partial sums into red[wave][column][row]
+    if (i16 < M) {
+#pragma unroll
+        for (int t = 0; t < RT; ++t)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) red[(wave * M + i16) * R + 16 * t + 4 * q + r] = 0.5f * acc[t][r];
+    }
+    __syncthreads();
+    for (int o = threadIdx.x; o < M * R; o += blockDim.x) {
+        const int m = o / R, row = o % R;
+        float v = 0.f;
+        for (int w = 0; w < nw; ++w) v += red[(w * M + m) * R + row];
+        if (n0 + row < N) y[(size_t)m * N + n0 + row] = v;
+    }
+}
+
+// waves of a workgroup: one per slice, at most 16 and as many as the LDS holds
+int t5_waves(int rt, int M, int K)
+{
+    const int ns = ((K + 159) / 160 + kT5SbPerSlice - 1) / kT5SbPerSlice;
+    const int per_wave = t5_wave_bytes(rt, M) + M * 16 * rt * 4;
+    int nw = ns < kT5MaxWaves ? ns : kT5MaxWaves;
+    if (nw > (kLdsPerCu - kT5LutBytes) / per_wave) nw = (kLdsPerCu - kT5LutBytes) / per_wave;
+    return nw;
+}
+
+size_t t5_lds(int rt, int mb, int nw)
+{
+    return (size_t)kT5LutBytes + (size_t)nw * t5_wave_bytes(rt, mb) + (size_t)nw * mb * 16 * rt * 4;
+}
+
+template <int RT>
+hipError_t t5_launch_rt(const uint8_t *codes, const uint16_t *scales, const uint16_t *x, float *y,
+                        int M, int N, int K, hipStream_t stream)
+{
+    const int mb = M < 16 ? M : 16;
+    const int nw = t5_waves(RT, mb, K);
+    if (nw < 1) return hipErrorInvalidValue;
+    const int64_t blocks = ((int64_t)N + 16 * RT - 1) / (16 * RT);
+    const int64_t yblocks = ((int64_t)M + 15) / 16;
+    if (blocks > INT_MAX || yblocks > 65535) return hipErrorInvalidValue;
+    static const bool attr = hipFuncSetAttribute(reinterpret_cast<const void *>(&t5_gemv_kernel<RT>),
+                                                 hipFuncAttributeMaxDynamicSharedMemorySize, kLdsPerCu) == hipSuccess;
+    if (!attr) return hipErrorInvalidValue;
+    void *args[] = {&codes, &scales, &x, &y, &M, &N, &K};
+    return launch_kernel(reinterpret_cast<const void *>(&t5_gemv_kernel<RT>), dim3((unsigned)blocks, (unsigned)yblocks),
+                         dim3(64 * nw), args, t5_lds(RT, mb, nw), stream);
+}
+
+}  // namespace
+
+// Any M >= 1 (16 rows of x per column block).  The row tile (16 or 32 rows) is the one whose
+// grid needs the fewest rounds of the chip's 256 CUs, the smaller on a tie.
+hipError_t launch_t5_matmul(const uint8_t *codes, const uint16_t *scales, const uint16_t *x, float *y,
+                            int M, int N, int K, hipStream_t stream)
+{
+    if (M < 1) return hipErrorInvalidValue;
+    constexpr int kCus = 256, kWavesPerCu = 32;
+    const int mb = M < 16 ? M : 16;
+    auto rounds = [&](int rt) -> int64_t {
+        const int nw = t5_waves(rt, mb, K);
+        if (nw < 1) return INT64_MAX;
+        int64_t per_cu = kLdsPerCu / (int64_t)t5_lds(rt, mb, nw);
+        if (per_cu > kWavesPerCu / nw) per_cu = kWavesPerCu / nw;
+        if (per_cu < 1) return INT64_MAX;
+        const int64_t blocks = (((int64_t)N + 16 * rt - 1) / (16 * rt)) * (((int64_t)M + 15) / 16);
+        return (blocks + per_cu * kCus - 1) / (per_cu * kCus);
+    };
+    if (rounds(1) <= rounds(2)) return t5_launch_rt<1>(codes, scales, x, y, M, N, K, stream);
+    return t5_launch_rt<2>(codes, scales, x, y, M, N, K, stream);
+}
+
+}  // namespace bonsai

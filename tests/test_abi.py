@@ -148,6 +148,50 @@ def test_gemm_accepts_large_m_in_validation_only(fn):
     assert f(FAKE, FAKE, FAKE, FAKE, (1 << 30) + 1, 64, 128, None) == bonsai.ERR_SHAPE
 
 
+def test_t5_pack_unpack_roundtrip_and_layout(orc):
+    """Round trip, and packed bytes dequantize (oracle, whose decoder is pinned to the layout's
+    definition) to trit x scale."""
+    import synth
+    for N, K in ((3, 640), (2, 1152), (5, 384), (1, 128), (2, 13824)):
+        t = synth.trits_i8(N, K, 7, f"abi/t5/{K}")
+        c = bonsai.t5_pack(t)
+        assert c.shape == (N, 32 * -(-K // 160))
+        assert c.max() < 243
+        assert np.array_equal(bonsai.t5_unpack(c, K), t)
+        s = synth.scales_f16(N, K // 128, 7, f"abi/t5/{K}")
+        want = t.astype(np.float64) * np.repeat(s.view(np.float16).astype(np.float64), 128, axis=1)
+        assert np.array_equal(orc.t5_dequant(c, s, K), want)
+
+
+def test_t5_unpack_rejects_reserved_and_padding():
+    c = bonsai.t5_pack(np.zeros((1, 384), np.int8))
+    bad = c.copy()
+    bad[0, 7] = 243
+    with pytest.raises(bonsai.BonsaiError) as e:
+        bonsai.t5_unpack(bad, 384)
+    assert e.value.status == bonsai.ERR_CODE
+    bad = c.copy()
+    bad[0, 64 + 3] = 3 ** 2          # superblock 2, digit 2: k = 320 + 3 + 64 = 387 >= K
+    with pytest.raises(bonsai.BonsaiError):
+        bonsai.t5_unpack(bad, 384)
+    ok = c.copy()
+    ok[0, 64 + 3] = 3 ** 1           # k = 320 + 3 + 32 = 355 < K: a real weight
+    assert bonsai.t5_unpack(ok, 384)[0, 355] == 1
+    with pytest.raises(bonsai.BonsaiError) as e:
+        bonsai.t5_pack(np.full((1, 160), 2, np.int8))
+    assert e.value.status == bonsai.ERR_VALUE
+
+
+def test_t5_matmul_validation():
+    f = bonsai.raw().bonsai_t5_matmul
+    p = FAKE
+    assert f(None, p, p, p, 1, 64, 128, None) == bonsai.ERR_NULL
+    assert f(p, p, p, None, 1, 64, 128, None) == bonsai.ERR_NULL
+    assert f(p, p, p, p, 1, 64, 100, None) == bonsai.ERR_SHAPE
+    assert f(p + 8, p, p, p, 1, 64, 128, None) == bonsai.ERR_ALIGN
+    assert f(None, None, None, None, 0, 64, 128, None) == bonsai.OK
+
+
 def test_affine_matmul_validation():
     f = bonsai.raw().bonsai_q1a_matmul
     p = FAKE

@@ -266,6 +266,103 @@ def test_gemm_matches_gemv_on_the_same_rows(orc):
     assert_close(yg, yv.astype(np.float64), 2 * a, "gemm vs gemv")
 
 
+# ---- base-3 ternary (five trits per byte) ------------------------------------------------------
+def _t5(codes, s, x):
+    import ternary_weight_quantized_bonsai_amd as bonsai
+    torch, dev = torch_dev()
+    note(f"t5_matmul M={x.shape[0]} N={codes.shape[0]} K={x.shape[1]}")
+    y = bonsai.t5_matmul(torch.from_numpy(codes).to(dev), to_dev(s), to_dev(x))
+    torch.cuda.synchronize()
+    return y.cpu().numpy()
+
+
+T5_SHAPES = [(1, 256, 640), (1, 300, 384), (2, 1000, 1152), (8, 2000, 1024), (16, 777, 768),
+             (17, 500, 1280), (3, 130, 13824), (1, 5, 128), (40, 96, 896)]
+
+
+@pytest.mark.parametrize("M,N,K", T5_SHAPES)
+def test_t5_matmul_vs_oracle(M, N, K, orc):
+    import ternary_weight_quantized_bonsai_amd as bonsai
+    t, s, x = synth.make_t5_trits(M, N, K, 71, f"t5{N}x{K}")
+    codes = bonsai.t5_pack(t)
+    y = _t5(codes, s, x)
+    yref, a = orc.t5_matmul(codes, s, x, K)
+    assert_close(y, yref, a, f"t5 M={M} N={N} K={K}")
+
+
+@pytest.mark.parametrize("M,N,K", [(1, 5120, 5120), (8, 5120, 5120), (1, 5120, 13824)])
+def test_t5_matmul_decode_shapes_sampled(M, N, K, orc):
+    import ternary_weight_quantized_bonsai_amd as bonsai
+    t, s, x = synth.make_t5_trits(M, N, K, 0, f"t5{N}x{K}")
+    codes = bonsai.t5_pack(t)
+    y = _t5(codes, s, x)
+    rng = np.random.default_rng(72)
+    n_idx = np.unique(np.concatenate([[0, N - 1], rng.integers(0, N, 200)]))
+    yref, a = orc.t5_matmul(codes, s, x, K, None, n_idx)
+    assert_close(y[:, n_idx], yref, a, "t5 sampled")
+
+
+@pytest.mark.parametrize("M,N,K", [(1, 300, 640), (5, 260, 1152), (20, 129, 384)])
+def test_t5_integer_inputs_bit_exact(M, N, K, orc):
+    """Small integer x and power-of-two scales: exact partial sums, so bit for bit."""
+    import ternary_weight_quantized_bonsai_amd as bonsai
+    rng = np.random.default_rng(73 + M)
+    t = synth.trits_i8(N, K, 73, f"t5int{N}x{K}")
+    s = (2.0 ** rng.integers(-3, 4, (N, K // 128))).astype(np.float16).view(np.uint16)
+    x = rng.integers(-8, 9, (M, K)).astype(np.float16).view(np.uint16)
+    codes = bonsai.t5_pack(t)
+    y = _t5(codes, s, x)
+    yref, _ = orc.t5_matmul(codes, s, x, K)
+    assert np.array_equal(y.astype(np.float64), yref)
+
+
+def test_t5_onehot_every_digit(orc):
+    """x = e_k for every k of two superblocks and a ragged third: y = W[:, k] exactly."""
+    import ternary_weight_quantized_bonsai_amd as bonsai
+    N, K = 40, 384
+    t, s, _ = synth.make_t5_trits(1, N, K, 74, "t5onehot")
+    codes = bonsai.t5_pack(t)
+    x = np.eye(K, dtype=np.float16).view(np.uint16)
+    y = _t5(codes, s, x)
+    assert np.array_equal(y.astype(np.float64), orc.t5_dequant(codes, s, K).T)
+
+
+def test_t5_matches_two_bit_ternary_on_the_same_trits(orc):
+    """The same trits in both ternary layouts give the same products (integer data: bit for bit)."""
+    import ternary_weight_quantized_bonsai_amd as bonsai
+    M, N, K = 4, 700, 1280
+    rng = np.random.default_rng(75)
+    t = synth.trits_i8(N, K, 75, "t5vsq2t")
+    s = (2.0 ** rng.integers(-2, 3, (N, K // 128))).astype(np.float16).view(np.uint16)
+    x = rng.integers(-8, 9, (M, K)).astype(np.float16).view(np.uint16)
+    y5 = _t5(bonsai.t5_pack(t), s, x)
+    y2 = call("q2t_gemv", bonsai.q2t_pack(t), s, x)
+    assert np.array_equal(y5, y2)
+
+
+def test_t5_poison_guard_and_empty(orc):
+    import ternary_weight_quantized_bonsai_amd as bonsai
+    torch, dev = torch_dev()
+    M, N, K = 9, 131, 768
+    t, s, x = synth.make_t5_trits(M, N, K, 76, "t5poison")
+    codes = bonsai.t5_pack(t)
+    buf = torch.full((M * N + 64,), float("nan"), dtype=torch.float32, device=dev)
+    cd, sd, xd = torch.from_numpy(codes).to(dev), to_dev(s), to_dev(x)
+    note(f"t5_matmul poison M={M} N={N} K={K}")
+    st = bonsai.raw().bonsai_t5_matmul(cd.data_ptr(), sd.data_ptr(), xd.data_ptr(), buf.data_ptr(), M, N, K,
+                                       torch.cuda.current_stream().cuda_stream)
+    torch.cuda.synchronize()
+    assert st == bonsai.OK
+    host = buf.cpu().numpy()
+    yref, a = orc.t5_matmul(codes, s, x, K)
+    assert_close(host[:M * N].reshape(M, N), yref, a, "t5 poison")
+    assert np.isnan(host[M * N:]).all()
+    out = torch.full((3, 5), 7.0, dtype=torch.float32, device=dev)
+    assert bonsai.raw().bonsai_t5_matmul(0, 0, 0, out.data_ptr(), 3, 5, 0, None) == bonsai.OK
+    torch.cuda.synchronize()
+    assert (out.cpu().numpy() == 0).all()
+
+
 # ---- affine 1-bit (MLX's scale-and-bias form) ------------------------------------------------
 def _affine(w, a, b, x):
     import ternary_weight_quantized_bonsai_amd as bonsai
