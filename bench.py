@@ -328,7 +328,7 @@ def main() -> int:
 
     def up(a):
         a = np.ascontiguousarray(a)
-        view = {np.dtype(np.uint32): np.int32, np.dtype(np.uint16): np.int16}[a.dtype]
+        view = {np.dtype(np.uint32): np.int32, np.dtype(np.uint16): np.int16, np.dtype(np.uint8): np.uint8}[a.dtype]
         return torch.from_numpy(a.view(view)).to(dev)
 
     # ---- headline workload: the two decode projections at hidden 5120 -------------------
@@ -525,6 +525,63 @@ def main() -> int:
             log(f"ternary M={M5}: {t5 * 1e3:.2f} us, {gb5:.1f} GB/s")
             del ws, ss, w, s, x, y
         extra["ternary_gemv"] = {"shape": "N=5120 K=5120", **tern}
+
+        # The same ternary decode on the base-3 layout (five trits per byte)
+        t5r = {}
+        for M5 in (1, 8):
+            t, s5, x5 = synth.make_t5_trits(M5, N5, K)
+            c5 = up(bonsai.t5_pack(t))
+            s5, x5 = up(s5), up(x5)
+            nb5 = c5.numel() + 2 * s5.numel()
+            R5 = max(3, math.ceil(ROTATE_BYTES / nb5))
+            cs = [c5] + [c5.clone() for _ in range(R5 - 1)]
+            ss = [s5] + [s5.clone() for _ in range(R5 - 1)]
+            y = torch.empty((M5, N5), dtype=torch.float32, device=dev)
+            bonsai.t5_matmul(cs[0], ss[0], x5, out=y)
+            kt5 = kernel_times(hip, bonsai, [lambda j=j: bonsai.t5_matmul(cs[j % R5], ss[j % R5], x5, out=y)
+                                             for j in range(R5)])
+            t5 = float(np.mean(kt5))
+            gb5 = nb5 / (t5 / 1e3) / 1e9
+            t5r[f"M{M5}"] = {"avg_kernel_us": round(t5 * 1e3, 2), "packed_weight_GBps": round(gb5, 1),
+                             "frac_of_8TBps": round(gb5 / PEAK_HBM_GBPS, 4)}
+            log(f"base-3 ternary M={M5}: {t5 * 1e3:.2f} us, {gb5:.1f} GB/s")
+            del cs, ss, c5, s5, x5, y, t
+        extra["ternary_base3_gemv"] = {"shape": "N=5120 K=5120, 1.725 bits per weight", **t5r}
+
+        # Affine 1-bit form (MLX's scale and bias per group): decode at the MLP shape
+        aff = {}
+        for M7 in (1, 8):
+            w, a7, b7, x = (up(v) for v in synth.make_q1a(M7, N4, K))
+            nb7 = q1_bytes(N4, K) + 2 * N4 * (K // 128)            # + the biases
+            R7 = max(3, math.ceil(ROTATE_BYTES / nb7))
+            ws = [w] + [w.clone() for _ in range(R7 - 1)]
+            as_ = [a7] + [a7.clone() for _ in range(R7 - 1)]
+            bs = [b7] + [b7.clone() for _ in range(R7 - 1)]
+            y = torch.empty((M7, N4), dtype=torch.float32, device=dev)
+            bonsai.q1a_matmul(ws[0], as_[0], bs[0], x, out=y)
+            kt7 = kernel_times(hip, bonsai, [lambda j=j: bonsai.q1a_matmul(ws[j % R7], as_[j % R7], bs[j % R7], x, out=y)
+                                             for j in range(R7)])
+            t7 = float(np.mean(kt7))
+            gb7 = nb7 / (t7 / 1e3) / 1e9
+            aff[f"M{M7}"] = {"avg_kernel_us": round(t7 * 1e3, 2), "packed_weight_GBps": round(gb7, 1),
+                             "frac_of_8TBps": round(gb7 / PEAK_HBM_GBPS, 4)}
+            log(f"affine M={M7}: {t7 * 1e3:.2f} us, {gb7:.1f} GB/s")
+            del ws, as_, bs, w, a7, b7, x, y
+        extra["affine_gemv"] = {"shape": "N=13824 K=5120, 1-bit affine (scale + bias per group)", **aff}
+
+        # Embedding gather: 512 token ids from the binary vocabulary table (V = 248320, K = 5120)
+        w, s, _ = (up(v) for v in synth.make_q1(1, N3, K))
+        ids = torch.from_numpy(np.random.default_rng(7).integers(0, N3, 512).astype(np.int64)).to(dev)
+        out = torch.empty((512, K), dtype=torch.float16, device=dev)
+        bonsai.q1_embed(w, s, ids, out=out)
+        kt8 = kernel_times(hip, bonsai, [lambda: bonsai.q1_embed(w, s, ids, out=out) for _ in range(20)])
+        t8 = float(np.mean(kt8))
+        nb8 = 512 * (2 * K + K // 8 + 2 * (K // 128) + 8)        # rows written + rows read + ids
+        gb8 = nb8 / (t8 / 1e3) / 1e9
+        extra["embed_gather"] = {"shape": "512 ids, V=248320 K=5120", "avg_kernel_us": round(t8 * 1e3, 2),
+                                 "GBps": round(gb8, 1), "frac_of_8TBps": round(gb8 / PEAK_HBM_GBPS, 4)}
+        log(f"embed gather: {t8 * 1e3:.2f} us, {gb8:.1f} GB/s")
+        del w, s, ids, out
 
     # Device copy probe: what a plain 1 GiB copy reaches on this machine (read + write bytes); its
     # dispatches also calibrate the HBM byte counters of the traffic summary

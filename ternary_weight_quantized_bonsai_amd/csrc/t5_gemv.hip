@@ -14,13 +14,13 @@
 // one MFMA per digit, and the lane's B operand is 8 consecutive halves of x, one 16-byte LDS
 // read with no repacking.
 //
-// Decoding.  A 256-entry table in LDS maps a byte to its five digits as 2-bit ternary codes
-// (00 -> 0, 01 -> +1, 11 -> -1) at fields 0..4 of both halves of a word.  One v_bfi_b32 joins
-// the low half of byte 2m's entry and the high half of byte 2m + 1's, so that digit i of the two
-// bytes sits at fields i and i + 8; (word << (14 - 2i)) & 0xC000C000 then gives the binary16
-// pair (2 t, 2 t') exactly (the exponent MSB is the code's low bit, the sign its high bit), and
-// the factor 2 comes off once at the end.  Bytes 243..255 are reserved: the table maps them to
-// zero weights, and results on them are unspecified.
+// Decoding.  A 256-entry table in LDS maps a byte to its five digits, each as the high byte of
+// the binary16 it becomes: 0x00 (0), 0x40 (+2) or 0xC0 (-2), digits 0..3 in the entry's first
+// dword and digit 4 in its second.  One v_perm_b32 then builds the operand pair of bytes 2m and
+// 2m + 1 for digit i, (0x00, digit byte, 0x00, digit byte), exactly; the factor 2 comes off once
+// at the end.  Bytes 243..255 are reserved: the table maps them to zero weights, and results on
+// them are unspecified.  The table reads land on random banks; that conflict cost, not the
+// VALU work, is what this decode adds over the 2-bit codes' shift-and-mask.
 //
 // Work split (as the small-M kernel for the other layouts).  A workgroup owns 16 RT weight rows
 // and one block of 16 rows of x; its waves take slices of 640 k (four superblocks, five groups):
@@ -43,7 +43,7 @@ constexpr int kT5SbPerSlice = 4;                     // superblocks of 160 k per
 constexpr int kT5GroupsPerSlice = 5;                 // groups of 128 k per slice (640 k)
 constexpr int kT5SliceBytes = 32 * kT5SbPerSlice;    // code bytes per row and slice
 constexpr int kT5XStride = 2 * 640 + 16;             // LDS bytes per row of x (640 k + pad)
-constexpr int kT5LutBytes = 256 * 4;
+constexpr int kT5LutBytes = 256 * 8;
 constexpr int kT5MaxWaves = 16;
 constexpr int kLdsPerCu = 160 * 1024;
 
@@ -74,7 +74,7 @@ __global__ __launch_bounds__(kT5MaxWaves * 64) void t5_gemv_kernel(const uint8_t
     const int ns = (SB + kT5SbPerSlice - 1) / kT5SbPerSlice;
     const int n0 = blockIdx.x * R;
     const int wbytes = t5_wave_bytes(RT, M);
-    uint32_t *const lut = reinterpret_cast<uint32_t *>(lds);
+    uint2 *const lut = reinterpret_cast<uint2 *>(lds);
     char *const mine = reinterpret_cast<char *>(lds) + kT5LutBytes + wave * wbytes;
     char *const tile = mine;
     char *const sc = mine + TILE;
@@ -84,19 +84,19 @@ __global__ __launch_bounds__(kT5MaxWaves * 64) void t5_gemv_kernel(const uint8_t
     const u32x4 *xg = reinterpret_cast<const u32x4 *>(x);
     const int xunits = K >> 3;                        // 16-byte units per row of x
 
-    // the byte -> codes table: digit i of v at fields i (low half) and i + 8 (high half)
+    // the byte -> digits table: digit i of v as byte i (0..3 of .x, 4 of .y) 0x00, 0x40 or 0xC0
     for (int v = threadIdx.x; v < 256; v += blockDim.x) {
-        uint32_t c = 0;
+        uint32_t b[2] = {0u, 0u};
         if (v < 243) {
             int r = v;
 #pragma unroll
             for (int i = 0; i < 5; ++i) {
                 const int d = r % 3;
                 r /= 3;
-                c |= (d == 0 ? 0u : d == 1 ? 1u : 3u) << (2 * i);
+                b[i >> 2] |= (d == 0 ? 0x00u : d == 1 ? 0x40u : 0xC0u) << (8 * (i & 3));
             }
         }
-        lut[v] = c | (c << 16);
+        lut[v] = uint2{b[0], b[1]};
     }
     __syncthreads();
 
@@ -147,21 +147,15 @@ __global__ __launch_bounds__(kT5MaxWaves * 64) void t5_gemv_kernel(const uint8_t
         float4_v d[RT];
 #pragma unroll
         for (int sb = 0; sb < kT5SbPerSlice; ++sb) {
-            // this lane's 8 bytes (8q .. 8q + 7) of superblock sb in each row tile, joined in
-            // pairs: wv[t][m] holds bytes 2m (fields 0..4) and 2m + 1 (fields 8..12)
-            uint32_t wv[RT][4];
+            // this lane's 8 bytes (8q .. 8q + 7) of superblock sb in each row tile, decoded
+            uint2 lv[RT][8];
 #pragma unroll
             for (int t = 0; t < RT; ++t) {
                 const int r = 16 * t + i16;
                 const int slot = (2 * sb + (q >> 1)) ^ (r & 7);
                 const uint2 b8 = *reinterpret_cast<const uint2 *>(tile + kT5SliceBytes * r + 16 * slot + 8 * (q & 1));
 #pragma unroll
-                for (int m = 0; m < 4; ++m) {
-                    const uint32_t w = m < 2 ? b8.x : b8.y;
-                    const uint32_t lo = lut[(w >> (16 * (m & 1))) & 0xFFu];
-                    const uint32_t hi = lut[(w >> (16 * (m & 1) + 8)) & 0xFFu];
-                    wv[t][m] = (lo & 0x0000FFFFu) | (hi & 0xFFFF0000u);     // v_bfi_b32
-                }
+                for (int e = 0; e < 8; ++e) lv[t][e] = lut[((e < 4 ? b8.x : b8.y) >> (8 * (e & 3))) & 0xFFu];
             }
 #pragma unroll
             for (int i = 0; i < 5; ++i) {
@@ -169,11 +163,15 @@ __global__ __launch_bounds__(kT5MaxWaves * 64) void t5_gemv_kernel(const uint8_t
                 const int u = blk >> 2;                       // its group in the slice
                 const u32x4 bv = *reinterpret_cast<const u32x4 *>(xrow + 64 * blk + 16 * q);
                 const half8_t bf = __builtin_bit_cast(half8_t, bv);
+                // (0x00, byte i' of the first source, 0x00, byte i' of the second)
+                const uint32_t sel = 0x000C000Cu | ((uint32_t)(i & 3) << 8) | ((uint32_t)(4 + (i & 3)) << 24);
 #pragma unroll
                 for (int t = 0; t < RT; ++t) {
                     u32x4 av;
 #pragma unroll
-                    for (int m = 0; m < 4; ++m) av[m] = (wv[t][m] << (14 - 2 * i)) & 0xC000C000u;
+                    for (int m = 0; m < 4; ++m)
+                        av[m] = i < 4 ? __builtin_amdgcn_perm(lv[t][2 * m + 1].x, lv[t][2 * m].x, sel)
+                                      : __builtin_amdgcn_perm(lv[t][2 * m + 1].y, lv[t][2 * m].y, sel);
                     d[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8_t, av), bf,
                                                                   (blk & 3) == 0 ? zero4 : d[t], 0, 0, 0);
                 }
