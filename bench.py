@@ -529,9 +529,7 @@ def main() -> int:
         # The same ternary decode on the base-3 layout (five trits per byte)
         t5r = {}
         for M5 in (1, 8):
-            t, s5, x5 = synth.make_t5_trits(M5, N5, K)
-            c5 = up(bonsai.t5_pack(t))
-            s5, x5 = up(s5), up(x5)
+            c5, s5, x5 = (up(v) for v in synth.make_t5(M5, N5, K))
             nb5 = c5.numel() + 2 * s5.numel()
             R5 = max(3, math.ceil(ROTATE_BYTES / nb5))
             cs = [c5] + [c5.clone() for _ in range(R5 - 1)]
@@ -545,7 +543,7 @@ def main() -> int:
             t5r[f"M{M5}"] = {"avg_kernel_us": round(t5 * 1e3, 2), "packed_weight_GBps": round(gb5, 1),
                              "frac_of_8TBps": round(gb5 / PEAK_HBM_GBPS, 4)}
             log(f"base-3 ternary M={M5}: {t5 * 1e3:.2f} us, {gb5:.1f} GB/s")
-            del cs, ss, c5, s5, x5, y, t
+            del cs, ss, c5, s5, x5, y
         extra["ternary_base3_gemv"] = {"shape": "N=5120 K=5120, 1.725 bits per weight", **t5r}
 
         # Affine 1-bit form (MLX's scale and bias per group): decode at the MLP shape

@@ -15,6 +15,9 @@ returned in its storage form:
 * activations  - IEEE binary16 bit patterns (uint16) of N(0, 1).
 * biases       - IEEE binary16 bit patterns (uint16) of N(0, 0.02), for the
                  affine (scale, bias) form of the binary words.
+* base-3 bytes - uint8, each byte independently uniform over 0..242 (every
+                 value below 243 is a valid byte; the generator knows only the
+                 row length, 32 bytes per 160 weights).
 
 The workload shapes are those of the model card ("1-bit Bonsai 27B",
 model-overview table and the config summary on the Bonsai-27B article):
@@ -30,8 +33,8 @@ import numpy as np
 
 __all__ = [
     "Config", "CONFIGS", "rng_for", "sign_words", "trit_words", "scales_f16",
-    "activations_f16", "biases_f16", "trits_i8", "make_q1", "make_q2t", "make_q1a", "make_t5_trits",
-    "digest",
+    "activations_f16", "biases_f16", "trits_i8", "t5_bytes", "make_q1", "make_q2t", "make_q1a", "make_t5",
+    "make_t5_trits", "digest",
 ]
 
 
@@ -112,6 +115,12 @@ def trits_i8(n_rows: int, k: int, seed: int, tag: str, p_zero: float = 0.4, p_pl
     return np.where(u < 1.0 - p_zero - p_plus, -1, np.where(u < 1.0 - p_zero, 1, 0)).astype(np.int8)
 
 
+def t5_bytes(n_rows: int, k: int, seed: int, tag: str) -> np.ndarray:
+    """uint8 [n_rows, 32 ceil(k/160)]: each byte uniform over 0..242."""
+    rng = rng_for(seed, tag + "/t5")
+    return rng.integers(0, 243, size=(n_rows, 32 * ((k + 159) // 160)), dtype=np.uint8)
+
+
 def make_q1(M: int, N: int, K: int, seed: int = 0, tag: str | None = None):
     """(sign words [N, K/32], scales [N, K/128], x [M, K]) for a binary matmul."""
     tag = tag or f"{N}x{K}"
@@ -131,6 +140,13 @@ def make_q1a(M: int, N: int, K: int, seed: int = 0, tag: str | None = None):
     tag = tag or f"a{N}x{K}"
     w, s, x = make_q1(M, N, K, seed, tag)
     return w, s, biases_f16(N, K // 128, seed, tag), x
+
+
+def make_t5(M: int, N: int, K: int, seed: int = 0, tag: str | None = None):
+    """(base-3 bytes [N, 32 ceil(K/160)], scales [N, K/128], x [M, K]) for a base-3 matmul."""
+    tag = tag or f"t5{N}x{K}"
+    return (t5_bytes(N, K, seed, tag), scales_f16(N, K // 128, seed, tag),
+            activations_f16(M, K, seed, f"{tag}/M{M}"))
 
 
 def make_t5_trits(M: int, N: int, K: int, seed: int = 0, tag: str | None = None):

@@ -282,9 +282,7 @@ T5_SHAPES = [(1, 256, 640), (1, 300, 384), (2, 1000, 1152), (8, 2000, 1024), (16
 
 @pytest.mark.parametrize("M,N,K", T5_SHAPES)
 def test_t5_matmul_vs_oracle(M, N, K, orc):
-    import ternary_weight_quantized_bonsai_amd as bonsai
-    t, s, x = synth.make_t5_trits(M, N, K, 71, f"t5{N}x{K}")
-    codes = bonsai.t5_pack(t)
+    codes, s, x = synth.make_t5(M, N, K, 71, f"t5{N}x{K}")
     y = _t5(codes, s, x)
     yref, a = orc.t5_matmul(codes, s, x, K)
     assert_close(y, yref, a, f"t5 M={M} N={N} K={K}")
@@ -292,9 +290,7 @@ def test_t5_matmul_vs_oracle(M, N, K, orc):
 
 @pytest.mark.parametrize("M,N,K", [(1, 5120, 5120), (8, 5120, 5120), (1, 5120, 13824)])
 def test_t5_matmul_decode_shapes_sampled(M, N, K, orc):
-    import ternary_weight_quantized_bonsai_amd as bonsai
-    t, s, x = synth.make_t5_trits(M, N, K, 0, f"t5{N}x{K}")
-    codes = bonsai.t5_pack(t)
+    codes, s, x = synth.make_t5(M, N, K, 0, f"t5{N}x{K}")
     y = _t5(codes, s, x)
     rng = np.random.default_rng(72)
     n_idx = np.unique(np.concatenate([[0, N - 1], rng.integers(0, N, 200)]))
@@ -305,12 +301,10 @@ def test_t5_matmul_decode_shapes_sampled(M, N, K, orc):
 @pytest.mark.parametrize("M,N,K", [(1, 300, 640), (5, 260, 1152), (20, 129, 384)])
 def test_t5_integer_inputs_bit_exact(M, N, K, orc):
     """Small integer x and power-of-two scales: exact partial sums, so bit for bit."""
-    import ternary_weight_quantized_bonsai_amd as bonsai
     rng = np.random.default_rng(73 + M)
-    t = synth.trits_i8(N, K, 73, f"t5int{N}x{K}")
+    codes = synth.t5_bytes(N, K, 73, f"t5int{N}x{K}")
     s = (2.0 ** rng.integers(-3, 4, (N, K // 128))).astype(np.float16).view(np.uint16)
     x = rng.integers(-8, 9, (M, K)).astype(np.float16).view(np.uint16)
-    codes = bonsai.t5_pack(t)
     y = _t5(codes, s, x)
     yref, _ = orc.t5_matmul(codes, s, x, K)
     assert np.array_equal(y.astype(np.float64), yref)
@@ -318,10 +312,8 @@ def test_t5_integer_inputs_bit_exact(M, N, K, orc):
 
 def test_t5_onehot_every_digit(orc):
     """x = e_k for every k of two superblocks and a ragged third: y = W[:, k] exactly."""
-    import ternary_weight_quantized_bonsai_amd as bonsai
     N, K = 40, 384
-    t, s, _ = synth.make_t5_trits(1, N, K, 74, "t5onehot")
-    codes = bonsai.t5_pack(t)
+    codes, s, _ = synth.make_t5(1, N, K, 74, "t5onehot")
     x = np.eye(K, dtype=np.float16).view(np.uint16)
     y = _t5(codes, s, x)
     assert np.array_equal(y.astype(np.float64), orc.t5_dequant(codes, s, K).T)
@@ -344,8 +336,7 @@ def test_t5_poison_guard_and_empty(orc):
     import ternary_weight_quantized_bonsai_amd as bonsai
     torch, dev = torch_dev()
     M, N, K = 9, 131, 768
-    t, s, x = synth.make_t5_trits(M, N, K, 76, "t5poison")
-    codes = bonsai.t5_pack(t)
+    codes, s, x = synth.make_t5(M, N, K, 76, "t5poison")
     buf = torch.full((M * N + 64,), float("nan"), dtype=torch.float32, device=dev)
     cd, sd, xd = torch.from_numpy(codes).to(dev), to_dev(s), to_dev(x)
     note(f"t5_matmul poison M={M} N={N} K={K}")
