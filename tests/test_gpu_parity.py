@@ -478,3 +478,58 @@ def test_embed_gather_vocab_shape(orc):
     w, s, _ = make("q1_gemv", 1, V, K, 0, f"{V}x{K}")
     ids = np.random.default_rng(6).integers(0, V, 512).astype(np.int64)
     assert np.array_equal(_embed(w, s, ids), _embed_ref(orc, w, s, ids, K))
+
+
+# ---- HIP graph capture ------------------------------------------------------------------------
+def test_graph_capture_and_replay_of_every_entry_point(orc):
+    """Each matmul entry point captured in one HIP graph (on torch's capture stream), replayed
+    several times with eager work and synchronisations between the replays; every replay must
+    equal the eager result bit for bit, and the eager result must meet the oracle."""
+    import ternary_weight_quantized_bonsai_amd as bonsai
+    torch, dev = torch_dev()
+    calls = []
+    w, s, x = synth.make_q1(1, 700, 1024, 81, "graph/q1")
+    calls.append(("q1_gemv M=1", bonsai.q1_gemv, (to_dev(w), to_dev(s), to_dev(x)), orc.q1_matmul(w, s, x, 1024)))
+    w, s, x = synth.make_q1(5, 700, 1024, 82, "graph/q1m")
+    calls.append(("q1_gemv M=5", bonsai.q1_gemv, (to_dev(w), to_dev(s), to_dev(x)), orc.q1_matmul(w, s, x, 1024)))
+    w, s, x = synth.make_q1(130, 300, 768, 83, "graph/gemm")
+    calls.append(("q1_gemm M=130", bonsai.q1_gemm, (to_dev(w), to_dev(s), to_dev(x)), orc.q1_matmul(w, s, x, 768)))
+    w, s, x = synth.make_q2t(3, 500, 640, 84, "graph/q2t")
+    calls.append(("q2t_gemv M=3", bonsai.q2t_gemv, (to_dev(w), to_dev(s), to_dev(x)), orc.q2t_matmul(w, s, x, 640)))
+    w, s, x = synth.make_q2t(100, 300, 640, 85, "graph/q2tg")
+    calls.append(("q2t_gemm M=100", bonsai.q2t_gemm, (to_dev(w), to_dev(s), to_dev(x)), orc.q2t_matmul(w, s, x, 640)))
+    c, s, x = synth.make_t5(2, 400, 1152, 86, "graph/t5")
+    calls.append(("t5_matmul M=2", bonsai.t5_matmul, (torch.from_numpy(c).to(dev), to_dev(s), to_dev(x)),
+                  orc.t5_matmul(c, s, x, 1152)))
+    w, a, b, x = synth.make_q1a(4, 300, 640, 87, "graph/q1a")
+    calls.append(("q1a_matmul M=4", bonsai.q1a_matmul, (to_dev(w), to_dev(a), to_dev(b), to_dev(x)),
+                  (orc.q1a_matmul(w, a, b, x, 640)[0], _affine_magnitude(orc, w, a, b, x))))
+    outs = [torch.empty((args[-1].shape[0], args[0].shape[0]), dtype=torch.float32, device=dev)
+            for _, _, args, _ in calls]
+    note("graph: eager reference run")
+    eager = []
+    for (name, fn, args, (yref, mag)), out in zip(calls, outs):
+        fn(*args, out=out)
+        torch.cuda.synchronize()
+        eager.append(out.clone())
+        assert_close(out.cpu().numpy(), yref, mag, f"eager {name}")
+    note("graph: capture")
+    g = torch.cuda.CUDAGraph()
+    stream = torch.cuda.Stream()
+    stream.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(stream):
+        for out in outs:
+            out.fill_(float("nan"))
+        with torch.cuda.graph(g, stream=stream):
+            for (name, fn, args, _), out in zip(calls, outs):
+                fn(*args, out=out)
+    torch.cuda.synchronize()
+    for rep in range(4):
+        note(f"graph: replay {rep}")
+        for out in outs:
+            out.fill_(float("nan"))               # eager work between replays
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for (name, _, _, _), out, ref in zip(calls, outs, eager):
+            assert torch.equal(out, ref), f"replay {rep}: {name} differs from the eager result"
