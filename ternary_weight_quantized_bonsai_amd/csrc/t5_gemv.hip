@@ -44,7 +44,10 @@ constexpr int kT5GroupsPerSlice = 5;                 // groups of 128 k per slic
 constexpr int kT5SliceBytes = 32 * kT5SbPerSlice;    // code bytes per row and slice
 constexpr int kT5XStride = 2 * 640 + 16;             // LDS bytes per row of x (640 k + pad)
 constexpr int kT5LutBytes = 256 * 8;
-constexpr int kT5MaxWaves = 16;
+// Waves per workgroup: at most 16 (WIDE), which caps a wave at 128 VGPRs, or 8.  The 32-row
+// tile takes about 160 VGPRs: the 8-wave build keeps them all, the 16-wave build spills two but
+// lets a CU hold two 8-wave workgroups by registers.
+constexpr int t5_max_waves(bool wide) { return wide ? 16 : 8; }
 constexpr int kLdsPerCu = 160 * 1024;
 
 constexpr int t5_scale_bytes(int rt) { return (5 * 16 * rt + 63) / 64 * 256; }
@@ -52,8 +55,8 @@ constexpr int t5_scale_bytes(int rt) { return (5 * 16 * rt + 63) / 64 * 256; }
 // LDS bytes of one wave: codes, scales and the M rows of x
 constexpr int t5_wave_bytes(int rt, int m) { return 16 * rt * kT5SliceBytes + t5_scale_bytes(rt) + m * kT5XStride; }
 
-template <int RT>
-__global__ __launch_bounds__(kT5MaxWaves * 64) void t5_gemv_kernel(const uint8_t *__restrict__ codes,
+template <int RT, bool WIDE>
+__global__ __launch_bounds__(t5_max_waves(WIDE) * 64) void t5_gemv_kernel(const uint8_t *__restrict__ codes,
                                                                   const uint16_t *__restrict__ scales,
                                                                   const uint16_t *__restrict__ x,
                                                                   float *__restrict__ y, int M, int N, int K)
@@ -208,11 +211,11 @@ __global__ __launch_bounds__(kT5MaxWaves * 64) void t5_gemv_kernel(const uint8_t
 }
 
 // waves of a workgroup: one per slice, at most 16 and as many as the LDS holds
-int t5_waves(int rt, int M, int K)
+int t5_waves(int rt, bool wide, int M, int K)
 {
     const int ns = ((K + 159) / 160 + kT5SbPerSlice - 1) / kT5SbPerSlice;
     const int per_wave = t5_wave_bytes(rt, M) + M * 16 * rt * 4;
-    int nw = ns < kT5MaxWaves ? ns : kT5MaxWaves;
+    int nw = ns < t5_max_waves(wide) ? ns : t5_max_waves(wide);
     if (nw > (kLdsPerCu - kT5LutBytes) / per_wave) nw = (kLdsPerCu - kT5LutBytes) / per_wave;
     return nw;
 }
@@ -222,45 +225,74 @@ size_t t5_lds(int rt, int mb, int nw)
     return (size_t)kT5LutBytes + (size_t)nw * t5_wave_bytes(rt, mb) + (size_t)nw * mb * 16 * rt * 4;
 }
 
-template <int RT>
+// waves of t5_gemv_kernel<RT> that one CU holds by registers: 512 VGPRs per SIMD lane, in
+// granules of 8, at most 8 waves per SIMD, 4 SIMDs
+template <int RT, bool WIDE>
+int t5_reg_waves_per_cu()
+{
+    static const int waves = [] {
+        hipFuncAttributes a;
+        if (hipFuncGetAttributes(&a, reinterpret_cast<const void *>(&t5_gemv_kernel<RT, WIDE>)) != hipSuccess ||
+            a.numRegs <= 0)
+            return 8;
+        const int per_simd = 512 / ((a.numRegs + 7) / 8 * 8);
+        return 4 * (per_simd < 8 ? per_simd : 8);
+    }();
+    return waves;
+}
+
+template <int RT, bool WIDE>
 hipError_t t5_launch_rt(const uint8_t *codes, const uint16_t *scales, const uint16_t *x, float *y,
                         int M, int N, int K, hipStream_t stream)
 {
     const int mb = M < 16 ? M : 16;
-    const int nw = t5_waves(RT, mb, K);
+    const int nw = t5_waves(RT, WIDE, mb, K);
     if (nw < 1) return hipErrorInvalidValue;
     const int64_t blocks = ((int64_t)N + 16 * RT - 1) / (16 * RT);
     const int64_t yblocks = ((int64_t)M + 15) / 16;
     if (blocks > INT_MAX || yblocks > 65535) return hipErrorInvalidValue;
-    static const bool attr = hipFuncSetAttribute(reinterpret_cast<const void *>(&t5_gemv_kernel<RT>),
+    static const bool attr = hipFuncSetAttribute(reinterpret_cast<const void *>(&t5_gemv_kernel<RT, WIDE>),
                                                  hipFuncAttributeMaxDynamicSharedMemorySize, kLdsPerCu) == hipSuccess;
     if (!attr) return hipErrorInvalidValue;
     void *args[] = {&codes, &scales, &x, &y, &M, &N, &K};
-    return launch_kernel(reinterpret_cast<const void *>(&t5_gemv_kernel<RT>), dim3((unsigned)blocks, (unsigned)yblocks),
+    return launch_kernel(reinterpret_cast<const void *>(&t5_gemv_kernel<RT, WIDE>), dim3((unsigned)blocks, (unsigned)yblocks),
                          dim3(64 * nw), args, t5_lds(RT, mb, nw), stream);
 }
 
 }  // namespace
 
-// Any M >= 1 (16 rows of x per column block).  The row tile (16 or 32 rows) is the one whose
-// grid needs the fewest rounds of the chip's 256 CUs, the smaller on a tie.
+// Any M >= 1 (16 rows of x per column block).  Three builds: 16-row tiles (up to 16 waves),
+// 32-row tiles with up to 8 waves (no spill), 32-row tiles with up to 16 waves (two registers
+// spilled, two workgroups per CU).  The launch takes the build whose grid needs the fewest rounds
+// of the chip's 256 CUs, given what the LDS and the registers of a CU hold; on a tie, in the
+// order that measured fastest: for one row of x the 16-row tile first (more workgroups in
+// flight), for more rows the 8-wave 32-row build first (x, held once per wave, fills the LDS).
 hipError_t launch_t5_matmul(const uint8_t *codes, const uint16_t *scales, const uint16_t *x, float *y,
                             int M, int N, int K, hipStream_t stream)
 {
     if (M < 1) return hipErrorInvalidValue;
-    constexpr int kCus = 256, kWavesPerCu = 32;
+    constexpr int kCus = 256;
     const int mb = M < 16 ? M : 16;
-    auto rounds = [&](int rt) -> int64_t {
-        const int nw = t5_waves(rt, mb, K);
+    auto rounds = [&](int rt, bool wide, int reg_waves) -> int64_t {
+        const int nw = t5_waves(rt, wide, mb, K);
         if (nw < 1) return INT64_MAX;
         int64_t per_cu = kLdsPerCu / (int64_t)t5_lds(rt, mb, nw);
-        if (per_cu > kWavesPerCu / nw) per_cu = kWavesPerCu / nw;
+        if (per_cu > reg_waves / nw) per_cu = reg_waves / nw;
         if (per_cu < 1) return INT64_MAX;
         const int64_t blocks = (((int64_t)N + 16 * rt - 1) / (16 * rt)) * (((int64_t)M + 15) / 16);
         return (blocks + per_cu * kCus - 1) / (per_cu * kCus);
     };
-    if (rounds(1) <= rounds(2)) return t5_launch_rt<1>(codes, scales, x, y, M, N, K, stream);
-    return t5_launch_rt<2>(codes, scales, x, y, M, N, K, stream);
+    const int64_t r1 = rounds(1, true, t5_reg_waves_per_cu<1, true>());
+    const int64_t r2n = rounds(2, false, t5_reg_waves_per_cu<2, false>());
+    const int64_t r2s = rounds(2, true, t5_reg_waves_per_cu<2, true>());
+    if (M == 1) {
+        if (r1 <= r2n && r1 <= r2s) return t5_launch_rt<1, true>(codes, scales, x, y, M, N, K, stream);
+        if (r2n <= r2s) return t5_launch_rt<2, false>(codes, scales, x, y, M, N, K, stream);
+        return t5_launch_rt<2, true>(codes, scales, x, y, M, N, K, stream);
+    }
+    if (r2n <= r2s && r2n <= r1) return t5_launch_rt<2, false>(codes, scales, x, y, M, N, K, stream);
+    if (r2s <= r1) return t5_launch_rt<2, true>(codes, scales, x, y, M, N, K, stream);
+    return t5_launch_rt<1, true>(codes, scales, x, y, M, N, K, stream);
 }
 
 }  // namespace bonsai
