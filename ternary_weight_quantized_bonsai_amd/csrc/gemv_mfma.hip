@@ -349,31 +349,70 @@ hipError_t launch_rt(const uint32_t *codes, const uint16_t *scales, const uint16
     return launch_kernel(fn, dim3((unsigned)blocks, (unsigned)yblocks), dim3(64 * nw), args, lds, stream);
 }
 
+// waves of gemv_mfma_kernel<TERN, AFF, RT, PAIRS> that one CU holds by registers: 512 VGPRs per
+// SIMD lane, in granules of 8, at most 8 waves per SIMD, 4 SIMDs
+template <bool TERN, bool AFF, int RT, bool PAIRS>
+int sm_reg_waves_per_cu()
+{
+    static const int waves = [] {
+        hipFuncAttributes a;
+        if (hipFuncGetAttributes(&a, reinterpret_cast<const void *>(&gemv_mfma_kernel<TERN, AFF, RT, PAIRS>)) !=
+                hipSuccess ||
+            a.numRegs <= 0)
+            return 8;
+        const int per_simd = 512 / ((a.numRegs + 7) / 8 * 8);
+        return 4 * (per_simd < 8 ? per_simd : 8);
+    }();
+    return waves;
+}
+
+template <bool TERN, bool AFF, int RT>
+int sm_reg_waves(bool pairs)
+{
+    return pairs ? sm_reg_waves_per_cu<TERN, AFF, RT, true>() : sm_reg_waves_per_cu<TERN, AFF, RT, false>();
+}
+
 template <bool TERN, bool AFF = false>
 hipError_t launch_sm(const uint32_t *codes, const uint16_t *scales, const uint16_t *biases, const uint16_t *x,
                      float *y, int M, int N, int K, hipStream_t stream)
 {
-    // Every wave loads its slice at once and then computes, so a second round of workgroups
-    // on a CU pays the load latency again: take the row tile (16, 32 or 64 rows) whose grid
-    // needs the fewest rounds of the chip's 256 CUs, given what the LDS and the 32 wave slots
-    // of a CU hold, and among those the smallest tile (the most workgroups).
-    constexpr int kCus = 256, kWavesPerCu = 32;
+    // Every wave loads its slice at once and then computes, so a second round of workgroups on
+    // a CU pays the load latency again.  The row tile (16, 32 or 64 rows) is the one whose grid
+    // needs the fewest rounds of the chip's 256 CUs, given what the LDS and the registers of a CU
+    // hold; among those, the one that leaves the busiest CU the fewest weight rows (workgroups
+    // per CU, rounded up, times the tile), then the larger tile (its x copies and reduction
+    // serve more rows).
+    constexpr int kCus = 256;
     const int mb = M < 16 ? M : 16;
-    auto rounds = [&](int rt) -> int64_t {
-        // the affine kernel keeps scales and biases in registers: no four-tile variant
-        if (AFF && rt == 4) return INT64_MAX;
+    const bool pairs = (K / 128) % 2 == 0;
+    struct Cost {
+        int64_t rounds, rows;
+    };
+    auto cost = [&](int rt, int reg_waves) -> Cost {
         const int nw = sm_waves<TERN, AFF>(rt, mb, K);
-        if (nw < 1) return INT64_MAX;
+        if (nw < 1) return {INT64_MAX, INT64_MAX};
         const int64_t lds = (int64_t)nw * sm_wave_bytes<TERN, AFF>(rt, mb) + (int64_t)nw * mb * 16 * rt * 4;
         int64_t per_cu = kLdsPerCu / lds;
-        if (per_cu > kWavesPerCu / nw) per_cu = kWavesPerCu / nw;
-        if (per_cu < 1) return INT64_MAX;
+        if (per_cu > reg_waves / nw) per_cu = reg_waves / nw;
+        if (per_cu < 1) return {INT64_MAX, INT64_MAX};
         const int64_t blocks = (((int64_t)N + 16 * rt - 1) / (16 * rt)) * (((int64_t)M + 15) / 16);
-        return (blocks + per_cu * kCus - 1) / (per_cu * kCus);
+        return {(blocks + per_cu * kCus - 1) / (per_cu * kCus), (blocks + kCus - 1) / kCus * 16 * rt};
     };
-    const int64_t r1 = rounds(1), r2 = rounds(2), r4 = rounds(4);
-    if (r1 <= r2 && r1 <= r4) return launch_rt<TERN, AFF, 1>(codes, scales, biases, x, y, M, N, K, stream);
-    if (r2 <= r4) return launch_rt<TERN, AFF, 2>(codes, scales, biases, x, y, M, N, K, stream);
+    auto better = [](const Cost &a, const Cost &b) {   // a strictly better than b, ties to b
+        return a.rounds < b.rounds || (a.rounds == b.rounds && a.rows < b.rows);
+    };
+    const Cost c1 = cost(1, sm_reg_waves<TERN, AFF, 1>(pairs));
+    const Cost c2 = cost(2, sm_reg_waves<TERN, AFF, 2>(pairs));
+    // the affine kernel keeps scales and biases in registers: no four-tile variant
+    Cost c4 = {INT64_MAX, INT64_MAX};
+    if constexpr (!AFF) c4 = cost(4, sm_reg_waves<TERN, AFF, 4>(pairs));
+    int rt = 4;
+    Cost best = c4;
+    if (better(c2, best)) rt = 2, best = c2;
+    if (better(c1, best)) rt = 1, best = c1;
+    if (best.rounds == INT64_MAX) return hipErrorInvalidValue;
+    if (rt == 1) return launch_rt<TERN, AFF, 1>(codes, scales, biases, x, y, M, N, K, stream);
+    if (rt == 2) return launch_rt<TERN, AFF, 2>(codes, scales, biases, x, y, M, N, K, stream);
     if constexpr (AFF) return hipErrorInvalidValue;
     else return launch_rt<TERN, AFF, 4>(codes, scales, biases, x, y, M, N, K, stream);
 }
