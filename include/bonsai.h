@@ -151,7 +151,9 @@ bonsai_status bonsai_q2t_pack(const int8_t *trits, int64_t N, int64_t K, uint32_
 bonsai_status bonsai_q2t_unpack(const uint32_t *wcodes, int64_t N, int64_t K, int8_t *trits);
 
 /* Name of the HIP runtime error behind the most recent BONSAI_ERR_DEVICE returned on the
- * calling thread ("none" if there was none).  Static string; never NULL. */
+ * calling thread ("none" if there was none).  Static string; never NULL.  A call that returns
+ * BONSAI_ERR_DEVICE also clears the HIP runtime's last-error state (hipGetLastError), so the
+ * caller's next HIP call does not report the refused launch again. */
 const char *bonsai_last_device_error(void);
 
 /* Measurement hook.  The next GPU entry point called on this thread launches its kernel with

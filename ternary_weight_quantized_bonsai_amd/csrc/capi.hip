@@ -47,6 +47,16 @@ bool f16_twice(uint16_t s, uint16_t *out)
     return true;
 }
 
+// A refused launch: keep its name for bonsai_last_device_error and clear the runtime's
+// last-error state, so that the caller's next, unrelated HIP call does not report it again.
+bonsai_status device_status(hipError_t e)
+{
+    if (e == hipSuccess) return BONSAI_OK;
+    g_last_device_error = hipGetErrorName(e);
+    (void)hipGetLastError();
+    return BONSAI_ERR_DEVICE;
+}
+
 template <typename Launch>
 bonsai_status run(const void *w, const void *s, const void *x, float *y, int64_t M, int64_t N,
                   int64_t K, int64_t max_m, void *stream, Launch launch)
@@ -56,9 +66,7 @@ bonsai_status run(const void *w, const void *s, const void *x, float *y, int64_t
     hipStream_t hs = static_cast<hipStream_t>(stream);
     const hipError_t e = K == 0 ? launch_fill_zero(y, M * N, hs)
                                 : launch((int)M, (int)N, (int)K, hs);
-    if (e == hipSuccess) return BONSAI_OK;
-    g_last_device_error = hipGetErrorName(e);
-    return BONSAI_ERR_DEVICE;
+    return device_status(e);
 }
 
 }  // namespace
@@ -215,10 +223,7 @@ bonsai_status bonsai_q1_embed(const uint32_t *wbits, const uint16_t *scales, con
     if (!ids || !out || (V > 0 && (!wbits || !scales))) return BONSAI_ERR_NULL;
     if (!aligned16(ids) || !aligned16(out) || (V > 0 && (!aligned16(wbits) || !aligned16(scales))))
         return BONSAI_ERR_ALIGN;
-    const hipError_t e = launch_q1_embed(wbits, scales, ids, out, n_ids, V, (int)K, static_cast<hipStream_t>(hip_stream));
-    if (e == hipSuccess) return BONSAI_OK;
-    g_last_device_error = hipGetErrorName(e);
-    return BONSAI_ERR_DEVICE;
+    return device_status(launch_q1_embed(wbits, scales, ids, out, n_ids, V, (int)K, static_cast<hipStream_t>(hip_stream)));
 }
 
 bonsai_status bonsai_q1_pack(const int8_t *signs, int64_t N, int64_t K, uint32_t *wbits)

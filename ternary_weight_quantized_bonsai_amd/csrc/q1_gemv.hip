@@ -7,10 +7,10 @@
 // 1.125 bits/weight from HBM once, with as few VALU operations per weight as possible: the
 // signs of four weights index a table of the 16 signed sums of their x values.
 //
-// Work split.  A workgroup owns 64 consecutive weight rows (lane r of every wave <-> row r);
-// its waves take disjoint K-slices (whole groups) of those rows and meet in LDS at the end,
-// summed in a fixed order.  Weight bytes reach LDS by direct global->LDS loads of whole lines.
-// Two to eight rows of x (M = 2..8) go to the matrix-core GEMV instead (gemv_mfma.hip).
+// Two kernels share the method: one for small N (a row tile per CU, the tile's waves splitting
+// K) and a persistent one for large N (tables built once per CU).  Weight bytes reach LDS by
+// direct global->LDS loads of whole lines.  K too long for their tables in LDS, and two to eight
+// rows of x (M = 2..8), go to the matrix-core GEMV instead (gemv_mfma.hip).
 #include "device.h"
 #include "launch.h"
 
@@ -30,11 +30,6 @@ namespace {
 // bits 8..31 hold the (256-aligned) table base.  Chunk c's table is 16 consecutive floats at
 // byte offset 64*c (the read's immediate offset), so the 16 possible addresses of a lookup lie
 // in 16 distinct LDS banks: lookups never conflict, equal nibbles broadcast.
-//
-// Weight tile: 8 groups (128 B) of each of the wave's 64 rows arrive through direct
-// global->LDS loads, 8 rows x 128 B per instruction (fully used lines).  The 16-byte cell of
-// (row r, group u) of a batch sits at 128*r + 16*(u ^ ((r >> 1) & 7)): the swizzle keeps a
-// wave's row-wise reads of one column free of bank conflicts.
 
 // r[7:0] = 4 * nibble (byte KB of v masked with 0x3C); r[31:8] keep the LUT base (256-aligned).
 template <int KB>
@@ -71,128 +66,7 @@ __device__ __forceinline__ void word_addrs(uint32_t w, uint32_t r[8], uint32_t m
     nib_addr<3>(r[6], l, mask_3c); nib_addr<3>(r[7], h, mask_3c);
 }
 
-constexpr int kLutBatch = 8;                        // groups per weight tile (128 B per row)
-constexpr int kLutTileBytes = 64 * kLutBatch * 16;  // 8 KB
 constexpr int kLutBytes = 32 * 16 * 4;              // 2 KB of tables per group
-
-__global__ __launch_bounds__(384) void q1_gemv_lut_kernel(const uint32_t *__restrict__ wbits,
-                                                          const uint16_t *__restrict__ scales,
-                                                          const uint16_t *__restrict__ x,
-                                                          float *__restrict__ y, int N, int K, int gps)
-{
-    constexpr int B = kLutBatch;
-    extern __shared__ u32x4 lds[];
-
-    const int lane = threadIdx.x & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int nwaves = blockDim.x >> 6;
-    const int G = K >> 7;
-    const int row0 = blockIdx.x * 64;
-    const int row = row0 + lane;
-    const int g0 = wave * gps;
-    const int g1 = min(G, g0 + gps);
-
-    char *wl = reinterpret_cast<char *>(lds) + wave * (kLutTileBytes + kLutBytes);
-    char *tile = wl;
-    char *lut = wl + kLutTileBytes;
-    const u32x4 *wg = reinterpret_cast<const u32x4 *>(wbits);      // (row n, group g) at n * G + g
-    const uint16_t *srow = scales + (size_t)min(row, N - 1) * G;
-    const bool vec_scales = (G & 7) == 0;       // batches then start at multiples of 8 groups
-    const uint32_t mask_3c = __builtin_amdgcn_readfirstlane(0x3Cu);
-    const uint32_t lut_addr = (uint32_t)(uintptr_t)((lds_char_t *)lut);
-    uint32_t raddr[16];
-#pragma unroll
-    for (int j = 0; j < 16; ++j) raddr[j] = lut_addr;
-
-    // table build: this lane writes entries 4*bt .. 4*bt+3 of chunks bc and bc + 16
-    const int bc = lane >> 2, bt = lane & 3;
-    const float sg2 = (bt & 1) ? 1.f : -1.f, sg3 = (bt & 2) ? 1.f : -1.f;
-    uint2 xq0 = *reinterpret_cast<const uint2 *>(x + (size_t)g0 * 128 + 4 * bc);
-    uint2 xq1 = *reinterpret_cast<const uint2 *>(x + (size_t)g0 * 128 + 4 * (bc + 16));
-
-    // tile load: instruction i fetches row 8i + lane/8, group (lane%8) ^ ((row >> 1) & 7)
-    float sc[B];
-    auto issue = [&](int gb) {
-#pragma unroll
-        for (int i = 0; i < B; ++i) {
-            const int r = 8 * i + (lane >> 3);
-            const int gg = min(gb + ((lane & 7) ^ ((r >> 1) & 7)), g1 - 1);
-            const int rr = min(row0 + r, N - 1);
-            __builtin_amdgcn_global_load_lds((glb_void_t *)(wg + (size_t)rr * G + gg),
-                                             (lds_void_t *)(tile + i * 1024), 16, 0, 0);
-        }
-        if (vec_scales) {
-            // the batch's 8 scales of this row in one 16-byte load (K % 1024 == 0 keeps every
-            // row's scales and every batch start 16-byte aligned)
-            const u32x4 v = *reinterpret_cast<const u32x4 *>(srow + gb);
-#pragma unroll
-            for (int u = 0; u < B; ++u) sc[u] = f16_bits_to_f32((uint16_t)(v[u >> 1] >> (16 * (u & 1))));
-        } else {
-#pragma unroll
-            for (int u = 0; u < B; ++u) sc[u] = f16_bits_to_f32(srow[min(gb + u, g1 - 1)]);
-        }
-    };
-
-    float acc = 0.f;
-    issue(g0);
-    for (int gb = g0; gb < g1; gb += B) {
-        vm_wait<0>();                                   // tile and scales of this batch
-#pragma unroll
-        for (int u = 0; u < B; ++u) {
-            const int g = gb + u;
-            if (g >= g1) break;
-            // build the 32 tables of group g, then fetch the next group's x
-            const uint2 xc[2] = {xq0, xq1};
-            if (g + 1 < g1) {
-                xq0 = *reinterpret_cast<const uint2 *>(x + (size_t)(g + 1) * 128 + 4 * bc);
-                xq1 = *reinterpret_cast<const uint2 *>(x + (size_t)(g + 1) * 128 + 4 * (bc + 16));
-            }
-#pragma unroll
-            for (int hq = 0; hq < 2; ++hq) {
-                const half2_t p01 = as_half2(xc[hq].x), p23 = as_half2(xc[hq].y);
-                const float x0 = (float)p01[0], x1 = (float)p01[1];
-                const float base = fmaf(sg3, (float)p23[1], fmaf(sg2, (float)p23[0], -x0 - x1));
-                u32x4 e;
-                e[0] = __builtin_bit_cast(uint32_t, base);                                  // v = 4bt
-                e[1] = __builtin_bit_cast(uint32_t, fmaf(2.f, x0, base));                  // v = 4bt + 1
-                e[2] = __builtin_bit_cast(uint32_t, fmaf(2.f, x1, base));                  // v = 4bt + 2
-                e[3] = __builtin_bit_cast(uint32_t, fmaf(2.f, x1, fmaf(2.f, x0, base)));   // v = 4bt + 3
-                *reinterpret_cast<u32x4 *>(lut + 64 * (bc + 16 * hq) + 16 * bt) = e;
-            }
-            // this lane's row: 4 words x 8 nibbles, two words (16 reads) in flight at a time
-            const u32x4 q = *reinterpret_cast<const u32x4 *>(tile + 128 * lane + 16 * (u ^ ((lane >> 1) & 7)));
-            float a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;
-#pragma unroll
-            for (int i = 0; i < 4; i += 2) {
-                word_addrs(q[i], &raddr[0], mask_3c);          // in place: only bits 0..7 change
-                word_addrs(q[i + 1], &raddr[8], mask_3c);
-                float t[16];
-#pragma unroll
-                for (int j = 0; j < 16; ++j) t[j] = lds_f32(raddr[j], 64 * (8 * i + j));
-                a0 += (t[0] + t[1]) + (t[2] + t[3]);
-                a1 += (t[4] + t[5]) + (t[6] + t[7]);
-                a2 += (t[8] + t[9]) + (t[10] + t[11]);
-                a3 += (t[12] + t[13]) + (t[14] + t[15]);
-            }
-            acc = fmaf(sc[u], (a0 + a1) + (a2 + a3), acc);
-        }
-        lgkm_wait0();                                   // tile reads done before reuse
-        if (gb + B < g1) issue(gb + B);
-    }
-
-    if (nwaves == 1) {
-        if (row < N) y[row] = acc;
-        return;
-    }
-    float *red = reinterpret_cast<float *>(reinterpret_cast<char *>(lds) + nwaves * (kLutTileBytes + kLutBytes));
-    red[wave * 64 + lane] = acc;
-    __syncthreads();
-    if (wave == 0 && row < N) {
-        float t = red[lane];
-        for (int w = 1; w < nwaves; ++w) t += red[w * 64 + lane];
-        y[row] = t;
-    }
-}
 
 // 16-byte LDS store at addr, issued from asm: the compiler cannot tell it apart from the LDS
 // the in-flight direct global->LDS copies write, and would otherwise wait for every copy
@@ -604,25 +478,6 @@ hipError_t launch_lutp(const uint32_t *wbits, const uint16_t *scales, const uint
     return launch_kernel(fn, dim3(grid), dim3(64 * nwaves), args, lds, stream);
 }
 
-hipError_t launch_lut(const uint32_t *wbits, const uint16_t *scales, const uint16_t *x, float *y,
-                      int N, int K, hipStream_t stream)
-{
-    const int G = K / 128;
-    const int tiles = (N + 63) / 64;
-    constexpr size_t per_wave = kLutTileBytes + kLutBytes;
-    // Split K across the waves of a workgroup only until the grid has a wave per SIMD
-    // (1024 SIMDs): the LDS each wave needs makes more, smaller waves a net loss.
-    int slices = 1;
-    while (slices < 6 && (int64_t)tiles * slices < 1024 && slices * kLutBatch < G) ++slices;
-    int gps = (G + slices - 1) / slices;
-    gps = ((gps + kLutBatch - 1) / kLutBatch) * kLutBatch;
-    slices = (G + gps - 1) / gps;
-    const size_t lds = (size_t)slices * per_wave + (slices > 1 ? (size_t)slices * 64 * sizeof(float) : 0);
-    void *args[] = {&wbits, &scales, &x, &y, &N, &K, &gps};
-    return launch_kernel(reinterpret_cast<const void *>(&q1_gemv_lut_kernel), dim3(tiles), dim3(64 * slices),
-                         args, lds, stream);
-}
-
 #undef BONSAI_L4_XREAD8
 
 }  // namespace
@@ -632,16 +487,22 @@ hipError_t launch_q1_gemv(const uint32_t *wbits, const uint16_t *scales, const u
 {
     if (M >= 2 && M <= 8) return launch_gemv_mfma(false, wbits, scales, x, y, M, N, K, stream);
     if (M != 1) return hipErrorInvalidValue;
-    // small N: one tile per CU at most, and the wave slices of K fit one workgroup; 32-row
-    // tiles while they still fit, for twice the CUs
+    // The route follows measurements at K = 5120 (N = 1024 ... 248320) and K = 13824:
+    // - 32-row tiles while one round of 256 CUs holds them (twice the CUs of 64-row tiles);
+    // - 64-row tiles (one workgroup per CU, about 5 us a round) up to six rounds;
+    // - beyond, the persistent kernel: about 15 us up front for the tables of all of K on every
+    //   CU, then about 0.15 ns a row, so it overtakes near 100k rows;
+    // - K too long for any of their tables in LDS: the matrix-core kernel, which measured 9.6 us
+    //   against 15.7 for a table-lookup kernel that stages K in batches (N = 5120, K = 13824).
     const int G = K / 128;
-    if ((N + 31) / 32 <= 256 && (G + L4<32>::gpw - 1) / L4<32>::gpw <= L4<32>::max_waves)
-        return launch_lut4<32>(wbits, scales, x, y, N, K, stream);
-    if ((N + 63) / 64 <= 256 && (G + L4<64>::gpw - 1) / L4<64>::gpw <= L4<64>::max_waves)
-        return launch_lut4<64>(wbits, scales, x, y, N, K, stream);
-    // large N: persistent workgroups with the tables of all of K, when they fit the LDS
+    const bool fits32 = (G + L4<32>::gpw - 1) / L4<32>::gpw <= L4<32>::max_waves;
+    const bool fits64 = (G + L4<64>::gpw - 1) / L4<64>::gpw <= L4<64>::max_waves;
+    const int64_t tiles64 = ((int64_t)N + 63) / 64;
+    if (fits32 && ((int64_t)N + 31) / 32 <= 256) return launch_lut4<32>(wbits, scales, x, y, N, K, stream);
+    if (fits64 && tiles64 <= 6 * 256) return launch_lut4<64>(wbits, scales, x, y, N, K, stream);
     if (const int nw = lutp_waves(G)) return launch_lutp(wbits, scales, x, y, N, K, nw, stream);
-    return launch_lut(wbits, scales, x, y, N, K, stream);
+    if (fits64) return launch_lut4<64>(wbits, scales, x, y, N, K, stream);
+    return launch_gemv_mfma(false, wbits, scales, x, y, M, N, K, stream);
 }
 
 }  // namespace bonsai

@@ -149,10 +149,12 @@ EDGE = {
     "q1_gemv": [(1, 1, 128), (1, 63, 256), (1, 65, 384), (3, 1000, 1152), (8, 777, 2048), (5, 64, 128),
                 (2, 130, 131072), (1, 4097, 640),
                 # M = 1 around the kernel boundaries: 32-row tiles up to N = 8192, 64-row tiles up
-                # to 16384, then the persistent kernel (odd G, G not a multiple of 4, ragged N, the
-                # most groups whose tables fit), and past that K the batched kernel
+                # to six rounds of 256 CUs (N = 98304, and the most groups whose tables fit), then
+                # the persistent kernel (odd G, ragged N), and K too long for the tables on the
+                # matrix-core kernel (G even and odd)
                 (1, 8192, 640), (1, 8193, 640), (1, 16384, 384), (1, 16385, 1152), (1, 20000, 640),
-                (1, 40000, 256), (1, 17000, 6144), (1, 16500, 8192)],
+                (1, 40000, 256), (1, 17000, 6144), (1, 98304, 384), (1, 98305, 384), (1, 100003, 640),
+                (1, 16500, 8192), (1, 5000, 7808)],
     "q2t_gemv": [(1, 1, 128), (1, 63, 256), (2, 65, 384), (8, 1000, 1152), (7, 777, 2048),
                  (1, 130, 131072), (4, 4097, 640)],
     # M <= 80 runs the small-M kernel in 16-row blocks of x (ragged last block), above it the tiles
