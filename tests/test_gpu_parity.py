@@ -4,7 +4,6 @@ Float results must satisfy |y - y_ref| <= 1e-3 * sum_k |w x| + 1e-6 elementwise.
 (one-hot x, integer-valued x with power-of-two scales) must match bit for bit, since every
 partial sum is then exactly representable in float32 whatever the summation order.
 """
-import ctypes
 
 import numpy as np
 import pytest

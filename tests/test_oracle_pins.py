@@ -1,7 +1,6 @@
 """The oracle against its pins, and the pins against planted mistakes in the oracle."""
 import json
 import os
-import shutil
 import subprocess
 import sys
 from pathlib import Path
