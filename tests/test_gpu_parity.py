@@ -278,7 +278,10 @@ def _t5(codes, s, x):
 
 
 T5_SHAPES = [(1, 256, 640), (1, 300, 384), (2, 1000, 1152), (8, 2000, 1024), (16, 777, 768),
-             (17, 500, 1280), (3, 130, 13824), (1, 5, 128), (40, 96, 896)]
+             (17, 500, 1280), (3, 130, 13824), (1, 5, 128), (40, 96, 896),
+             # the largest K the library accepts (820 superblocks, several slices per wave), and
+             # many 16-row blocks of x
+             (1, 40, 131072), (5, 33, 131072), (200, 70, 640)]
 
 
 @pytest.mark.parametrize("M,N,K", T5_SHAPES)
@@ -375,7 +378,8 @@ def _affine_magnitude(orc, w, a, b, x, m_idx=None, n_idx=None):
 
 
 AFFINE_SHAPES = [(1, 256, 512), (1, 300, 640), (2, 1000, 1152), (8, 2000, 1024), (16, 777, 640),
-                 (17, 500, 1152), (33, 130, 384), (80, 300, 896), (1, 5, 128)]
+                 (17, 500, 1152), (33, 130, 384), (80, 300, 896), (1, 5, 128),
+                 (1, 40, 131072), (6, 33, 131072), (200, 70, 640)]
 
 
 @pytest.mark.parametrize("M,N,K", AFFINE_SHAPES)
