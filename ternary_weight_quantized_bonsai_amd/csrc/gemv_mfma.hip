@@ -433,6 +433,7 @@ hipError_t launch_q1a_matmul(const uint32_t *wbits, const uint16_t *scales, cons
                              const uint16_t *x, float *y, int M, int N, int K, hipStream_t stream)
 {
     if (M < 1) return hipErrorInvalidValue;
+    if (M == 1 && q1a_lut_fits(N, K)) return launch_q1a_lut(wbits, scales, biases, x, y, N, K, stream);
     return launch_sm<false, true>(wbits, scales, biases, x, y, M, N, K, stream);
 }
 

@@ -18,6 +18,10 @@ hipError_t launch_q2t_gemm(const uint32_t *wcodes, const uint16_t *scales, const
 // entry points use it for ternary M = 1..8 and binary M = 2..8, the GEMMs for small M).
 hipError_t launch_gemv_mfma(bool ternary, const uint32_t *codes, const uint16_t *scales, const uint16_t *x,
                             float *y, int M, int N, int K, hipStream_t stream);
+// Affine 1-bit weights at M = 1 on the table kernels, where their tables fit (q1a_lut_fits).
+bool q1a_lut_fits(int N, int K);
+hipError_t launch_q1a_lut(const uint32_t *wbits, const uint16_t *scales, const uint16_t *biases, const uint16_t *x,
+                          float *y, int N, int K, hipStream_t stream);
 // Affine 1-bit weights (binary words with a binary16 scale and bias per group), any M >= 1.
 hipError_t launch_q1a_matmul(const uint32_t *wbits, const uint16_t *scales, const uint16_t *biases,
                              const uint16_t *x, float *y, int M, int N, int K, hipStream_t stream);

@@ -89,7 +89,12 @@ __device__ __forceinline__ void lds_store_b128(uint32_t addr, u32x4 v)
 // its tables while the tile is still on its way from HBM.  (Read through the compiler, x would
 // wait for every copy: it cannot tell the copies' LDS writes from the table writes, and orders
 // loads of mixed kinds by waiting for all of them.)
-template <int ROWS>
+// AFF: affine 1-bit weights (MLX's form, a scale a and a bias b per group, weight a q + b for
+// the bit q; "1-bit Bonsai 27B" model card, "MLX packaging").  With D the group's table sum of
+// +-x and X the group's plain sum of x, the group contributes a sum(q x) + b X =
+// (a / 2) D + (a / 2 + b) X.  X is the same for every row: each wave adds up its groups' x from
+// the quads its lanes already hold (one lane of the four that hold a quad), across the wave.
+template <int ROWS, bool AFF = false>
 struct L4 {
     static constexpr int lpr = 64 / ROWS;               // lanes per row
     static constexpr int gpw = 4 * lpr;                 // groups per wave
@@ -97,8 +102,9 @@ struct L4 {
     static constexpr int lut = gpw * kLutBytes;         // tables; x is staged in the first gpw * 256 B
     static constexpr int scales = ROWS * gpw * 4;       // 1 KB: one dword per (row, group) at most;
                                                         // the wave's partial sums once the lookups end
-    static constexpr int wave = tile + lut + scales;    // 13 KB (ROWS 64) or 21 KB (ROWS 32)
-    static constexpr int max_waves = (160 * 1024) / wave;   // 12 or 7
+                                                        // (AFF: the biases follow, laid out alike)
+    static constexpr int wave = tile + lut + (AFF ? 2 : 1) * scales;   // 13 / 14 KB (ROWS 64), 21 / 22 (32)
+    static constexpr int max_waves = (160 * 1024) / wave;   // 12 / 11 or 7
     static constexpr int rows_per_copy = 1024 / (gpw * 16);  // tile rows per 1 KB copy
     // the 16-byte cell of (row r, group u) sits at gpw * 16 * r + 16 (u ^ swz(r))
     static __device__ __forceinline__ int swz(int r) { return (r / (16 / gpw)) & (gpw - 1); }
@@ -121,13 +127,13 @@ __device__ __forceinline__ void compiler_fence() { asm volatile("" : : : "memory
                  : "memory")
 
 // PAIRS: G is even, so the scales of groups 2p, 2p + 1 of a row are one aligned dword.
-template <int ROWS, bool PAIRS>
-__global__ __launch_bounds__(L4<ROWS>::max_waves * 64) void q1_gemv_lut4_kernel(const uint32_t *__restrict__ wbits,
-                                                                                const uint16_t *__restrict__ scales,
-                                                                                const uint16_t *__restrict__ x,
-                                                                                float *__restrict__ y, int N, int K)
+// AFF: affine weights (biases used only then).
+template <int ROWS, bool PAIRS, bool AFF>
+__global__ __launch_bounds__((L4<ROWS, AFF>::max_waves * 64)) void q1_gemv_lut4_kernel(
+    const uint32_t *__restrict__ wbits, const uint16_t *__restrict__ scales, const uint16_t *__restrict__ biases,
+    const uint16_t *__restrict__ x, float *__restrict__ y, int N, int K)
 {
-    using L = L4<ROWS>;
+    using L = L4<ROWS, AFF>;
     extern __shared__ u32x4 lds[];
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -139,6 +145,7 @@ __global__ __launch_bounds__(L4<ROWS>::max_waves * 64) void q1_gemv_lut4_kernel(
     char *const tile = reinterpret_cast<char *>(lds) + wave * L::wave;
     char *const lut = tile + L::tile;
     char *const sc = lut + L::lut;
+    char *const bc = sc + L::scales;                         // biases (AFF only)
     float *const part = reinterpret_cast<float *>(sc);
 
     // x: copy j, lane l brings x[128 g0 + 512 j + 8 l .. + 7] to lut + 1 KB j + 16 l (clamped
@@ -161,29 +168,58 @@ __global__ __launch_bounds__(L4<ROWS>::max_waves * 64) void q1_gemv_lut4_kernel(
     // scales: element d = 64 k + lane of copy k is (row d % ROWS, pair d / ROWS) for PAIRS
     // (4 bytes), else (row d % ROWS, group d / ROWS) (2 bytes, the low half of its dword); it
     // lands in the dword at sc + 4 d
+    // (AFF: the biases likewise, to bc)
     constexpr int kScaleCopies = PAIRS ? 2 : 4;
 #pragma unroll
-    for (int k = 0; k < kScaleCopies; ++k) {
-        const int d = 64 * k + lane;
-        const size_t rbase = (size_t)min(n0 + d % ROWS, N - 1) * G;
-        if constexpr (PAIRS)
-            __builtin_amdgcn_global_load_lds((glb_void_t *)(scales + rbase + min(g0 + 2 * (d / ROWS), G - 2)),
-                                             (lds_void_t *)(sc + 256 * k), 4, 0, 0);
-        else
-            __builtin_amdgcn_global_load_lds((glb_void_t *)(scales + rbase + min(g0 + d / ROWS, gl)),
-                                             (lds_void_t *)(sc + 256 * k), 2, 0, 0);
+    for (int which = 0; which < (AFF ? 2 : 1); ++which) {
+        const uint16_t *const src = which ? biases : scales;
+        char *const dst = which ? bc : sc;
+#pragma unroll
+        for (int k = 0; k < kScaleCopies; ++k) {
+            const int d = 64 * k + lane;
+            const size_t rbase = (size_t)min(n0 + d % ROWS, N - 1) * G;
+            if constexpr (PAIRS)
+                __builtin_amdgcn_global_load_lds((glb_void_t *)(src + rbase + min(g0 + 2 * (d / ROWS), G - 2)),
+                                                 (lds_void_t *)(dst + 256 * k), 4, 0, 0);
+            else
+                __builtin_amdgcn_global_load_lds((glb_void_t *)(src + rbase + min(g0 + d / ROWS, gl)),
+                                                 (lds_void_t *)(dst + 256 * k), 2, 0, 0);
+        }
     }
     compiler_fence();
 
     // x quads: quad k of this lane is x[128 g0 + 64 k + 4 (lane / 4) .. + 3], at
-    // lut + 128 k + 8 (lane / 4); the first block waits until at most the tile and scale
-    // copies are in flight
+    // lut + 128 k + 8 (lane / 4); the first block waits until at most the tile, scale (and
+    // bias) copies are in flight
     constexpr int kQuads = 8 * L::lpr;
     uint2 xq[kQuads];
     const uint32_t xa = (uint32_t)(uintptr_t)((lds_char_t *)lut) + 8 * (lane >> 2);
-    if constexpr (PAIRS) BONSAI_L4_XREAD8("s_waitcnt vmcnt(6)\n\t", xq, xa);
-    else BONSAI_L4_XREAD8("s_waitcnt vmcnt(8)\n\t", xq, xa);
+    if constexpr (PAIRS && !AFF) BONSAI_L4_XREAD8("s_waitcnt vmcnt(6)\n\t", xq, xa);
+    else if constexpr (PAIRS || !AFF) BONSAI_L4_XREAD8("s_waitcnt vmcnt(8)\n\t", xq, xa);
+    else BONSAI_L4_XREAD8("s_waitcnt vmcnt(12)\n\t", xq, xa);
     if constexpr (kQuads == 16) BONSAI_L4_XREAD8("", xq + 8, xa + 1024);
+
+    // AFF: X of the wave's group u is the sum of quads 2u, 2u + 1 over the 16 values of lane / 4;
+    // lanes with lane % 4 == 0 contribute, and a fixed butterfly adds them across the wave.
+    // Groups 0..3 and 4..7 are kept apart (xs0, xs1): a select between one array's elements by
+    // the lane's h would become a dynamically indexed, scratch-resident array.
+    float xs0[4] = {0.f, 0.f, 0.f, 0.f}, xs1[4] = {0.f, 0.f, 0.f, 0.f};
+    if constexpr (AFF) {
+#pragma unroll
+        for (int u = 0; u < L::gpw; ++u) {
+            float t = 0.f;
+#pragma unroll
+            for (int k = 2 * u; k < 2 * u + 2; ++k) {
+                const half2_t p01 = as_half2(xq[k].x), p23 = as_half2(xq[k].y);
+                t += ((float)p01[0] + (float)p01[1]) + ((float)p23[0] + (float)p23[1]);
+            }
+            t = (lane & 3) == 0 ? t : 0.f;
+#pragma unroll
+            for (int off = 32; off >= 1; off >>= 1) t += __shfl_xor(t, off);
+            if (u < 4) xs0[u] = t;
+            else xs1[u & 3] = t;
+        }
+    }
 
     // tables: lane builds quads e = lane + 64 k of the wave's groups (group e / 128, chunk
     // (e / 4) % 32, entries 4 bt .. 4 bt + 3); they overwrite the staged x, which this wave
@@ -207,11 +243,15 @@ __global__ __launch_bounds__(L4<ROWS>::max_waves * 64) void q1_gemv_lut4_kernel(
     vm_wait<0>();                                   // the tile and the scales landed
     lgkm_wait0();                                   // this wave's tables are written
 
-    // this lane's scales (row r, groups 4 h .. 4 h + 3 of the wave's), before the lookups
-    uint32_t sw[PAIRS ? 2 : 4];
+    // this lane's scales (and biases) (row r, groups 4 h .. 4 h + 3 of the wave's), before the
+    // lookups
+    uint32_t sw[PAIRS ? 2 : 4], bw[AFF ? (PAIRS ? 2 : 4) : 1];
 #pragma unroll
-    for (int k = 0; k < (PAIRS ? 2 : 4); ++k)
-        sw[k] = *reinterpret_cast<const uint32_t *>(sc + 4 * ((PAIRS ? 2 * h : 4 * h) + k) * ROWS + 4 * r);
+    for (int k = 0; k < (PAIRS ? 2 : 4); ++k) {
+        const int off = 4 * ((PAIRS ? 2 * h : 4 * h) + k) * ROWS + 4 * r;
+        sw[k] = *reinterpret_cast<const uint32_t *>(sc + off);
+        if constexpr (AFF) bw[k] = *reinterpret_cast<const uint32_t *>(bc + off);
+    }
 
     const uint32_t mask_3c = __builtin_amdgcn_readfirstlane(0x3Cu);
     // the tables of this lane's 4 groups start at lut + 8 KB h (256-aligned)
@@ -239,8 +279,18 @@ __global__ __launch_bounds__(L4<ROWS>::max_waves * 64) void q1_gemv_lut4_kernel(
         }
         const uint16_t sbits = (uint16_t)(PAIRS ? sw[u >> 1] >> (16 * (u & 1)) : sw[u]);
         // groups past K (the last wave's slice may be short) count with scale 0
-        const float s = (g0 + ug < g1) ? f16_bits_to_f32(sbits) : 0.f;
-        acc = fmaf(s, (a0 + a1) + (a2 + a3), acc);
+        const bool live = g0 + ug < g1;
+        if constexpr (AFF) {
+            const uint16_t bbits = (uint16_t)(PAIRS ? bw[u >> 1] >> (16 * (u & 1)) : bw[u]);
+            const float ha = live ? 0.5f * f16_bits_to_f32(sbits) : 0.f;          // a / 2
+            const float hb = live ? ha + f16_bits_to_f32(bbits) : 0.f;           // a / 2 + b
+            const float xu = (L::gpw == 8 && h) ? xs1[u] : xs0[u];
+            acc = fmaf(ha, (a0 + a1) + (a2 + a3), acc);
+            acc = fmaf(hb, xu, acc);
+        } else {
+            const float s = live ? f16_bits_to_f32(sbits) : 0.f;
+            acc = fmaf(s, (a0 + a1) + (a2 + a3), acc);
+        }
     }
     part[lane] = acc;                               // the scales were read before the lookups
     __syncthreads();
@@ -255,27 +305,27 @@ __global__ __launch_bounds__(L4<ROWS>::max_waves * 64) void q1_gemv_lut4_kernel(
     }
 }
 
-template <int ROWS>
-hipError_t launch_lut4(const uint32_t *wbits, const uint16_t *scales, const uint16_t *x, float *y,
-                       int N, int K, hipStream_t stream)
+template <int ROWS, bool AFF>
+hipError_t launch_lut4(const uint32_t *wbits, const uint16_t *scales, const uint16_t *biases, const uint16_t *x,
+                       float *y, int N, int K, hipStream_t stream)
 {
-    using L = L4<ROWS>;
+    using L = L4<ROWS, AFF>;
     const int G = K / 128;
     const int tiles = (N + ROWS - 1) / ROWS;
     const int waves = (G + L::gpw - 1) / L::gpw;
     const size_t lds = (size_t)waves * L::wave;
     const bool pairs = (G % 2) == 0;                // a row's scale pairs are then dword aligned
-    const void *fn = pairs ? reinterpret_cast<const void *>(&q1_gemv_lut4_kernel<ROWS, true>)
-                           : reinterpret_cast<const void *>(&q1_gemv_lut4_kernel<ROWS, false>);
+    const void *fn = pairs ? reinterpret_cast<const void *>(&q1_gemv_lut4_kernel<ROWS, true, AFF>)
+                           : reinterpret_cast<const void *>(&q1_gemv_lut4_kernel<ROWS, false, AFF>);
     static const bool attrs_set = [] {
         const int most = L::max_waves * L::wave;
-        return hipFuncSetAttribute(reinterpret_cast<const void *>(&q1_gemv_lut4_kernel<ROWS, true>),
+        return hipFuncSetAttribute(reinterpret_cast<const void *>(&q1_gemv_lut4_kernel<ROWS, true, AFF>),
                                    hipFuncAttributeMaxDynamicSharedMemorySize, most) == hipSuccess &&
-               hipFuncSetAttribute(reinterpret_cast<const void *>(&q1_gemv_lut4_kernel<ROWS, false>),
+               hipFuncSetAttribute(reinterpret_cast<const void *>(&q1_gemv_lut4_kernel<ROWS, false, AFF>),
                                    hipFuncAttributeMaxDynamicSharedMemorySize, most) == hipSuccess;
     }();
     if (!attrs_set) return hipErrorInvalidValue;
-    void *args[] = {&wbits, &scales, &x, &y, &N, &K};
+    void *args[] = {&wbits, &scales, &biases, &x, &y, &N, &K};
     return launch_kernel(fn, dim3(tiles), dim3(64 * waves), args, lds, stream);
 }
 
@@ -482,6 +532,26 @@ hipError_t launch_lutp(const uint32_t *wbits, const uint16_t *scales, const uint
 
 }  // namespace
 
+// Affine 1-bit weights, one row of x, on the table kernels: the binary routes of
+// launch_q1_gemv up to six rounds of 64-row tiles (the persistent kernel has no affine form).
+bool q1a_lut_fits(int N, int K)
+{
+    const int G = K / 128;
+    const bool fits32 = (G + L4<32, true>::gpw - 1) / L4<32, true>::gpw <= L4<32, true>::max_waves;
+    const bool fits64 = (G + L4<64, true>::gpw - 1) / L4<64, true>::gpw <= L4<64, true>::max_waves;
+    return (fits32 && ((int64_t)N + 31) / 32 <= 256) || (fits64 && ((int64_t)N + 63) / 64 <= 6 * 256);
+}
+
+hipError_t launch_q1a_lut(const uint32_t *wbits, const uint16_t *scales, const uint16_t *biases, const uint16_t *x,
+                          float *y, int N, int K, hipStream_t stream)
+{
+    const int G = K / 128;
+    const bool fits32 = (G + L4<32, true>::gpw - 1) / L4<32, true>::gpw <= L4<32, true>::max_waves;
+    if (fits32 && ((int64_t)N + 31) / 32 <= 256) return launch_lut4<32, true>(wbits, scales, biases, x, y, N, K, stream);
+    if (!q1a_lut_fits(N, K)) return hipErrorInvalidValue;
+    return launch_lut4<64, true>(wbits, scales, biases, x, y, N, K, stream);
+}
+
 hipError_t launch_q1_gemv(const uint32_t *wbits, const uint16_t *scales, const uint16_t *x, float *y,
                           int M, int N, int K, hipStream_t stream)
 {
@@ -498,10 +568,10 @@ hipError_t launch_q1_gemv(const uint32_t *wbits, const uint16_t *scales, const u
     const bool fits32 = (G + L4<32>::gpw - 1) / L4<32>::gpw <= L4<32>::max_waves;
     const bool fits64 = (G + L4<64>::gpw - 1) / L4<64>::gpw <= L4<64>::max_waves;
     const int64_t tiles64 = ((int64_t)N + 63) / 64;
-    if (fits32 && ((int64_t)N + 31) / 32 <= 256) return launch_lut4<32>(wbits, scales, x, y, N, K, stream);
-    if (fits64 && tiles64 <= 6 * 256) return launch_lut4<64>(wbits, scales, x, y, N, K, stream);
+    if (fits32 && ((int64_t)N + 31) / 32 <= 256) return launch_lut4<32, false>(wbits, scales, nullptr, x, y, N, K, stream);
+    if (fits64 && tiles64 <= 6 * 256) return launch_lut4<64, false>(wbits, scales, nullptr, x, y, N, K, stream);
     if (const int nw = lutp_waves(G)) return launch_lutp(wbits, scales, x, y, N, K, nw, stream);
-    if (fits64) return launch_lut4<64>(wbits, scales, x, y, N, K, stream);
+    if (fits64) return launch_lut4<64, false>(wbits, scales, nullptr, x, y, N, K, stream);
     return launch_gemv_mfma(false, wbits, scales, x, y, M, N, K, stream);
 }
 

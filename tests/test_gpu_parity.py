@@ -379,7 +379,9 @@ def _affine_magnitude(orc, w, a, b, x, m_idx=None, n_idx=None):
 
 AFFINE_SHAPES = [(1, 256, 512), (1, 300, 640), (2, 1000, 1152), (8, 2000, 1024), (16, 777, 640),
                  (17, 500, 1152), (33, 130, 384), (80, 300, 896), (1, 5, 128),
-                 (1, 40, 131072), (6, 33, 131072), (200, 70, 640)]
+                 (1, 40, 131072), (6, 33, 131072), (200, 70, 640),
+                 # one row of x on the table kernels: 64-row tiles (N > 8192), G even and odd
+                 (1, 9000, 1024), (1, 9000, 1152), (1, 20000, 640)]
 
 
 @pytest.mark.parametrize("M,N,K", AFFINE_SHAPES)
@@ -411,7 +413,7 @@ def test_affine_bonsai_packing_matches_binary(M, N, K, orc):
     assert_close(y, yref, 3 * mag, "q1a as binary")
 
 
-@pytest.mark.parametrize("M,N,K", [(1, 300, 640), (7, 260, 1024), (20, 129, 384)])
+@pytest.mark.parametrize("M,N,K", [(1, 300, 640), (1, 9000, 1024), (7, 260, 1024), (20, 129, 384)])
 def test_affine_integer_inputs_bit_exact(M, N, K, orc):
     """Small integer x, scales and biases: every partial sum is exact in float32, so the kernel
     must equal the exact result bit for bit."""
