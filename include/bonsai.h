@@ -117,6 +117,12 @@ bonsai_status bonsai_t5_matmul(const uint8_t *codes, const uint16_t *scales, con
                                float *y, int64_t M, int64_t N, int64_t K, void *hip_stream);
 bonsai_status bonsai_t5_pack(const int8_t *trits, int64_t N, int64_t K, uint8_t *codes);
 bonsai_status bonsai_t5_unpack(const uint8_t *codes, int64_t N, int64_t K, int8_t *trits);
+/* Direct host conversions between the 2-bit codes and the base-3 layout, a row at a time with no
+ * int8 intermediate (the 2-bit storage of today's release to native density, and back).  K must
+ * be a multiple of 16.  q2t_to_t5 rejects field value 2, t5_to_q2t reserved bytes and nonzero
+ * padding (BONSAI_ERR_CODE); on an error the output is unspecified. */
+bonsai_status bonsai_q2t_to_t5(const uint32_t *wcodes, int64_t N, int64_t K, uint8_t *codes);
+bonsai_status bonsai_t5_to_q2t(const uint8_t *codes, int64_t N, int64_t K, uint32_t *wcodes);
 
 /* Affine 1-bit matmul: y[M][N] = x[M][K] * W^T with W[n][k] = a * q + b, q the bit of W[n][k] in
  * the binary layout above and (a, b) = (mlx_scales, biases)[n][k / 128], binary16 [N][K/128]

@@ -41,7 +41,7 @@ for _name in ("bonsai_q1_pack", "bonsai_q1_unpack", "bonsai_q2t_pack", "bonsai_q
     _f.restype = ctypes.c_int
 _lib.bonsai_t5_matmul.argtypes = [_vp, _vp, _vp, _vp, _c_i64, _c_i64, _c_i64, _vp]
 _lib.bonsai_t5_matmul.restype = ctypes.c_int
-for _name in ("bonsai_t5_pack", "bonsai_t5_unpack"):
+for _name in ("bonsai_t5_pack", "bonsai_t5_unpack", "bonsai_q2t_to_t5", "bonsai_t5_to_q2t"):
     _f = getattr(_lib, _name)
     _f.argtypes = [_vp, _c_i64, _c_i64, _vp]
     _f.restype = ctypes.c_int
@@ -259,6 +259,28 @@ def t5_unpack(codes: np.ndarray, K: int) -> np.ndarray:
         raise ValueError("codes must be [N, 32 ceil(K/160)]")
     out = np.empty((N, K), dtype=np.int8)
     _check("bonsai_t5_unpack", _lib.bonsai_t5_unpack(c.ctypes.data, N, K, out.ctypes.data))
+    return out
+
+
+def q2t_to_t5(wcodes: np.ndarray, K: int) -> np.ndarray:
+    """2-bit ternary words [N, K/16] -> base-3 bytes [N, 32 ceil(K/160)] (bonsai_q2t_to_t5)."""
+    w = _host(wcodes, np.uint32)
+    N = w.shape[0]
+    if w.shape[1] * 16 != K:
+        raise ValueError("wcodes must be [N, K/16]")
+    out = np.zeros((N, t5_row_bytes(K)), dtype=np.uint8)
+    _check("bonsai_q2t_to_t5", _lib.bonsai_q2t_to_t5(w.ctypes.data, N, K, out.ctypes.data))
+    return out
+
+
+def t5_to_q2t(codes: np.ndarray, K: int) -> np.ndarray:
+    """Base-3 bytes [N, 32 ceil(K/160)] -> 2-bit ternary words [N, K/16] (bonsai_t5_to_q2t)."""
+    c = _host(codes, np.uint8)
+    N = c.shape[0]
+    if c.shape[1] != t5_row_bytes(K) or K % 16:
+        raise ValueError("codes must be [N, 32 ceil(K/160)] and K a multiple of 16")
+    out = np.empty((N, K // 16), dtype=np.uint32)
+    _check("bonsai_t5_to_q2t", _lib.bonsai_t5_to_q2t(c.ctypes.data, N, K, out.ctypes.data))
     return out
 
 

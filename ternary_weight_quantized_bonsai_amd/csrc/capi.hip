@@ -186,6 +186,57 @@ bonsai_status bonsai_t5_unpack(const uint8_t *codes, int64_t N, int64_t K, int8_
     return BONSAI_OK;
 }
 
+bonsai_status bonsai_q2t_to_t5(const uint32_t *wcodes, int64_t N, int64_t K, uint8_t *codes)
+{
+    if (N < 0 || K < 0 || K % 16 != 0) return BONSAI_ERR_SHAPE;
+    if (N == 0 || K == 0) return BONSAI_OK;
+    if (!wcodes || !codes) return BONSAI_ERR_NULL;
+    const int64_t sb = (K + 159) / 160;
+    for (int64_t n = 0; n < N; ++n) {
+        const uint32_t *row = wcodes + n * (K / 16);
+        for (int64_t b = 0; b < sb; ++b)
+            for (int c = 0; c < 32; ++c) {
+                unsigned v = 0, place = 1;
+                for (int i = 0; i < 5; ++i, place *= 3) {
+                    const int64_t k = 160 * b + c + 32 * i;
+                    if (k >= K) continue;
+                    const unsigned f = (row[k / 16] >> (2 * (k % 16))) & 3u;
+                    if (f == 2) return BONSAI_ERR_CODE;
+                    v += (f == 0 ? 0u : f == 1 ? 1u : 2u) * place;   // digit = w mod 3
+                }
+                codes[n * 32 * sb + 32 * b + c] = (uint8_t)v;
+            }
+    }
+    return BONSAI_OK;
+}
+
+bonsai_status bonsai_t5_to_q2t(const uint8_t *codes, int64_t N, int64_t K, uint32_t *wcodes)
+{
+    if (N < 0 || K < 0 || K % 16 != 0) return BONSAI_ERR_SHAPE;
+    if (N == 0 || K == 0) return BONSAI_OK;
+    if (!wcodes || !codes) return BONSAI_ERR_NULL;
+    const int64_t sb = (K + 159) / 160;
+    for (int64_t n = 0; n < N; ++n) {
+        uint32_t *row = wcodes + n * (K / 16);
+        for (int64_t w = 0; w < K / 16; ++w) row[w] = 0;
+        for (int64_t b = 0; b < sb; ++b)
+            for (int c = 0; c < 32; ++c) {
+                unsigned v = codes[n * 32 * sb + 32 * b + c];
+                if (v >= 243) return BONSAI_ERR_CODE;
+                for (int i = 0; i < 5; ++i, v /= 3) {
+                    const int64_t k = 160 * b + c + 32 * i;
+                    const unsigned d = v % 3;
+                    if (k >= K) {
+                        if (d != 0) return BONSAI_ERR_CODE;      // padding must hold zero weights
+                        continue;
+                    }
+                    row[k / 16] |= (d == 0 ? 0u : d == 1 ? 1u : 3u) << (2 * (k % 16));
+                }
+            }
+    }
+    return BONSAI_OK;
+}
+
 bonsai_status bonsai_q1_to_affine(const uint16_t *scales, int64_t n_groups, uint16_t *mlx_scales,
                                   uint16_t *mlx_biases)
 {

@@ -182,6 +182,29 @@ def test_t5_unpack_rejects_reserved_and_padding():
     assert e.value.status == bonsai.ERR_VALUE
 
 
+def test_q2t_t5_direct_conversions():
+    """The direct conversions agree with unpack-then-pack both ways, and refuse what the
+    packers and unpackers refuse."""
+    import synth
+    for N, K in ((3, 640), (2, 1152), (5, 384), (1, 16), (2, 13824)):
+        t = synth.trits_i8(N, K, 9, f"abi/conv/{K}")
+        w2 = bonsai.q2t_pack(t)
+        c5 = bonsai.t5_pack(t)
+        assert np.array_equal(bonsai.q2t_to_t5(w2, K), c5)
+        assert np.array_equal(bonsai.t5_to_q2t(c5, K), w2)
+    bad = bonsai.q2t_pack(np.zeros((1, 160), np.int8))
+    bad[0, 3] |= np.uint32(2 << 6)                  # field value 2
+    with pytest.raises(bonsai.BonsaiError):
+        bonsai.q2t_to_t5(bad, 160)
+    c = bonsai.t5_pack(np.zeros((1, 176), np.int8))  # K = 176: superblock 1 holds k 160..175
+    c[0, 32 + 20] = 3                                # digit 1 of byte 20: k = 160 + 20 + 32 >= K
+    with pytest.raises(bonsai.BonsaiError):
+        bonsai.t5_to_q2t(c, 176)
+    c[0, 32 + 20] = 250
+    with pytest.raises(bonsai.BonsaiError):
+        bonsai.t5_to_q2t(c, 176)
+
+
 def test_t5_matmul_validation():
     f = bonsai.raw().bonsai_t5_matmul
     p = FAKE
