@@ -76,12 +76,14 @@ __device__ __forceinline__ void lds_store_b128(uint32_t addr, u32x4 v)
     asm volatile("ds_write_b128 %0, %1" : : "v"(addr), "v"(v) : "memory");
 }
 
-// Small N (at most 256 row tiles, one per CU): one tile of ROWS = 64 or 32 rows per
-// workgroup.  A wave owns GPW = 4 * 64 / ROWS consecutive groups of the tile's rows: lane l
-// takes row l % ROWS and the 4 groups 4 (l / ROWS) .. + 3 of the wave's, so every wave has a
-// single 4 KB tile copy and 128 lookups per lane after it lands, whatever ROWS.  32-row tiles
-// spread a small N over twice the CUs, at the price of tables for twice the groups per wave.
-// The waves' partial sums meet in LDS and are added in a fixed order.
+// Up to mid N: one tile of ROWS = 64 or 32 rows per workgroup.  A wave owns GPW = GPL * 64 / ROWS
+// consecutive groups of the tile's rows: lane l takes row l % ROWS and the GPL groups
+// GPL (l / ROWS) .. + GPL - 1 of the wave's.  With GPL = 4 every wave has a single 4 KB tile
+// copy and 128 lookups per lane after it lands, whatever ROWS; 32-row tiles spread a small N
+// over twice the CUs, at the price of tables for twice the groups per wave.  GPL = 2 (32-row
+// tiles) halves each wave's share, so a workgroup has twice the waves and spreads them more
+// evenly over the CU's four SIMDs (10 waves go 3-3-2-2, where 5 went 2-1-1-1).  The waves'
+// partial sums meet in LDS and are added in a fixed order.
 //
 // Everything a wave needs reaches its LDS by direct global->LDS copies, issued in this order:
 // its x values, the weight tile, the scales.  Copies complete in issue order, so waiting until
@@ -94,11 +96,15 @@ __device__ __forceinline__ void lds_store_b128(uint32_t addr, u32x4 v)
 // +-x and X the group's plain sum of x, the group contributes a sum(q x) + b X =
 // (a / 2) D + (a / 2 + b) X.  X is the same for every row: each wave adds up its groups' x from
 // the quads its lanes already hold (one lane of the four that hold a quad), across the wave.
-template <int ROWS, bool AFF = false>
+// GPL: groups per lane (4, or 2 for 32-row tiles: twice the waves, each half the work, so that
+// the waves spread more evenly over a CU's four SIMDs).
+template <int ROWS, bool AFF = false, int GPL = 4>
 struct L4 {
     static constexpr int lpr = 64 / ROWS;               // lanes per row
-    static constexpr int gpw = 4 * lpr;                 // groups per wave
-    static constexpr int tile = ROWS * gpw * 16;        // 4 KB of cells
+    static constexpr int gpw = GPL * lpr;               // groups per wave
+    static_assert(gpw >= 4 && gpw <= 8, "a wave's x (gpw * 256 B) is staged by whole 1 KB copies");
+    static_assert(!AFF || GPL == 4, "the affine group sums assume four groups per lane");
+    static constexpr int tile = ROWS * gpw * 16;        // 4 KB of cells (2 KB at GPL 2)
     static constexpr int lut = gpw * kLutBytes;         // tables; x is staged in the first gpw * 256 B
     static constexpr int scales = ROWS * gpw * 4;       // 1 KB: one dword per (row, group) at most;
                                                         // the wave's partial sums once the lookups end
@@ -127,20 +133,20 @@ __device__ __forceinline__ void compiler_fence() { asm volatile("" : : : "memory
                  : "memory")
 
 // PAIRS: G is even, so the scales of groups 2p, 2p + 1 of a row are one aligned dword.
-// AFF: affine weights (biases used only then).
-template <int ROWS, bool PAIRS, bool AFF>
-__global__ __launch_bounds__((L4<ROWS, AFF>::max_waves * 64)) void q1_gemv_lut4_kernel(
+// AFF: affine weights (biases used only then).  GPL: groups per lane (see L4).
+template <int ROWS, bool PAIRS, bool AFF, int GPL>
+__global__ __launch_bounds__((L4<ROWS, AFF, GPL>::max_waves * 64)) void q1_gemv_lut4_kernel(
     const uint32_t *__restrict__ wbits, const uint16_t *__restrict__ scales, const uint16_t *__restrict__ biases,
     const uint16_t *__restrict__ x, float *__restrict__ y, int N, int K)
 {
-    using L = L4<ROWS, AFF>;
+    using L = L4<ROWS, AFF, GPL>;
     extern __shared__ u32x4 lds[];
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int nwaves = blockDim.x >> 6;
     const int G = K >> 7;
     const int g0 = wave * L::gpw, g1 = min(G, g0 + L::gpw), gl = g1 - 1;
-    const int r = lane % ROWS, h = lane / ROWS;             // this lane's row and group quarter
+    const int r = lane % ROWS, h = lane / ROWS;             // this lane's row and group block
     const int n0 = blockIdx.x * ROWS;
     char *const tile = reinterpret_cast<char *>(lds) + wave * L::wave;
     char *const lut = tile + L::tile;
@@ -159,7 +165,7 @@ __global__ __launch_bounds__((L4<ROWS, AFF>::max_waves * 64)) void q1_gemv_lut4_
     // tile: copy k covers rows rows_per_copy * k + lane / gpw, one 16-byte cell per lane
     const u32x4 *wg = reinterpret_cast<const u32x4 *>(wbits);
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
+    for (int k = 0; k < L::tile / 1024; ++k) {
         const int rr = L::rows_per_copy * k + lane / L::gpw;
         const int gg = min(g0 + ((lane % L::gpw) ^ L::swz(rr)), gl);
         __builtin_amdgcn_global_load_lds((glb_void_t *)(wg + (size_t)min(n0 + rr, N - 1) * G + gg),
@@ -169,7 +175,7 @@ __global__ __launch_bounds__((L4<ROWS, AFF>::max_waves * 64)) void q1_gemv_lut4_
     // (4 bytes), else (row d % ROWS, group d / ROWS) (2 bytes, the low half of its dword); it
     // lands in the dword at sc + 4 d
     // (AFF: the biases likewise, to bc)
-    constexpr int kScaleCopies = PAIRS ? 2 : 4;
+    constexpr int kScaleCopies = (PAIRS ? ROWS * L::gpw / 2 : ROWS * L::gpw) / 64;
 #pragma unroll
     for (int which = 0; which < (AFF ? 2 : 1); ++which) {
         const uint16_t *const src = which ? biases : scales;
@@ -191,11 +197,15 @@ __global__ __launch_bounds__((L4<ROWS, AFF>::max_waves * 64)) void q1_gemv_lut4_
     // x quads: quad k of this lane is x[128 g0 + 64 k + 4 (lane / 4) .. + 3], at
     // lut + 128 k + 8 (lane / 4); the first block waits until at most the tile, scale (and
     // bias) copies are in flight
-    constexpr int kQuads = 8 * L::lpr;
+    constexpr int kQuads = 2 * L::gpw;
     uint2 xq[kQuads];
     const uint32_t xa = (uint32_t)(uintptr_t)((lds_char_t *)lut) + 8 * (lane >> 2);
-    if constexpr (PAIRS && !AFF) BONSAI_L4_XREAD8("s_waitcnt vmcnt(6)\n\t", xq, xa);
-    else if constexpr (PAIRS || !AFF) BONSAI_L4_XREAD8("s_waitcnt vmcnt(8)\n\t", xq, xa);
+    constexpr int kAfterX = L::tile / 1024 + (AFF ? 2 : 1) * kScaleCopies;   // copies issued after x
+    static_assert(kAfterX == 3 || kAfterX == 4 || kAfterX == 6 || kAfterX == 8 || kAfterX == 12);
+    if constexpr (kAfterX == 3) BONSAI_L4_XREAD8("s_waitcnt vmcnt(3)\n\t", xq, xa);
+    else if constexpr (kAfterX == 4) BONSAI_L4_XREAD8("s_waitcnt vmcnt(4)\n\t", xq, xa);
+    else if constexpr (kAfterX == 6) BONSAI_L4_XREAD8("s_waitcnt vmcnt(6)\n\t", xq, xa);
+    else if constexpr (kAfterX == 8) BONSAI_L4_XREAD8("s_waitcnt vmcnt(8)\n\t", xq, xa);
     else BONSAI_L4_XREAD8("s_waitcnt vmcnt(12)\n\t", xq, xa);
     if constexpr (kQuads == 16) BONSAI_L4_XREAD8("", xq + 8, xa + 1024);
 
@@ -243,26 +253,27 @@ __global__ __launch_bounds__((L4<ROWS, AFF>::max_waves * 64)) void q1_gemv_lut4_
     vm_wait<0>();                                   // the tile and the scales landed
     lgkm_wait0();                                   // this wave's tables are written
 
-    // this lane's scales (and biases) (row r, groups 4 h .. 4 h + 3 of the wave's), before the
-    // lookups
-    uint32_t sw[PAIRS ? 2 : 4], bw[AFF ? (PAIRS ? 2 : 4) : 1];
+    // this lane's scales (and biases) (row r, groups GPL h .. GPL h + GPL - 1 of the wave's),
+    // before the lookups
+    constexpr int kSw = PAIRS ? GPL / 2 : GPL;
+    uint32_t sw[kSw], bw[AFF ? kSw : 1];
 #pragma unroll
-    for (int k = 0; k < (PAIRS ? 2 : 4); ++k) {
-        const int off = 4 * ((PAIRS ? 2 * h : 4 * h) + k) * ROWS + 4 * r;
+    for (int k = 0; k < kSw; ++k) {
+        const int off = 4 * (kSw * h + k) * ROWS + 4 * r;
         sw[k] = *reinterpret_cast<const uint32_t *>(sc + off);
         if constexpr (AFF) bw[k] = *reinterpret_cast<const uint32_t *>(bc + off);
     }
 
     const uint32_t mask_3c = __builtin_amdgcn_readfirstlane(0x3Cu);
-    // the tables of this lane's 4 groups start at lut + 8 KB h (256-aligned)
-    const uint32_t lut_addr = (uint32_t)(uintptr_t)((lds_char_t *)lut) + 4 * kLutBytes * h;
+    // the tables of this lane's GPL groups start at lut + GPL * 2 KB * h (256-aligned)
+    const uint32_t lut_addr = (uint32_t)(uintptr_t)((lds_char_t *)lut) + GPL * kLutBytes * h;
     uint32_t raddr[16];
 #pragma unroll
     for (int j = 0; j < 16; ++j) raddr[j] = lut_addr;
     float acc = 0.f;
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-        const int ug = 4 * h + u;                   // group of the wave's slice
+    for (int u = 0; u < GPL; ++u) {
+        const int ug = GPL * h + u;                 // group of the wave's slice
         const u32x4 q = *reinterpret_cast<const u32x4 *>(tile + L::gpw * 16 * r + 16 * (ug ^ L::swz(r)));
         float a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;
 #pragma unroll
@@ -305,23 +316,23 @@ __global__ __launch_bounds__((L4<ROWS, AFF>::max_waves * 64)) void q1_gemv_lut4_
     }
 }
 
-template <int ROWS, bool AFF>
+template <int ROWS, bool AFF, int GPL = 4>
 hipError_t launch_lut4(const uint32_t *wbits, const uint16_t *scales, const uint16_t *biases, const uint16_t *x,
                        float *y, int N, int K, hipStream_t stream)
 {
-    using L = L4<ROWS, AFF>;
+    using L = L4<ROWS, AFF, GPL>;
     const int G = K / 128;
     const int tiles = (N + ROWS - 1) / ROWS;
     const int waves = (G + L::gpw - 1) / L::gpw;
     const size_t lds = (size_t)waves * L::wave;
     const bool pairs = (G % 2) == 0;                // a row's scale pairs are then dword aligned
-    const void *fn = pairs ? reinterpret_cast<const void *>(&q1_gemv_lut4_kernel<ROWS, true, AFF>)
-                           : reinterpret_cast<const void *>(&q1_gemv_lut4_kernel<ROWS, false, AFF>);
+    const void *fn = pairs ? reinterpret_cast<const void *>(&q1_gemv_lut4_kernel<ROWS, true, AFF, GPL>)
+                           : reinterpret_cast<const void *>(&q1_gemv_lut4_kernel<ROWS, false, AFF, GPL>);
     static const bool attrs_set = [] {
         const int most = L::max_waves * L::wave;
-        return hipFuncSetAttribute(reinterpret_cast<const void *>(&q1_gemv_lut4_kernel<ROWS, true, AFF>),
+        return hipFuncSetAttribute(reinterpret_cast<const void *>(&q1_gemv_lut4_kernel<ROWS, true, AFF, GPL>),
                                    hipFuncAttributeMaxDynamicSharedMemorySize, most) == hipSuccess &&
-               hipFuncSetAttribute(reinterpret_cast<const void *>(&q1_gemv_lut4_kernel<ROWS, false, AFF>),
+               hipFuncSetAttribute(reinterpret_cast<const void *>(&q1_gemv_lut4_kernel<ROWS, false, AFF, GPL>),
                                    hipFuncAttributeMaxDynamicSharedMemorySize, most) == hipSuccess;
     }();
     if (!attrs_set) return hipErrorInvalidValue;
@@ -558,17 +569,20 @@ hipError_t launch_q1_gemv(const uint32_t *wbits, const uint16_t *scales, const u
     if (M >= 2 && M <= 8) return launch_gemv_mfma(false, wbits, scales, x, y, M, N, K, stream);
     if (M != 1) return hipErrorInvalidValue;
     // The route follows measurements at K = 5120 (N = 1024 ... 248320) and K = 13824:
-    // - 32-row tiles while one round of 256 CUs holds them (twice the CUs of 64-row tiles);
+    // - 32-row tiles while one round of 256 CUs holds them (twice the CUs of 64-row tiles), with
+    //   two groups per lane where the waves fit (10 waves instead of 5 at K = 5120, 5120 x 5120:
+    //   4.4 us instead of 5.3);
     // - 64-row tiles (one workgroup per CU, about 5 us a round) up to six rounds;
     // - beyond, the persistent kernel: about 15 us up front for the tables of all of K on every
     //   CU, then about 0.15 ns a row, so it overtakes near 100k rows;
     // - K too long for any of their tables in LDS: the matrix-core kernel, which measured 9.6 us
     //   against 15.7 for a table-lookup kernel that stages K in batches (N = 5120, K = 13824).
     const int G = K / 128;
-    const bool fits32 = (G + L4<32>::gpw - 1) / L4<32>::gpw <= L4<32>::max_waves;
+    using L32 = L4<32, false, 2>;
+    const bool fits32 = (G + L32::gpw - 1) / L32::gpw <= L32::max_waves;
     const bool fits64 = (G + L4<64>::gpw - 1) / L4<64>::gpw <= L4<64>::max_waves;
     const int64_t tiles64 = ((int64_t)N + 63) / 64;
-    if (fits32 && ((int64_t)N + 31) / 32 <= 256) return launch_lut4<32, false>(wbits, scales, nullptr, x, y, N, K, stream);
+    if (fits32 && ((int64_t)N + 31) / 32 <= 256) return launch_lut4<32, false, 2>(wbits, scales, nullptr, x, y, N, K, stream);
     if (fits64 && tiles64 <= 6 * 256) return launch_lut4<64, false>(wbits, scales, nullptr, x, y, N, K, stream);
     if (const int nw = lutp_waves(G)) return launch_lutp(wbits, scales, x, y, N, K, nw, stream);
     if (fits64) return launch_lut4<64, false>(wbits, scales, nullptr, x, y, N, K, stream);

@@ -153,7 +153,9 @@ EDGE = {
                 # matrix-core kernel (G even and odd)
                 (1, 8192, 640), (1, 8193, 640), (1, 16384, 384), (1, 16385, 1152), (1, 20000, 640),
                 (1, 40000, 256), (1, 17000, 6144), (1, 98304, 384), (1, 98305, 384), (1, 100003, 640),
-                (1, 16500, 8192), (1, 5000, 7808)],
+                (1, 16500, 8192), (1, 5000, 7808),
+                # 32-row tiles at two groups per lane, up to their 60 groups (G even and odd)
+                (1, 3000, 7680), (1, 2999, 7552)],
     "q2t_gemv": [(1, 1, 128), (1, 63, 256), (2, 65, 384), (8, 1000, 1152), (7, 777, 2048),
                  (1, 130, 131072), (4, 4097, 640)],
     # M <= 80 runs the small-M kernel in 16-row blocks of x (ragged last block), above it the tiles
