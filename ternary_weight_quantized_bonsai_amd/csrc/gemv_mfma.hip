@@ -35,10 +35,10 @@
 // and of the output, so a skinny product (a few dozen rows of x, as in checking several draft
 // tokens at once) runs as that many 16-column passes over the same weight tiles.
 //
-// Work split.  A workgroup owns R = 16 RT weight rows; its waves take 4-group slices of K.
-// Each slice's codes (R rows x 4 groups), scales and x (M rows x 512 k) are copied straight
-// into the wave's LDS (direct global->LDS loads, whole lines), the wave's partial sums of the
-// R x M outputs meet the other waves' in LDS and are added in a fixed order.
+// Work split.  A workgroup owns R = 16 RT weight rows; its waves take slices of K of SG = 4 or
+// 2 groups.  Each slice's codes (R rows x SG groups), scales and x (M rows x 128 SG k) are
+// copied straight into the wave's LDS (direct global->LDS loads, whole lines), the wave's
+// partial sums of the R x M outputs meet the other waves' in LDS and are added in a fixed order.
 #include <limits.h>
 
 #include <type_traits>
@@ -53,27 +53,33 @@ typedef float float4_v __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) void lds_void_t;
 typedef __attribute__((address_space(1))) const void glb_void_t;
 
-constexpr int kSmGroups = 4;                   // groups per K-slice
 constexpr int kSmMaxWaves = 16;
-constexpr int kSmScaleBytes = 64 * kSmGroups * 4;   // room for one dword per (row, group)
 
-template <bool TERN>
+// SG: groups per K-slice, 4 or 2.  Two-group slices give twice the waves for the same K, which
+// spread more evenly over a CU's four SIMDs when four-group slices would leave them uneven.
+template <bool TERN, int SG>
 struct SmLayout {
     // (affine weights use the binary layout; their biases take a second scale-sized region)
     static constexpr int cell = TERN ? 32 : 16;           // bytes per (row, group)
-    static constexpr int row_bytes = kSmGroups * cell;     // bytes per row and slice
+    static constexpr int row_bytes = SG * cell;            // bytes per row and slice
     static constexpr int lanes_per_row = row_bytes / 16;
     static constexpr int rows_per_copy = 64 / lanes_per_row;
-    // LDS bytes per row of x (512 k): the pad puts the x rows a lane quarter reads on distinct
-    // banks (4 dwords apart for the one-dword ternary reads, 8 for the two-dword binary ones)
-    static constexpr int xstride = 1024 + (TERN ? 16 : 32);
+    // LDS bytes per row of x (128 SG k): the pad puts the x rows a lane quarter reads on
+    // distinct banks (4 dwords apart for the one-dword ternary reads, 8 for the two-dword
+    // binary ones)
+    static constexpr int xstride = 256 * SG + (TERN ? 16 : 32);
+    // the 16-byte unit c of row r sits at row_bytes r + 16 (c ^ swz(r)): rows 256 B apart (the
+    // same banks) hold their units in different places
+    static __device__ __forceinline__ int swz(int r) { return (r / (256 / row_bytes)) & (lanes_per_row - 1); }
+    static constexpr int scale_bytes = 64 * SG * 4;       // room for one dword per (row, group), 64 rows
 };
 
 // LDS bytes of one wave: codes, scales (and biases) and the M rows of x
-template <bool TERN, bool AFF>
+template <bool TERN, bool AFF, int SG>
 constexpr int sm_wave_bytes(int rt, int m)
 {
-    return 16 * rt * SmLayout<TERN>::row_bytes + (AFF ? 2 : 1) * kSmScaleBytes + m * SmLayout<TERN>::xstride;
+    using L = SmLayout<TERN, SG>;
+    return 16 * rt * L::row_bytes + (AFF ? 2 : 1) * L::scale_bytes + m * L::xstride;
 }
 
 // four row tiles per wave need more than the 128 VGPRs that 16 waves per workgroup leave
@@ -81,7 +87,7 @@ constexpr int sm_max_waves(int rt) { return rt >= 4 ? 12 : kSmMaxWaves; }
 
 // PAIRS: the group count is even, so a row's scales of groups 2p, 2p + 1 are one aligned dword.
 // AFF: affine 1-bit weights (binary words, scales and biases); biases is unused otherwise.
-template <bool TERN, bool AFF, int RT, bool PAIRS>
+template <bool TERN, bool AFF, int RT, bool PAIRS, int SG>
 __global__ __launch_bounds__(sm_max_waves(RT) * 64) void gemv_mfma_kernel(const uint32_t *__restrict__ codes,
                                                                      const uint16_t *__restrict__ scales,
                                                                      const uint16_t *__restrict__ biases,
@@ -89,7 +95,8 @@ __global__ __launch_bounds__(sm_max_waves(RT) * 64) void gemv_mfma_kernel(const 
                                                                      float *__restrict__ y, int M, int N, int K)
 {
     static_assert(!(TERN && AFF), "affine weights are binary words");
-    using L = SmLayout<TERN>;
+    static_assert(SG == 4 || SG == 2, "four- or two-group slices");
+    using L = SmLayout<TERN, SG>;
     constexpr int R = 16 * RT;
     constexpr int TILE = R * L::row_bytes;
     extern __shared__ u32x4 lds[];
@@ -101,14 +108,14 @@ __global__ __launch_bounds__(sm_max_waves(RT) * 64) void gemv_mfma_kernel(const 
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int nw = blockDim.x >> 6;
     const int G = K >> 7;
-    const int ns = (G + kSmGroups - 1) / kSmGroups;       // slices of K
+    const int ns = (G + SG - 1) / SG;                     // slices of K
     const int n0 = blockIdx.x * R;
-    const int wbytes = sm_wave_bytes<TERN, AFF>(RT, M);
+    const int wbytes = sm_wave_bytes<TERN, AFF, SG>(RT, M);
     char *const mine = reinterpret_cast<char *>(lds) + wave * wbytes;
     char *const tile = mine;
     char *const sc = mine + TILE;
-    char *const bc = sc + kSmScaleBytes;                  // biases (affine only), laid out as sc
-    char *const xs = sc + (AFF ? 2 : 1) * kSmScaleBytes;
+    char *const bc = sc + L::scale_bytes;                 // biases (affine only), laid out as sc
+    char *const xs = sc + (AFF ? 2 : 1) * L::scale_bytes;
     float *const red = reinterpret_cast<float *>(reinterpret_cast<char *>(lds) + nw * wbytes);
     const int q = lane >> 4, i16 = lane & 15;
     const int units = G * (L::cell / 16);                  // 16-byte units per weight row
@@ -121,62 +128,67 @@ __global__ __launch_bounds__(sm_max_waves(RT) * 64) void gemv_mfma_kernel(const 
     const float4_v zero4 = float4_v{0.f, 0.f, 0.f, 0.f};
 
     for (int s = wave; s < ns; s += nw) {
-        const int g0 = s * kSmGroups;
-        const int g1 = min(G, g0 + kSmGroups), gl = g1 - 1;
-        // codes: copy k covers rows rows_per_copy * k + lane / lanes_per_row; the 16-byte
-        // chunk c of row r lands at row_bytes * r + 16 (c ^ swizzle(r))
+        const int g0 = s * SG;
+        const int g1 = min(G, g0 + SG), gl = g1 - 1;
+        // codes: copy k covers rows rows_per_copy * k + lane / lanes_per_row (a tile under 1 KB,
+        // binary 16 rows of two groups, takes the first lanes of one copy); the 16-byte chunk c
+        // of row r lands at row_bytes * r + 16 (c ^ swz(r))
 #pragma unroll
-        for (int k = 0; k < TILE / 1024; ++k) {
-            const int r = L::rows_per_copy * k + lane / L::lanes_per_row;
-            const int sw = TERN ? ((r >> 1) & 7) : ((r >> 2) & 3);
-            const int c = (lane % L::lanes_per_row) ^ sw;
-            const int unit = min(g0 * (L::cell / 16) + c, units - 1);
-            __builtin_amdgcn_global_load_lds((glb_void_t *)(cg + (size_t)min(n0 + r, N - 1) * units + unit),
-                                             (lds_void_t *)(tile + k * 1024), 16, 0, 0);
+        for (int k = 0; k < (TILE + 1023) / 1024; ++k) {
+            if (1024 * k + 16 * lane < TILE) {
+                const int r = L::rows_per_copy * k + lane / L::lanes_per_row;
+                const int c = (lane % L::lanes_per_row) ^ L::swz(r);
+                const int unit = min(g0 * (L::cell / 16) + c, units - 1);
+                __builtin_amdgcn_global_load_lds((glb_void_t *)(cg + (size_t)min(n0 + r, N - 1) * units + unit),
+                                                 (lds_void_t *)(tile + k * 1024), 16, 0, 0);
+            }
         }
-        // scales: the scale of (row r, group u) is half u of the 8 bytes at sc + 8 r (PAIRS:
-        // one 4-byte copy per row and pair of groups), or the low half of the dword at
-        // sc + 16 r + 4 u (one 2-byte copy per row and group)
+        // scales: SW dwords per row; the scale of (row r, group u) is half u % 2 of the dword at
+        // sc + 4 (SW r + u / 2) (PAIRS, SW = SG / 2: one 4-byte copy per row and pair of groups),
+        // or the low half of the dword at sc + 4 (SW r + u) (SW = SG: one 2-byte copy per row and
+        // group)
+        constexpr int SW = PAIRS ? SG / 2 : SG;
 #pragma unroll
         for (int which = 0; which < (AFF ? 2 : 1); ++which) {
             const uint16_t *const src = which ? biases : scales;
             char *const dst = which ? bc : sc;
             if constexpr (PAIRS) {
 #pragma unroll
-                for (int k = 0; k < (2 * R + 63) / 64; ++k) {
-                    const int e = 64 * k + lane, r = min(e >> 1, R - 1), p = e & 1;
+                for (int k = 0; k < (SW * R + 63) / 64; ++k) {
+                    const int e = 64 * k + lane, r = min(e / SW, R - 1), p = e % SW;
                     __builtin_amdgcn_global_load_lds((glb_void_t *)(src + (size_t)min(n0 + r, N - 1) * G + min(g0 + 2 * p, G - 2)),
                                                      (lds_void_t *)(dst + 256 * k), 4, 0, 0);
                 }
             } else {
 #pragma unroll
-                for (int k = 0; k < (4 * R + 63) / 64; ++k) {
-                    const int e = 64 * k + lane, r = min(e >> 2, R - 1), u = e & 3;
+                for (int k = 0; k < (SW * R + 63) / 64; ++k) {
+                    const int e = 64 * k + lane, r = min(e / SW, R - 1), u = e % SW;
                     __builtin_amdgcn_global_load_lds((glb_void_t *)(src + (size_t)min(n0 + r, N - 1) * G + min(g0 + u, gl)),
                                                      (lds_void_t *)(dst + 256 * k), 2, 0, 0);
                 }
             }
         }
-        // x: row m, k = 128 g0 .. 128 g0 + 511 (clamped inside K; past-K groups count 0)
-        for (int m = 0; m < M; ++m)
-            __builtin_amdgcn_global_load_lds((glb_void_t *)(xg + (size_t)m * (K >> 3) + min(16 * g0 + lane, (K >> 3) - 1)),
-                                             (lds_void_t *)(xs + m * L::xstride), 16, 0, 0);
+        // x: row m, k = 128 g0 .. 128 g0 + 128 SG - 1 (clamped inside K; past-K groups count 0)
+        if (lane < 16 * SG) {
+            for (int m = 0; m < M; ++m)
+                __builtin_amdgcn_global_load_lds((glb_void_t *)(xg + (size_t)m * (K >> 3) + min(16 * g0 + lane, (K >> 3) - 1)),
+                                                 (lds_void_t *)(xs + m * L::xstride), 16, 0, 0);
+        }
         vm_wait<0>();                                     // this wave's slice landed
-        if (g1 - g0 < kSmGroups) {
+        if (g1 - g0 < SG) {
             // groups past K (last slice only) hold clamped copies: their scales (and biases)
             // become zero
-            for (int e = lane; e < R * kSmGroups; e += 64) {
-                const int r = e >> 2, u = e & 3;
-                const int off = PAIRS ? 8 * r + 2 * u : 16 * r + 4 * u;
+            for (int e = lane; e < R * SG; e += 64) {
+                const int r = e / SG, u = e % SG;
+                const int off = PAIRS ? 4 * SW * r + 2 * u : 4 * SW * r + 4 * u;
                 if (g0 + u >= g1) {
                     *reinterpret_cast<uint16_t *>(sc + off) = 0;
                     if constexpr (AFF) *reinterpret_cast<uint16_t *>(bc + off) = 0;
                 }
             }
         }
-        // the scales of this lane's D rows 16 t + 4 q + r, all four groups: the binary16 of
-        // group u is half u % 2 of sp[t][r][u / 2] (PAIRS) or the low half of sp[t][r][u]
-        constexpr int SW = PAIRS ? 2 : 4;
+        // the scales of this lane's D rows 16 t + 4 q + r, all SG groups: the binary16 of group u
+        // is half u % 2 of sp[t][r][u / 2] (PAIRS) or the low half of sp[t][r][u]
         constexpr int NB = AFF ? 2 : 1;
         uint32_t sp[NB][RT][4][SW];                       // [0] scales, [1] biases
 #pragma unroll
@@ -187,26 +199,28 @@ __global__ __launch_bounds__(sm_max_waves(RT) * 64) void gemv_mfma_kernel(const 
                 for (int r = 0; r < 4; ++r) {
                     const int row = 16 * t + 4 * q + r;
                     const char *const base = b ? bc : sc;
-                    if constexpr (PAIRS) {
+                    if constexpr (SW == 4) {
+                        const u32x4 v = *reinterpret_cast<const u32x4 *>(base + 16 * row);
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) sp[b][t][r][e] = v[e];
+                    } else if constexpr (SW == 2) {
                         const uint2 v = *reinterpret_cast<const uint2 *>(base + 8 * row);
                         sp[b][t][r][0] = v.x;
                         sp[b][t][r][1] = v.y;
                     } else {
-                        const u32x4 v = *reinterpret_cast<const u32x4 *>(base + 16 * row);
-#pragma unroll
-                        for (int e = 0; e < 4; ++e) sp[b][t][r][e] = v[e];
+                        sp[b][t][r][0] = *reinterpret_cast<const uint32_t *>(base + 4 * row);
                     }
                 }
-        float xq[kSmGroups];                              // affine: this quarter's part of X per group
+        float xq[SG];                                     // affine: this quarter's part of X per group
 
 #pragma unroll
-        for (int u = 0; u < kSmGroups; ++u) {
+        for (int u = 0; u < SG; ++u) {
             // this lane's weight rows: 16 t + i16, one cell each
             uint32_t wd[RT][L::cell / 4];
 #pragma unroll
             for (int t = 0; t < RT; ++t) {
                 const int r = 16 * t + i16;
-                const int sw = TERN ? ((r >> 1) & 7) : ((r >> 2) & 3);
+                const int sw = L::swz(r);
 #pragma unroll
                 for (int h = 0; h < L::cell / 16; ++h) {
                     const int c = (L::cell / 16) * u + h;
@@ -282,7 +296,7 @@ __global__ __launch_bounds__(sm_max_waves(RT) * 64) void gemv_mfma_kernel(const 
         if constexpr (AFF) {
             // the bias term: X of column i16 is the sum of the four quarters' parts
 #pragma unroll
-            for (int u = 0; u < kSmGroups; ++u) {
+            for (int u = 0; u < SG; ++u) {
                 float xg = xq[u] + __shfl_xor(xq[u], 16);
                 xg = (xg + __shfl_xor(xg, 32)) * 0x1p-7f;
 #pragma unroll
@@ -316,47 +330,47 @@ __global__ __launch_bounds__(sm_max_waves(RT) * 64) void gemv_mfma_kernel(const 
 constexpr int kLdsPerCu = 160 * 1024;
 
 // waves of a workgroup: one per slice of K, at most 16 and as many as the LDS holds
-template <bool TERN, bool AFF>
+template <bool TERN, bool AFF, int SG>
 int sm_waves(int rt, int M, int K)
 {
-    const int ns = (K / 128 + kSmGroups - 1) / kSmGroups;
-    const int per_wave = sm_wave_bytes<TERN, AFF>(rt, M) + M * 16 * rt * 4;
+    const int ns = (K / 128 + SG - 1) / SG;
+    const int per_wave = sm_wave_bytes<TERN, AFF, SG>(rt, M) + M * 16 * rt * 4;
     int nw = ns < sm_max_waves(rt) ? ns : sm_max_waves(rt);
     if (nw > kLdsPerCu / per_wave) nw = kLdsPerCu / per_wave;
     return nw;
 }
 
-template <bool TERN, bool AFF, int RT>
+template <bool TERN, bool AFF, int RT, int SG>
 hipError_t launch_rt(const uint32_t *codes, const uint16_t *scales, const uint16_t *biases, const uint16_t *x,
                      float *y, int M, int N, int K, hipStream_t stream)
 {
     const int mb = M < 16 ? M : 16;                 // rows of x per workgroup
-    const int nw = sm_waves<TERN, AFF>(RT, mb, K);
+    const int nw = sm_waves<TERN, AFF, SG>(RT, mb, K);
     if (nw < 1) return hipErrorInvalidValue;
-    const size_t lds = (size_t)nw * sm_wave_bytes<TERN, AFF>(RT, mb) + (size_t)nw * mb * 16 * RT * 4;
+    const size_t lds = (size_t)nw * sm_wave_bytes<TERN, AFF, SG>(RT, mb) + (size_t)nw * mb * 16 * RT * 4;
     const int64_t blocks = ((int64_t)N + 16 * RT - 1) / (16 * RT);
     const int64_t yblocks = ((int64_t)M + 15) / 16;
     if (blocks > INT_MAX || yblocks > 65535) return hipErrorInvalidValue;
-    const void *fn = (K / 128) % 2 == 0 ? reinterpret_cast<const void *>(&gemv_mfma_kernel<TERN, AFF, RT, true>)
-                                        : reinterpret_cast<const void *>(&gemv_mfma_kernel<TERN, AFF, RT, false>);
+    const void *fn = (K / 128) % 2 == 0 ? reinterpret_cast<const void *>(&gemv_mfma_kernel<TERN, AFF, RT, true, SG>)
+                                        : reinterpret_cast<const void *>(&gemv_mfma_kernel<TERN, AFF, RT, false, SG>);
     static const bool attr =
-        hipFuncSetAttribute(reinterpret_cast<const void *>(&gemv_mfma_kernel<TERN, AFF, RT, true>),
+        hipFuncSetAttribute(reinterpret_cast<const void *>(&gemv_mfma_kernel<TERN, AFF, RT, true, SG>),
                             hipFuncAttributeMaxDynamicSharedMemorySize, kLdsPerCu) == hipSuccess &&
-        hipFuncSetAttribute(reinterpret_cast<const void *>(&gemv_mfma_kernel<TERN, AFF, RT, false>),
+        hipFuncSetAttribute(reinterpret_cast<const void *>(&gemv_mfma_kernel<TERN, AFF, RT, false, SG>),
                             hipFuncAttributeMaxDynamicSharedMemorySize, kLdsPerCu) == hipSuccess;
     if (!attr) return hipErrorInvalidValue;
     void *args[] = {&codes, &scales, &biases, &x, &y, &M, &N, &K};
     return launch_kernel(fn, dim3((unsigned)blocks, (unsigned)yblocks), dim3(64 * nw), args, lds, stream);
 }
 
-// waves of gemv_mfma_kernel<TERN, AFF, RT, PAIRS> that one CU holds by registers: 512 VGPRs per
-// SIMD lane, in granules of 8, at most 8 waves per SIMD, 4 SIMDs
-template <bool TERN, bool AFF, int RT, bool PAIRS>
+// waves of gemv_mfma_kernel<TERN, AFF, RT, PAIRS, SG> that one CU holds by registers: 512 VGPRs
+// per SIMD lane, in granules of 8, at most 8 waves per SIMD, 4 SIMDs
+template <bool TERN, bool AFF, int RT, bool PAIRS, int SG>
 int sm_reg_waves_per_cu()
 {
     static const int waves = [] {
         hipFuncAttributes a;
-        if (hipFuncGetAttributes(&a, reinterpret_cast<const void *>(&gemv_mfma_kernel<TERN, AFF, RT, PAIRS>)) !=
+        if (hipFuncGetAttributes(&a, reinterpret_cast<const void *>(&gemv_mfma_kernel<TERN, AFF, RT, PAIRS, SG>)) !=
                 hipSuccess ||
             a.numRegs <= 0)
             return 8;
@@ -366,10 +380,76 @@ int sm_reg_waves_per_cu()
     return waves;
 }
 
-template <bool TERN, bool AFF, int RT>
+template <bool TERN, bool AFF, int RT, int SG>
 int sm_reg_waves(bool pairs)
 {
-    return pairs ? sm_reg_waves_per_cu<TERN, AFF, RT, true>() : sm_reg_waves_per_cu<TERN, AFF, RT, false>();
+    return pairs ? sm_reg_waves_per_cu<TERN, AFF, RT, true, SG>() : sm_reg_waves_per_cu<TERN, AFF, RT, false, SG>();
+}
+
+template <bool TERN, bool AFF, int SG>
+struct SmChoice {
+    int rt, simd;                                 // tile, groups on the busiest SIMD
+    int64_t rounds, rows;
+};
+
+// groups that the busiest SIMD of a workgroup computes: wave w runs on SIMD w % 4 and takes
+// slices w, w + nw, ... of the ns slices of SG groups
+inline int sm_simd_groups(int nw, int ns, int sg)
+{
+    int most = 0;
+    for (int s = 0; s < 4; ++s) {
+        int n = 0;
+        for (int w = s; w < nw; w += 4) n += (ns - w + nw - 1) / nw;
+        most = n > most ? n : most;
+    }
+    return sg * most;
+}
+
+// The row tile (16, 32 or 64 rows) for slices of SG groups: the one whose grid needs the fewest
+// rounds of the chip's 256 CUs, given what the LDS and the registers of a CU hold; among those,
+// the one that leaves the busiest CU the fewest weight rows (workgroups per CU, rounded up,
+// times the tile), then the larger tile (its x copies and reduction serve more rows).
+template <bool TERN, bool AFF, int SG>
+SmChoice<TERN, AFF, SG> sm_choose(int M, int N, int K)
+{
+    constexpr int kCus = 256;
+    const int mb = M < 16 ? M : 16;
+    const bool pairs = (K / 128) % 2 == 0;
+    using C = SmChoice<TERN, AFF, SG>;
+    auto cost = [&](int rt, int reg_waves) -> C {
+        const int nw = sm_waves<TERN, AFF, SG>(rt, mb, K);
+        if (nw < 1) return {rt, 0, INT64_MAX, INT64_MAX};
+        const int simd = sm_simd_groups(nw, (K / 128 + SG - 1) / SG, SG);
+        const int64_t lds = (int64_t)nw * sm_wave_bytes<TERN, AFF, SG>(rt, mb) + (int64_t)nw * mb * 16 * rt * 4;
+        int64_t per_cu = kLdsPerCu / lds;
+        if (per_cu > reg_waves / nw) per_cu = reg_waves / nw;
+        if (per_cu < 1) return {rt, 0, INT64_MAX, INT64_MAX};
+        const int64_t blocks = (((int64_t)N + 16 * rt - 1) / (16 * rt)) * (((int64_t)M + 15) / 16);
+        return {rt, simd, (blocks + per_cu * kCus - 1) / (per_cu * kCus), (blocks + kCus - 1) / kCus * 16 * rt};
+    };
+    auto better = [](const C &a, const C &b) {   // a strictly better than b, ties to b
+        return a.rounds < b.rounds || (a.rounds == b.rounds && a.rows < b.rows);
+    };
+    const C c1 = cost(1, sm_reg_waves<TERN, AFF, 1, SG>(pairs));
+    const C c2 = cost(2, sm_reg_waves<TERN, AFF, 2, SG>(pairs));
+    // the affine kernel keeps scales and biases in registers: no four-tile variant
+    C best = {4, 0, INT64_MAX, INT64_MAX};
+    if constexpr (!AFF) best = cost(4, sm_reg_waves<TERN, AFF, 4, SG>(pairs));
+    if (better(c2, best)) best = c2;
+    if (better(c1, best)) best = c1;
+    return best;
+}
+
+template <bool TERN, bool AFF, int SG>
+hipError_t launch_choice(const SmChoice<TERN, AFF, SG> &c, const uint32_t *codes, const uint16_t *scales,
+                         const uint16_t *biases, const uint16_t *x, float *y, int M, int N, int K,
+                         hipStream_t stream)
+{
+    if (c.rounds == INT64_MAX) return hipErrorInvalidValue;
+    if (c.rt == 1) return launch_rt<TERN, AFF, 1, SG>(codes, scales, biases, x, y, M, N, K, stream);
+    if (c.rt == 2) return launch_rt<TERN, AFF, 2, SG>(codes, scales, biases, x, y, M, N, K, stream);
+    if constexpr (AFF) return hipErrorInvalidValue;
+    else return launch_rt<TERN, AFF, 4, SG>(codes, scales, biases, x, y, M, N, K, stream);
 }
 
 template <bool TERN, bool AFF = false>
@@ -377,44 +457,16 @@ hipError_t launch_sm(const uint32_t *codes, const uint16_t *scales, const uint16
                      float *y, int M, int N, int K, hipStream_t stream)
 {
     // Every wave loads its slice at once and then computes, so a second round of workgroups on
-    // a CU pays the load latency again.  The row tile (16, 32 or 64 rows) is the one whose grid
-    // needs the fewest rounds of the chip's 256 CUs, given what the LDS and the registers of a CU
-    // hold; among those, the one that leaves the busiest CU the fewest weight rows (workgroups
-    // per CU, rounded up, times the tile), then the larger tile (its x copies and reduction
-    // serve more rows).
-    constexpr int kCus = 256;
-    const int mb = M < 16 ? M : 16;
-    const bool pairs = (K / 128) % 2 == 0;
-    struct Cost {
-        int64_t rounds, rows;
-    };
-    auto cost = [&](int rt, int reg_waves) -> Cost {
-        const int nw = sm_waves<TERN, AFF>(rt, mb, K);
-        if (nw < 1) return {INT64_MAX, INT64_MAX};
-        const int64_t lds = (int64_t)nw * sm_wave_bytes<TERN, AFF>(rt, mb) + (int64_t)nw * mb * 16 * rt * 4;
-        int64_t per_cu = kLdsPerCu / lds;
-        if (per_cu > reg_waves / nw) per_cu = reg_waves / nw;
-        if (per_cu < 1) return {INT64_MAX, INT64_MAX};
-        const int64_t blocks = (((int64_t)N + 16 * rt - 1) / (16 * rt)) * (((int64_t)M + 15) / 16);
-        return {(blocks + per_cu * kCus - 1) / (per_cu * kCus), (blocks + kCus - 1) / kCus * 16 * rt};
-    };
-    auto better = [](const Cost &a, const Cost &b) {   // a strictly better than b, ties to b
-        return a.rounds < b.rounds || (a.rounds == b.rounds && a.rows < b.rows);
-    };
-    const Cost c1 = cost(1, sm_reg_waves<TERN, AFF, 1>(pairs));
-    const Cost c2 = cost(2, sm_reg_waves<TERN, AFF, 2>(pairs));
-    // the affine kernel keeps scales and biases in registers: no four-tile variant
-    Cost c4 = {INT64_MAX, INT64_MAX};
-    if constexpr (!AFF) c4 = cost(4, sm_reg_waves<TERN, AFF, 4>(pairs));
-    int rt = 4;
-    Cost best = c4;
-    if (better(c2, best)) rt = 2, best = c2;
-    if (better(c1, best)) rt = 1, best = c1;
-    if (best.rounds == INT64_MAX) return hipErrorInvalidValue;
-    if (rt == 1) return launch_rt<TERN, AFF, 1>(codes, scales, biases, x, y, M, N, K, stream);
-    if (rt == 2) return launch_rt<TERN, AFF, 2>(codes, scales, biases, x, y, M, N, K, stream);
-    if constexpr (AFF) return hipErrorInvalidValue;
-    else return launch_rt<TERN, AFF, 4>(codes, scales, biases, x, y, M, N, K, stream);
+    // a CU pays the load latency again: the best tile for four-group and for two-group slices,
+    // then the one of the two with fewer rounds, then fewer rows on the busiest CU, then fewer
+    // groups on the busiest SIMD (two-group slices spread a short K over more waves), then four
+    // groups (half the slice iterations, each with its waits and scale reads).
+    const auto c4 = sm_choose<TERN, AFF, 4>(M, N, K);
+    const auto c2 = sm_choose<TERN, AFF, 2>(M, N, K);
+    const bool two = c2.rounds < c4.rounds ||
+                     (c2.rounds == c4.rounds && (c2.rows < c4.rows || (c2.rows == c4.rows && c2.simd < c4.simd)));
+    return two ? launch_choice(c2, codes, scales, biases, x, y, M, N, K, stream)
+               : launch_choice(c4, codes, scales, biases, x, y, M, N, K, stream);
 }
 
 }  // namespace
