@@ -1,4 +1,5 @@
-"""Build libbonsai.so (the gfx950 kernels and the C ABI) in-tree with hipcc."""
+"""Build libbonsai.so (the gfx950 kernels and the C ABI) in-tree: hipcc for the kernel sources
+(*.hip), the host compiler for the host-only part of the C ABI (*.cpp)."""
 from __future__ import annotations
 
 import os
@@ -14,6 +15,8 @@ OUT = PKG / "_lib" / "libbonsai.so"
 OBJ = ROOT / "_build" / "obj"
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+CXX = os.environ.get("CXX", "g++")
+HOST_FLAGS = ["-O2", "-std=c++17", "-fPIC", "-Wall", "-Wextra", f"-I{ROOT / 'include'}"]
 FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
     # packed fp32 VALU forms are kept out of every kernel
@@ -23,7 +26,7 @@ FLAGS = [
 
 
 def sources() -> list[Path]:
-    return sorted(CSRC.glob("*.hip"))
+    return sorted(CSRC.glob("*.hip")) + sorted(CSRC.glob("*.cpp"))
 
 
 def build(verbose: bool = False) -> Path:
@@ -33,13 +36,16 @@ def build(verbose: bool = False) -> Path:
 
     def compile_one(src: Path) -> Path:
         obj = OBJ / (src.stem + ".o")
-        cmd = [HIPCC, *FLAGS, "-c", str(src), "-o", str(obj)]
+        if src.suffix == ".cpp":
+            cmd = [CXX, *HOST_FLAGS, "-c", str(src), "-o", str(obj)]
+        else:
+            cmd = [HIPCC, *FLAGS, "-c", str(src), "-o", str(obj)]
         if verbose:
             print(" ".join(cmd), flush=True)
         r = subprocess.run(cmd, capture_output=True, text=True)
         if r.returncode != 0:
             sys.stderr.write(r.stdout + r.stderr)
-            raise RuntimeError(f"hipcc failed on {src.name}")
+            raise RuntimeError(f"{Path(cmd[0]).name} failed on {src.name}")
         return obj
 
     with ThreadPoolExecutor(max_workers=min(8, os.cpu_count() or 1)) as ex:
