@@ -177,6 +177,42 @@ def test_edge_shapes(kind, M, N, K, orc):
     assert_close(y, yref, a, f"{kind} {M}x{N}x{K}")
 
 
+# The small-M matrix-core kernel picks, per call, a slice width (four or two groups of K), a row
+# tile (16, 32 or 64 rows) and, from the parity of K / 128, paired or single scale copies; a slice
+# width that does not divide K / 128 leaves a partial last slice.  These shapes were chosen so that
+# the launcher's choices, as they stand, reach every such combination of each weight form (no
+# 64-row tile for the affine form).  Whatever the launcher picks, each case is checked against the
+# oracle on sampled rows.
+SMALL_M_VARIANTS = sorted({(2, 33, 128), (2, 33, 256), (2, 5000, 128), (2, 5000, 256), (2, 13824, 128),
+                           (2, 13824, 256), (2, 33, 1152), (16, 33, 5120), (2, 33, 1280), (2, 5000, 1152),
+                           (2, 5000, 1280), (2, 13824, 1152), (2, 13824, 1280), (33, 1500, 5120),
+                           (33, 3000, 5120), (12, 5000, 5120), (12, 9000, 5120), (3, 9000, 5120)})
+
+
+def _sampled_rows(N, seed):
+    rng = np.random.default_rng(seed)
+    return np.unique(np.concatenate([np.arange(min(N, 40)), np.arange(max(0, N - 40), N),
+                                     rng.integers(0, N, 200)]))
+
+
+@pytest.mark.parametrize("form", ["binary", "ternary", "affine"])
+@pytest.mark.parametrize("M,N,K", SMALL_M_VARIANTS)
+def test_small_m_kernel_variants(form, M, N, K, orc):
+    rows = _sampled_rows(N, 91)
+    if form == "affine":
+        w, a, b, x = synth.make_q1a(M, N, K, 91, f"smv{N}x{K}")
+        y = _affine(w, a, b, x)
+        yref, _ = orc.q1a_matmul(w, a, b, x, K, None, rows)
+        assert_close(y[:, rows], yref, _affine_magnitude(orc, w, a, b, x, None, rows),
+                     f"q1a M={M} N={N} K={K}")
+        return
+    kind = ("q1" if form == "binary" else "q2t") + ("_gemv" if M <= 8 else "_gemm")
+    w, s, x = make(kind, M, N, K, 91, f"smv{N}x{K}")
+    y = call(kind, w, s, x)
+    yref, a = ref(kind, orc, w, s, x, n_idx=rows)
+    assert_close(y[:, rows], yref, a, f"{kind} M={M} N={N} K={K}")
+
+
 @pytest.mark.parametrize("kind", KINDS)
 def test_every_m_from_1_to_8(kind, orc):
     for M in range(1, 9):
