@@ -100,7 +100,11 @@ HEADLINE_KERNEL = "q1_gemv_lut4_kernel"
 
 
 def src_digest(path: Path) -> str:
-    return hashlib.sha256(path.read_bytes()).hexdigest()[:16]
+    """Digest of a kernel source together with the library's build recipe (compiler flags), so
+    that counters taken on one build are not reported for a kernel compiled differently."""
+    h = hashlib.sha256(path.read_bytes())
+    h.update((ROOT / "ternary_weight_quantized_bonsai_amd" / "build.py").read_bytes())
+    return h.hexdigest()[:16]
 
 
 def read_pmc(name: str, digest: str):
@@ -114,7 +118,7 @@ def read_pmc(name: str, digest: str):
         if ":" in line and not line.startswith("#"):
             k, v = line.split(":", 1)
             kv[k.strip()] = v.strip()
-    if kv.get("kernel_source_sha256_16") != digest or "hbm_bytes_per_launch" not in kv:
+    if kv.get("kernel_build_sha256_16") != digest or "hbm_bytes_per_launch" not in kv:
         return None
     return float(kv["hbm_bytes_per_launch"])
 
@@ -234,7 +238,7 @@ def summarize_pmc(fetch_dir: str, write_dir: str, out: str, cmds: list[str], ker
               "# Counters are KiB per dispatch; each is scaled by 1 GiB over what it reads for the copy",
               "# probe's 1 GiB device-to-device copy (median over its dispatches).", "",
               f"kernel: {kernel}",
-              f"kernel_source_sha256_16: {src_digest(ROOT / src)}",
+              f"kernel_build_sha256_16: {src_digest(ROOT / src)}",
               f"copy_kernel: __amd_rocclr_copyBuffer, the {ncf} (fetch run) / {ncw} (write run) 1 GiB copies",
               f"copy_fetch_kib: {cf:.1f}", f"copy_write_kib: {cw:.1f}",
               f"fetch_scale: {sf:.4f}", f"write_scale: {sw:.4f}", ""]
