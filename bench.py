@@ -315,7 +315,7 @@ def main() -> int:
                       "ternary_weight_quantized_bonsai_amd/csrc/q1_gemv.hip")
         return 0
     if args.gpus != 1:
-        print("bench.py measures one GPU: this build has no multi-GPU path (the GEMV shards by "
+        print("bench.py measures one GPU: the library has no multi-GPU path (the GEMV shards by "
               "rows with no collective; see the design notes). Run with --gpus 1.", file=sys.stderr)
         return 2
     if args.steps < 1 or args.warmup < 0:
