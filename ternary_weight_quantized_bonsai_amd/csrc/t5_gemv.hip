@@ -19,8 +19,10 @@
 // dword and digit 4 in its second.  One v_perm_b32 then builds the operand pair of bytes 2m and
 // 2m + 1 for digit i, (0x00, digit byte, 0x00, digit byte), exactly; the factor 2 comes off once
 // at the end.  Bytes 243..255 are reserved: the table maps them to zero weights, and results on
-// them are unspecified.  The table reads land on random banks; that conflict cost, not the
-// VALU work, is what this decode adds over the 2-bit codes' shift-and-mask.
+// them are unspecified.  The table is a static LDS array, so its address is a constant the
+// compiler folds into the reads, and a lookup's address (8 times byte k of a word) is one SDWA
+// shift.  The table reads land on random banks; that conflict cost is what this decode adds over
+// the 2-bit codes' shift-and-mask.
 //
 // Work split (as the small-M kernel for the other layouts).  A workgroup owns 16 RT weight rows
 // and one block of 16 rows of x; its waves take slices of 640 k (four superblocks, five groups):
@@ -45,12 +47,38 @@ constexpr int kT5SliceBytes = 32 * kT5SbPerSlice;    // code bytes per row and s
 constexpr int kT5XStride = 2 * 640 + 16;             // LDS bytes per row of x (640 k + pad)
 constexpr int kT5LutBytes = 256 * 8;
 // Waves per workgroup: at most 16 (WIDE), which caps a wave at 128 VGPRs, or 8.  The 32-row
-// tile takes about 160 VGPRs: the 8-wave build keeps them all, the 16-wave build spills two but
-// lets a CU hold two 8-wave workgroups by registers.
+// tile takes about 160 VGPRs: the 8-wave build keeps them all, the 16-wave build fits in 128
+// (no spill) and lets a CU hold two 8-wave workgroups by registers.
 constexpr int t5_max_waves(bool wide) { return wide ? 16 : 8; }
 constexpr int kLdsPerCu = 160 * 1024;
 
 constexpr int t5_scale_bytes(int rt) { return (5 * 16 * rt + 63) / 64 * 256; }
+
+typedef __attribute__((address_space(3))) char lds_char_t;
+typedef __attribute__((address_space(3))) const unsigned long long lds_u64_t;
+
+// the 8-byte table entry at LDS byte address a
+__device__ __forceinline__ uint2 lut_entry(uint32_t a)
+{
+    const unsigned long long v = *reinterpret_cast<lds_u64_t *>((uintptr_t)a);
+    return uint2{(uint32_t)v, (uint32_t)(v >> 32)};
+}
+
+// 8 * (byte KB of v): the byte offset of its 8-byte table entry, one SDWA shift
+template <int KB>
+__device__ __forceinline__ uint32_t entry_offset(uint32_t v, uint32_t three)
+{
+    uint32_t r;
+    if constexpr (KB == 0)
+        asm("v_lshlrev_b32_sdwa %0, %1, %2 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:DWORD src1_sel:BYTE_0" : "=v"(r) : "s"(three), "v"(v));
+    else if constexpr (KB == 1)
+        asm("v_lshlrev_b32_sdwa %0, %1, %2 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:DWORD src1_sel:BYTE_1" : "=v"(r) : "s"(three), "v"(v));
+    else if constexpr (KB == 2)
+        asm("v_lshlrev_b32_sdwa %0, %1, %2 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:DWORD src1_sel:BYTE_2" : "=v"(r) : "s"(three), "v"(v));
+    else
+        asm("v_lshlrev_b32_sdwa %0, %1, %2 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:DWORD src1_sel:BYTE_3" : "=v"(r) : "s"(three), "v"(v));
+    return r;
+}
 
 // LDS bytes of one wave: codes, scales and the M rows of x
 constexpr int t5_wave_bytes(int rt, int m) { return 16 * rt * kT5SliceBytes + t5_scale_bytes(rt) + m * kT5XStride; }
@@ -64,6 +92,9 @@ __global__ __launch_bounds__(t5_max_waves(WIDE) * 64) void t5_gemv_kernel(const 
     constexpr int R = 16 * RT;
     constexpr int TILE = R * kT5SliceBytes;
     constexpr int SCB = t5_scale_bytes(RT);
+    // the byte table is a static LDS array: its address is then a constant the compiler folds
+    // into the table reads, so a lookup is one SDWA shift; the rest of LDS is dynamic
+    __shared__ uint2 lut[256];
     extern __shared__ u32x4 lds[];
     x += (size_t)16 * blockIdx.y * K;
     y += (size_t)16 * blockIdx.y * N;
@@ -77,12 +108,11 @@ __global__ __launch_bounds__(t5_max_waves(WIDE) * 64) void t5_gemv_kernel(const 
     const int ns = (SB + kT5SbPerSlice - 1) / kT5SbPerSlice;
     const int n0 = blockIdx.x * R;
     const int wbytes = t5_wave_bytes(RT, M);
-    uint2 *const lut = reinterpret_cast<uint2 *>(lds);
-    char *const mine = reinterpret_cast<char *>(lds) + kT5LutBytes + wave * wbytes;
+    char *const mine = reinterpret_cast<char *>(lds) + wave * wbytes;
     char *const tile = mine;
     char *const sc = mine + TILE;
     char *const xs = sc + SCB;
-    float *const red = reinterpret_cast<float *>(reinterpret_cast<char *>(lds) + kT5LutBytes + nw * wbytes);
+    float *const red = reinterpret_cast<float *>(reinterpret_cast<char *>(lds) + nw * wbytes);
     const int q = lane >> 4, i16 = lane & 15;
     const u32x4 *xg = reinterpret_cast<const u32x4 *>(x);
     const int xunits = K >> 3;                        // 16-byte units per row of x
@@ -107,6 +137,8 @@ __global__ __launch_bounds__(t5_max_waves(WIDE) * 64) void t5_gemv_kernel(const 
 #pragma unroll
     for (int t = 0; t < RT; ++t) acc[t] = float4_v{0.f, 0.f, 0.f, 0.f};
     const float4_v zero4 = float4_v{0.f, 0.f, 0.f, 0.f};
+    const uint32_t lut_base = (uint32_t)(uintptr_t)((lds_char_t *)lut);
+    const uint32_t three = __builtin_amdgcn_readfirstlane(3u);
 
     for (int s = wave; s < ns; s += nw) {
         const int g0 = kT5GroupsPerSlice * s;
@@ -157,8 +189,14 @@ __global__ __launch_bounds__(t5_max_waves(WIDE) * 64) void t5_gemv_kernel(const 
                 const int r = 16 * t + i16;
                 const int slot = (2 * sb + (q >> 1)) ^ (r & 7);
                 const uint2 b8 = *reinterpret_cast<const uint2 *>(tile + kT5SliceBytes * r + 16 * slot + 8 * (q & 1));
-#pragma unroll
-                for (int e = 0; e < 8; ++e) lv[t][e] = lut[((e < 4 ? b8.x : b8.y) >> (8 * (e & 3))) & 0xFFu];
+                lv[t][0] = lut_entry(lut_base + entry_offset<0>(b8.x, three));
+                lv[t][1] = lut_entry(lut_base + entry_offset<1>(b8.x, three));
+                lv[t][2] = lut_entry(lut_base + entry_offset<2>(b8.x, three));
+                lv[t][3] = lut_entry(lut_base + entry_offset<3>(b8.x, three));
+                lv[t][4] = lut_entry(lut_base + entry_offset<0>(b8.y, three));
+                lv[t][5] = lut_entry(lut_base + entry_offset<1>(b8.y, three));
+                lv[t][6] = lut_entry(lut_base + entry_offset<2>(b8.y, three));
+                lv[t][7] = lut_entry(lut_base + entry_offset<3>(b8.y, three));
             }
 #pragma unroll
             for (int i = 0; i < 5; ++i) {
@@ -251,19 +289,21 @@ hipError_t t5_launch_rt(const uint8_t *codes, const uint16_t *scales, const uint
     const int64_t blocks = ((int64_t)N + 16 * RT - 1) / (16 * RT);
     const int64_t yblocks = ((int64_t)M + 15) / 16;
     if (blocks > INT_MAX || yblocks > 65535) return hipErrorInvalidValue;
+    // dynamic LDS: everything but the static 2 KB byte table
     static const bool attr = hipFuncSetAttribute(reinterpret_cast<const void *>(&t5_gemv_kernel<RT, WIDE>),
-                                                 hipFuncAttributeMaxDynamicSharedMemorySize, kLdsPerCu) == hipSuccess;
+                                                 hipFuncAttributeMaxDynamicSharedMemorySize,
+                                                 kLdsPerCu - kT5LutBytes) == hipSuccess;
     if (!attr) return hipErrorInvalidValue;
     void *args[] = {&codes, &scales, &x, &y, &M, &N, &K};
     return launch_kernel(reinterpret_cast<const void *>(&t5_gemv_kernel<RT, WIDE>), dim3((unsigned)blocks, (unsigned)yblocks),
-                         dim3(64 * nw), args, t5_lds(RT, mb, nw), stream);
+                         dim3(64 * nw), args, t5_lds(RT, mb, nw) - kT5LutBytes, stream);
 }
 
 }  // namespace
 
 // Any M >= 1 (16 rows of x per column block).  Three builds: 16-row tiles (up to 16 waves),
-// 32-row tiles with up to 8 waves (no spill), 32-row tiles with up to 16 waves (two registers
-// spilled, two workgroups per CU).  The launch takes the build whose grid needs the fewest rounds
+// 32-row tiles with up to 8 waves (163 VGPRs), 32-row tiles with up to 16 waves (held to 128
+// VGPRs, two workgroups per CU).  The launch takes the build whose grid needs the fewest rounds
 // of the chip's 256 CUs, given what the LDS and the registers of a CU hold; on a tie, in the
 // order that measured fastest: for one row of x the 16-row tile first (more workgroups in
 // flight), for more rows the 8-wave 32-row build first (x, held once per wave, fills the LDS).
