@@ -578,3 +578,52 @@ def test_graph_capture_and_replay_of_every_entry_point(orc):
         torch.cuda.synchronize()
         for (name, _, _, _), out, ref in zip(calls, outs, eager):
             assert torch.equal(out, ref), f"replay {rep}: {name} differs from the eager result"
+
+
+# ---- seeded random shapes over every entry point ----------------------------------------
+# Beside the hand-picked boundary shapes: shapes drawn from a fixed generator, so that routing
+# combinations nobody listed (table kernels, slice widths, tiles, passes over 16-row blocks of x,
+# ragged tails) get exercised.  Sizes are capped so the whole set runs in seconds; each case is
+# checked against the oracle on sampled rows.
+def _random_shapes(kind, count, seed):
+    rng = np.random.default_rng(seed)
+    out = []
+    while len(out) < count:
+        # one row of x half of the time where it has kernels of its own (the table GEMVs)
+        if kind in ("q1_gemv", "q2t_gemv"):
+            M = 1 if rng.random() < 0.5 else int(rng.integers(2, 9))
+        elif kind in ("q1_gemm", "q2t_gemm"):
+            M = int(rng.choice([rng.integers(1, 97), rng.integers(97, 600)]))
+        elif kind == "q1a_matmul":
+            M = 1 if rng.random() < 0.5 else int(rng.integers(2, 41))
+        else:
+            M = int(rng.integers(1, 41))
+        N = int(np.exp(rng.uniform(0.0, np.log(30000.0)))) + 1
+        K = 128 * int(rng.integers(1, 71))
+        if N * K <= 40_000_000 and M * N <= 2_000_000 and M * K <= 2_000_000:
+            out.append((M, N, K))
+    return out
+
+
+RANDOM_CASES = [(kind, *shape) for i, kind in enumerate(KINDS + ["t5_matmul", "q1a_matmul"])
+                for shape in _random_shapes(kind, 10, 1000 + i)]
+
+
+@pytest.mark.parametrize("kind,M,N,K", RANDOM_CASES)
+def test_random_shapes(kind, M, N, K, orc):
+    rows = _sampled_rows(N, 7)
+    tag = f"rnd{N}x{K}"
+    if kind == "t5_matmul":
+        codes, s, x = synth.make_t5(M, N, K, 7, tag)
+        y = _t5(codes, s, x)
+        yref, a = orc.t5_matmul(codes, s, x, K, None, rows)
+    elif kind == "q1a_matmul":
+        w, sa, b, x = synth.make_q1a(M, N, K, 7, tag)
+        y = _affine(w, sa, b, x)
+        yref, _ = orc.q1a_matmul(w, sa, b, x, K, None, rows)
+        a = _affine_magnitude(orc, w, sa, b, x, None, rows)
+    else:
+        w, s, x = make(kind, M, N, K, 7, tag)
+        y = call(kind, w, s, x)
+        yref, a = ref(kind, orc, w, s, x, n_idx=rows)
+    assert_close(y[:, rows], yref, a, f"{kind} M={M} N={N} K={K}")
