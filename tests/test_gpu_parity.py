@@ -627,3 +627,75 @@ def test_random_shapes(kind, M, N, K, orc):
         y = call(kind, w, s, x)
         yref, a = ref(kind, orc, w, s, x, n_idx=rows)
     assert_close(y[:, rows], yref, a, f"{kind} M={M} N={N} K={K}")
+
+
+# ---- concurrency: several host threads, each on its own stream ---------------------------
+def test_concurrent_calls_from_threads_on_their_own_streams():
+    """The C ABI is reentrant and asynchronous on the caller's stream: host threads that call
+    different entry points at once, each on a stream of its own, get exactly the results of
+    one-thread calls (every kernel is deterministic, so the comparison is bitwise)."""
+    import threading
+
+    import ternary_weight_quantized_bonsai_amd as bonsai
+    torch, dev = torch_dev()
+
+    def d(a):
+        return to_dev(a)
+
+    cases = []
+    w, s, x = synth.make_q1(1, 13824, 5120, 3, "thr1")
+    cases.append(("q1_gemv M=1", lambda o, w=d(w), s=d(s), x=d(x): bonsai.q1_gemv(w, s, x, out=o), (1, 13824)))
+    w, s, x = synth.make_q1(4, 5000, 2048, 3, "thr2")
+    cases.append(("q1_gemv M=4", lambda o, w=d(w), s=d(s), x=d(x): bonsai.q1_gemv(w, s, x, out=o), (4, 5000)))
+    w, s, x = synth.make_q1(300, 2048, 1024, 3, "thr3")
+    cases.append(("q1_gemm M=300", lambda o, w=d(w), s=d(s), x=d(x): bonsai.q1_gemm(w, s, x, out=o), (300, 2048)))
+    w, s, x = synth.make_q2t(1, 5120, 5120, 3, "thr4")
+    cases.append(("q2t_gemv M=1", lambda o, w=d(w), s=d(s), x=d(x): bonsai.q2t_gemv(w, s, x, out=o), (1, 5120)))
+    c5, s, x = synth.make_t5(2, 3000, 1152, 3, "thr5")
+    cases.append(("t5_matmul M=2", lambda o, c=torch.from_numpy(c5).to(dev), s=d(s), x=d(x):
+                  bonsai.t5_matmul(c, s, x, out=o), (2, 3000)))
+    w, a, b, x = synth.make_q1a(1, 9000, 1024, 3, "thr6")
+    cases.append(("q1a_matmul M=1", lambda o, w=d(w), a=d(a), b=d(b), x=d(x):
+                  bonsai.q1a_matmul(w, a, b, x, out=o), (1, 9000)))
+    torch.cuda.synchronize()
+
+    expected = []
+    for name, fn, shape in cases:
+        note(f"concurrency reference {name}")
+        o = torch.empty(shape, dtype=torch.float32, device=dev)
+        fn(o)
+        torch.cuda.synchronize()
+        expected.append(o.cpu().numpy())
+
+    threads, reps = 4, 3
+    outs = [[torch.full(shape, float("nan"), dtype=torch.float32, device=dev) for _, _, shape in cases]
+            for _ in range(threads)]
+    torch.cuda.synchronize()
+    errors = []
+
+    def worker(t):
+        try:
+            stream = torch.cuda.Stream(device=dev)
+            order = list(range(len(cases)))
+            np.random.default_rng(t).shuffle(order)
+            with torch.cuda.stream(stream):
+                for _ in range(reps):
+                    for i in order:
+                        cases[i][1](outs[t][i])
+            stream.synchronize()
+        except Exception as e:      # reported by the main thread
+            errors.append(f"thread {t}: {e!r}")
+
+    note(f"concurrency: {threads} threads x {reps} passes over {len(cases)} entry points")
+    pool = [threading.Thread(target=worker, args=(t,)) for t in range(threads)]
+    for th in pool:
+        th.start()
+    for th in pool:
+        th.join(timeout=120)
+    assert not any(th.is_alive() for th in pool), "a worker thread did not finish"
+    assert not errors, errors
+    torch.cuda.synchronize()
+    for t in range(threads):
+        for i, (name, _, _) in enumerate(cases):
+            got = outs[t][i].cpu().numpy()
+            assert np.array_equal(got.view(np.uint32), expected[i].view(np.uint32)), f"thread {t}: {name}"
