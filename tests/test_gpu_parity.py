@@ -699,3 +699,19 @@ def test_concurrent_calls_from_threads_on_their_own_streams():
         for i, (name, _, _) in enumerate(cases):
             got = outs[t][i].cpu().numpy()
             assert np.array_equal(got.view(np.uint32), expected[i].view(np.uint32)), f"thread {t}: {name}"
+
+
+# ---- the C ABI from plain C ---------------------------------------------------------------
+def test_c_abi_from_plain_c():
+    """tests/c_abi/abi_from_c.c (built by __graft_entry__.build()): host pack, HIP device buffers
+    and a stream, then the binary, affine, ternary and base-3 entry points from C alone, checked
+    bit for bit on exactly representable inputs, and the refused calls' statuses."""
+    import subprocess
+    from pathlib import Path
+
+    exe = Path(__file__).resolve().parent / "c_abi" / "_build" / "abi_from_c"
+    assert exe.exists(), f"{exe} is missing: run `python -c 'import __graft_entry__ as g; g.build()'`"
+    note("C ABI program")
+    r = subprocess.run([str(exe)], capture_output=True, text=True, timeout=120)
+    assert r.returncode == 0, f"exit {r.returncode}:\n{r.stdout}{r.stderr}"
+    assert "all checks passed" in r.stdout
