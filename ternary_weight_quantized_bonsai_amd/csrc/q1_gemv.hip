@@ -103,7 +103,6 @@ struct L4 {
     static constexpr int lpr = 64 / ROWS;               // lanes per row
     static constexpr int gpw = GPL * lpr;               // groups per wave
     static_assert(gpw >= 4 && gpw <= 8, "a wave's x (gpw * 256 B) is staged by whole 1 KB copies");
-    static_assert(!AFF || GPL == 4, "the affine group sums assume four groups per lane");
     static constexpr int tile = ROWS * gpw * 16;        // 4 KB of cells (2 KB at GPL 2)
     static constexpr int lut = gpw * kLutBytes;         // tables; x is staged in the first gpw * 256 B
     static constexpr int scales = ROWS * gpw * 4;       // 1 KB: one dword per (row, group) at most;
@@ -295,7 +294,11 @@ __global__ __launch_bounds__((L4<ROWS, AFF, GPL>::max_waves * 64)) void q1_gemv_
             const uint16_t bbits = (uint16_t)(PAIRS ? bw[u >> 1] >> (16 * (u & 1)) : bw[u]);
             const float ha = live ? 0.5f * f16_bits_to_f32(sbits) : 0.f;          // a / 2
             const float hb = live ? ha + f16_bits_to_f32(bbits) : 0.f;           // a / 2 + b
-            const float xu = (L::gpw == 8 && h) ? xs1[u] : xs0[u];
+            // X of this lane's group GPL h + u of the wave's
+            float xu;
+            if constexpr (L::gpw == 8) xu = h ? xs1[u] : xs0[u];
+            else if constexpr (GPL == 4) xu = xs0[u];
+            else xu = h ? xs0[2 + u] : xs0[u];
             acc = fmaf(ha, (a0 + a1) + (a2 + a3), acc);
             acc = fmaf(hb, xu, acc);
         } else {
@@ -548,7 +551,8 @@ hipError_t launch_lutp(const uint32_t *wbits, const uint16_t *scales, const uint
 bool q1a_lut_fits(int N, int K)
 {
     const int G = K / 128;
-    const bool fits32 = (G + L4<32, true>::gpw - 1) / L4<32, true>::gpw <= L4<32, true>::max_waves;
+    const bool fits32 = (G + L4<32, true, 2>::gpw - 1) / L4<32, true, 2>::gpw <= L4<32, true, 2>::max_waves ||
+                        (G + L4<32, true>::gpw - 1) / L4<32, true>::gpw <= L4<32, true>::max_waves;
     const bool fits64 = (G + L4<64, true>::gpw - 1) / L4<64, true>::gpw <= L4<64, true>::max_waves;
     return (fits32 && ((int64_t)N + 31) / 32 <= 256) || (fits64 && ((int64_t)N + 63) / 64 <= 6 * 256);
 }
@@ -556,9 +560,15 @@ bool q1a_lut_fits(int N, int K)
 hipError_t launch_q1a_lut(const uint32_t *wbits, const uint16_t *scales, const uint16_t *biases, const uint16_t *x,
                           float *y, int N, int K, hipStream_t stream)
 {
+    // as the binary route: 32-row tiles while one round of 256 CUs holds them, with two groups
+    // per lane where their waves fit, then 64-row tiles
     const int G = K / 128;
+    const bool one_round32 = ((int64_t)N + 31) / 32 <= 256;
+    using A2 = L4<32, true, 2>;
+    if (one_round32 && (G + A2::gpw - 1) / A2::gpw <= A2::max_waves)
+        return launch_lut4<32, true, 2>(wbits, scales, biases, x, y, N, K, stream);
     const bool fits32 = (G + L4<32, true>::gpw - 1) / L4<32, true>::gpw <= L4<32, true>::max_waves;
-    if (fits32 && ((int64_t)N + 31) / 32 <= 256) return launch_lut4<32, true>(wbits, scales, biases, x, y, N, K, stream);
+    if (fits32 && one_round32) return launch_lut4<32, true>(wbits, scales, biases, x, y, N, K, stream);
     if (!q1a_lut_fits(N, K)) return hipErrorInvalidValue;
     return launch_lut4<64, true>(wbits, scales, biases, x, y, N, K, stream);
 }
