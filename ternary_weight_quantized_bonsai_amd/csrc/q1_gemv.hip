@@ -554,7 +554,9 @@ bool q1a_lut_fits(int N, int K)
     const bool fits32 = (G + L4<32, true, 2>::gpw - 1) / L4<32, true, 2>::gpw <= L4<32, true, 2>::max_waves ||
                         (G + L4<32, true>::gpw - 1) / L4<32, true>::gpw <= L4<32, true>::max_waves;
     const bool fits64 = (G + L4<64, true>::gpw - 1) / L4<64, true>::gpw <= L4<64, true>::max_waves;
-    return (fits32 && ((int64_t)N + 31) / 32 <= 256) || (fits64 && ((int64_t)N + 63) / 64 <= 6 * 256);
+    // 64-row tiles at any N: the affine form has no persistent kernel, and the tiles beat the
+    // matrix-core kernel at every N timed (N = 248320: about 2x)
+    return (fits32 && ((int64_t)N + 31) / 32 <= 256) || fits64;
 }
 
 hipError_t launch_q1a_lut(const uint32_t *wbits, const uint16_t *scales, const uint16_t *biases, const uint16_t *x,

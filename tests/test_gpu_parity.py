@@ -430,7 +430,9 @@ def test_affine_matmul_vs_oracle(M, N, K, orc):
     assert_close(y, yref, _affine_magnitude(orc, w, a, b, x), f"q1a M={M} N={N} K={K}")
 
 
-@pytest.mark.parametrize("M,N,K", [(1, 5120, 5120), (8, 13824, 5120)])
+@pytest.mark.parametrize("M,N,K", [(1, 5120, 5120), (8, 13824, 5120),
+                                   # one row of x past six rounds of 64-row tiles (ragged N, odd G)
+                                   (1, 100003, 1152)])
 def test_affine_matmul_decode_shapes_sampled(M, N, K, orc):
     w, a, b, x = synth.make_q1a(M, N, K, 0, f"aff{N}x{K}")
     y = _affine(w, a, b, x)
