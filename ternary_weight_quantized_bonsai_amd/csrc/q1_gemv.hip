@@ -355,19 +355,27 @@ hipError_t launch_lut4(const uint32_t *wbits, const uint16_t *scales, const uint
 // i + 1 are in flight while batch i is looked up.  Every iteration issues exactly one batch's
 // copies (past the wave's last batch, that batch again), so one wait with a fixed count finds
 // the older batch landed.
+// AFF: affine 1-bit weights, as in the tile kernels: the biases travel with the scales, and X,
+// the plain sum of x over each group, is added up once per workgroup while the tables are built
+// (held in LDS beside them); a group then contributes (a / 2) D + (a / 2 + b) X.
 constexpr int kLPGroups = 4;
 constexpr int kLPTile = 64 * kLPGroups * 16;        // 4 KB of cells per batch
 constexpr int kLPScales = 64 * kLPGroups * 4;       // 1 KB: one dword per (row, group) at most
 constexpr int kLPBuf = kLPTile + kLPScales;         // 5 KB; buffer 1 first stages the wave's x
 constexpr int kLPMaxWaves = 8;
 constexpr int kLPMaxPer = kLPBuf / 256;             // groups of x one buffer can stage
+// buffer bytes (AFF: the biases follow the scales) and the LDS bytes for X of every group
+constexpr int lp_buf(bool aff) { return aff ? kLPBuf + kLPScales : kLPBuf; }
+constexpr int lp_xsum_bytes(int GT, bool aff) { return aff ? (4 * GT + 15) / 16 * 16 : 0; }
 
-template <bool PAIRS>
+template <bool PAIRS, bool AFF>
 __global__ __launch_bounds__(kLPMaxWaves * 64) void q1_gemv_lutp_kernel(const uint32_t *__restrict__ wbits,
                                                                         const uint16_t *__restrict__ scales,
+                                                                        const uint16_t *__restrict__ biases,
                                                                         const uint16_t *__restrict__ x,
                                                                         float *__restrict__ y, int N, int K)
 {
+    constexpr int BUF = lp_buf(AFF);
     extern __shared__ u32x4 lds[];
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -376,20 +384,21 @@ __global__ __launch_bounds__(kLPMaxWaves * 64) void q1_gemv_lutp_kernel(const ui
     const int nb = (G + kLPGroups - 1) / kLPGroups;         // batches per tile
     const int GT = kLPGroups * nb;                          // groups with tables (past G: scale 0)
     char *const tables = reinterpret_cast<char *>(lds);     // group g at tables + 2 KB g
-    char *const bufs = tables + GT * kLutBytes + wave * (2 * kLPBuf);
+    float *const xsum = reinterpret_cast<float *>(tables + GT * kLutBytes);   // AFF: X of group g
+    char *const bufs = tables + GT * kLutBytes + lp_xsum_bytes(GT, AFF) + wave * (2 * BUF);
     const int tiles = (N + 63) / 64;
     const int W = gridDim.x * nwaves;
     const int gw = wave * gridDim.x + blockIdx.x;
     const int nbat = (gw < tiles ? (tiles - 1 - gw) / W + 1 : 0) * nb;     // this wave's batches
     const u32x4 *wg = reinterpret_cast<const u32x4 *>(wbits);
-    constexpr int kCopies = 4 + (PAIRS ? 2 : 4);            // copies per batch
+    constexpr int kCopies = 4 + (PAIRS ? 2 : 4) * (AFF ? 2 : 1);   // copies per batch
 
     // batch i of this wave (tile i / nb, groups 4 (i % nb) ..) into buffer i % 2
     auto issue = [&](int i) {
         const int ic = min(i, max(nbat - 1, 0));
         const int n0 = (gw + W * (ic / nb)) * 64;           // rows clamp to N - 1 (a wave without tiles too)
         const int g0 = kLPGroups * (ic % nb);
-        char *const buf = bufs + (i & 1) * kLPBuf;
+        char *const buf = bufs + (i & 1) * BUF;
         // cells: copy k covers rows 16 k .. 16 k + 15, 4 lanes per row; cell (r, u) at 64 r + 16 (u ^ ((r >> 2) & 3))
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
@@ -400,15 +409,21 @@ __global__ __launch_bounds__(kLPMaxWaves * 64) void q1_gemv_lutp_kernel(const ui
         }
         // scales of row `lane`: PAIRS, copy p brings groups g0 + 2p, g0 + 2p + 1 as the dword at
         // buf + 4 KB + 256 p + 4 lane; else copy u brings group g0 + u as that dword's low half
+        // (AFF: the biases likewise, 1 KB further)
         const size_t rbase = (size_t)min(n0 + lane, N - 1) * G;
 #pragma unroll
-        for (int k = 0; k < (PAIRS ? 2 : 4); ++k) {
-            if constexpr (PAIRS)
-                __builtin_amdgcn_global_load_lds((glb_void_t *)(scales + rbase + min(g0 + 2 * k, G - 2)),
-                                                 (lds_void_t *)(buf + kLPTile + 256 * k), 4, 0, 0);
-            else
-                __builtin_amdgcn_global_load_lds((glb_void_t *)(scales + rbase + min(g0 + k, G - 1)),
-                                                 (lds_void_t *)(buf + kLPTile + 256 * k), 2, 0, 0);
+        for (int which = 0; which < (AFF ? 2 : 1); ++which) {
+            const uint16_t *const src = which ? biases : scales;
+            char *const dst = buf + kLPTile + kLPScales * which;
+#pragma unroll
+            for (int k = 0; k < (PAIRS ? 2 : 4); ++k) {
+                if constexpr (PAIRS)
+                    __builtin_amdgcn_global_load_lds((glb_void_t *)(src + rbase + min(g0 + 2 * k, G - 2)),
+                                                     (lds_void_t *)(dst + 256 * k), 4, 0, 0);
+                else
+                    __builtin_amdgcn_global_load_lds((glb_void_t *)(src + rbase + min(g0 + k, G - 1)),
+                                                     (lds_void_t *)(dst + 256 * k), 2, 0, 0);
+            }
         }
     };
 
@@ -416,7 +431,7 @@ __global__ __launch_bounds__(kLPMaxWaves * 64) void q1_gemv_lutp_kernel(const ui
     // lane l brings x[128 ga + 512 j + 8 l .. + 7] (clamped inside x) to buffer 1 + 1 KB j + 16 l
     const int per = (GT + nwaves - 1) / nwaves;             // at most kLPMaxPer (host check)
     const int ga = min(GT, wave * per), gb = min(GT, ga + per);
-    char *const xs = bufs + kLPBuf;
+    char *const xs = bufs + BUF;
     const u32x4 *xg = reinterpret_cast<const u32x4 *>(x);
     for (int j = 0; j < (gb - ga + 3) / 4; ++j)
         __builtin_amdgcn_global_load_lds((glb_void_t *)(xg + min(16 * ga + 64 * j + lane, 16 * G - 1)),
@@ -435,8 +450,10 @@ __global__ __launch_bounds__(kLPMaxWaves * 64) void q1_gemv_lutp_kernel(const ui
     for (int kb = 0; kb < nq; kb += 8) {
         uint2 xq[8];
         if (kb == 0) {
-            if constexpr (PAIRS) BONSAI_L4_XREAD8("s_waitcnt vmcnt(6)\n\t", xq, xa);
-            else BONSAI_L4_XREAD8("s_waitcnt vmcnt(8)\n\t", xq, xa);
+            // x landed once at most batch 0's copies are in flight
+            if constexpr (kCopies == 6) BONSAI_L4_XREAD8("s_waitcnt vmcnt(6)\n\t", xq, xa);
+            else if constexpr (kCopies == 8) BONSAI_L4_XREAD8("s_waitcnt vmcnt(8)\n\t", xq, xa);
+            else BONSAI_L4_XREAD8("s_waitcnt vmcnt(12)\n\t", xq, xa);
         } else {
             BONSAI_L4_XREAD8("", xq, xa + 128 * kb);
         }
@@ -455,6 +472,24 @@ __global__ __launch_bounds__(kLPMaxWaves * 64) void q1_gemv_lutp_kernel(const ui
             ev[3] = __builtin_bit_cast(uint32_t, fmaf(2.f, x1, fmaf(2.f, x0, base)));  // v = 4bt + 3
             lds_store_b128(tl + 1024 * (kb + k), ev);
         }
+        if constexpr (AFF) {
+            // X of groups ga + (kb + k) / 2 (quads k, k + 1): one lane of the four that hold a
+            // quad contributes, and a fixed butterfly adds across the wave
+#pragma unroll
+            for (int k = 0; k < 8; k += 2) {
+                if (kb + k >= nq) break;
+                float t = 0.f;
+#pragma unroll
+                for (int kk = k; kk < k + 2; ++kk) {
+                    const half2_t p01 = as_half2(xq[kk].x), p23 = as_half2(xq[kk].y);
+                    t += ((float)p01[0] + (float)p01[1]) + ((float)p23[0] + (float)p23[1]);
+                }
+                t = (lane & 3) == 0 ? t : 0.f;
+#pragma unroll
+                for (int off = 32; off >= 1; off >>= 1) t += __shfl_xor(t, off);
+                if (lane == 0) xsum[ga + (kb + k) / 2] = t;
+            }
+        }
     }
     issue(1);                                       // buffer 1: its staged x has been read
     lgkm_wait0();                                   // this wave's tables are written ...
@@ -466,10 +501,13 @@ __global__ __launch_bounds__(kLPMaxWaves * 64) void q1_gemv_lutp_kernel(const ui
     int b = 0, t = gw;                              // batch of the tile, tile
     for (int i = 0; i < nbat; ++i) {
         vm_wait<kCopies>();                         // batch i landed; batch i + 1 may be in flight
-        const char *buf = bufs + (i & 1) * kLPBuf;
-        uint32_t sw[PAIRS ? 2 : 4];
+        const char *buf = bufs + (i & 1) * BUF;
+        uint32_t sw[PAIRS ? 2 : 4], bw[AFF ? (PAIRS ? 2 : 4) : 1];
 #pragma unroll
-        for (int k = 0; k < (PAIRS ? 2 : 4); ++k) sw[k] = *reinterpret_cast<const uint32_t *>(buf + kLPTile + 256 * k + 4 * lane);
+        for (int k = 0; k < (PAIRS ? 2 : 4); ++k) {
+            sw[k] = *reinterpret_cast<const uint32_t *>(buf + kLPTile + 256 * k + 4 * lane);
+            if constexpr (AFF) bw[k] = *reinterpret_cast<const uint32_t *>(buf + kLPTile + kLPScales + 256 * k + 4 * lane);
+        }
         // tables of groups 4 b .. 4 b + 3 start at tbase + 8 KB b (256-aligned)
         uint32_t raddr[16];
 #pragma unroll
@@ -491,8 +529,17 @@ __global__ __launch_bounds__(kLPMaxWaves * 64) void q1_gemv_lutp_kernel(const ui
                 a3 += (tv[12] + tv[13]) + (tv[14] + tv[15]);
             }
             const uint16_t sbits = (uint16_t)(PAIRS ? sw[u >> 1] >> (16 * (u & 1)) : sw[u]);
-            const float s = (kLPGroups * b + u < G) ? f16_bits_to_f32(sbits) : 0.f;
-            acc = fmaf(s, (a0 + a1) + (a2 + a3), acc);
+            const bool live = kLPGroups * b + u < G;
+            if constexpr (AFF) {
+                const uint16_t bbits = (uint16_t)(PAIRS ? bw[u >> 1] >> (16 * (u & 1)) : bw[u]);
+                const float ha = live ? 0.5f * f16_bits_to_f32(sbits) : 0.f;          // a / 2
+                const float hb = live ? ha + f16_bits_to_f32(bbits) : 0.f;           // a / 2 + b
+                acc = fmaf(ha, (a0 + a1) + (a2 + a3), acc);
+                acc = fmaf(hb, xsum[kLPGroups * b + u], acc);
+            } else {
+                const float s = live ? f16_bits_to_f32(sbits) : 0.f;
+                acc = fmaf(s, (a0 + a1) + (a2 + a3), acc);
+            }
         }
         if (++b == nb) {                            // the tile is complete
             const int row = 64 * t + lane;
@@ -507,38 +554,44 @@ __global__ __launch_bounds__(kLPMaxWaves * 64) void q1_gemv_lutp_kernel(const ui
     vm_wait<0>();                                   // no copy into LDS outlives the wave
 }
 
-template <bool PAIRS>
-size_t lutp_lds(int G, int nwaves) { return (size_t)kLutBytes * 4 * ((G + 3) / 4) + (size_t)nwaves * 2 * kLPBuf; }
+template <bool AFF>
+size_t lutp_lds(int G, int nwaves)
+{
+    const int GT = 4 * ((G + 3) / 4);
+    return (size_t)kLutBytes * GT + lp_xsum_bytes(GT, AFF) + (size_t)nwaves * 2 * lp_buf(AFF);
+}
 
 // Waves per workgroup for the persistent kernel (0: the tables of K do not fit the LDS).
+template <bool AFF = false>
 int lutp_waves(int G)
 {
     const int GT = 4 * ((G + 3) / 4);
-    const long room = 160L * 1024 - (long)kLutBytes * GT;
-    int nw = room > 0 ? (int)(room / (2 * kLPBuf)) : 0;
+    const long room = 160L * 1024 - (long)kLutBytes * GT - lp_xsum_bytes(GT, AFF);
+    int nw = room > 0 ? (int)(room / (2 * lp_buf(AFF))) : 0;
     if (nw > kLPMaxWaves) nw = kLPMaxWaves;
-    if (nw < 4 || (GT + nw - 1) / nw > kLPMaxPer) return 0;
+    if (nw < 4 || (GT + nw - 1) / nw > lp_buf(AFF) / 256) return 0;
     return nw;
 }
 
-hipError_t launch_lutp(const uint32_t *wbits, const uint16_t *scales, const uint16_t *x, float *y,
-                       int N, int K, int nwaves, hipStream_t stream)
+template <bool AFF = false>
+hipError_t launch_lutp(const uint32_t *wbits, const uint16_t *scales, const uint16_t *biases, const uint16_t *x,
+                       float *y, int N, int K, int nwaves, hipStream_t stream)
 {
     constexpr int kCus = 256;
     const int G = K / 128;
     const int tiles = (N + 63) / 64;
     const int grid = min(kCus, (tiles + nwaves - 1) / nwaves);
-    const size_t lds = lutp_lds<true>(G, nwaves);
+    const size_t lds = lutp_lds<AFF>(G, nwaves);
     const bool pairs = (G % 2) == 0;
-    const void *fn = pairs ? reinterpret_cast<const void *>(&q1_gemv_lutp_kernel<true>)
-                           : reinterpret_cast<const void *>(&q1_gemv_lutp_kernel<false>);
+    const void *fn = pairs ? reinterpret_cast<const void *>(&q1_gemv_lutp_kernel<true, AFF>)
+                           : reinterpret_cast<const void *>(&q1_gemv_lutp_kernel<false, AFF>);
     static const bool attrs_set =
-        hipFuncSetAttribute(reinterpret_cast<const void *>(&q1_gemv_lutp_kernel<true>),
+        hipFuncSetAttribute(reinterpret_cast<const void *>(&q1_gemv_lutp_kernel<true, AFF>),
                             hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024) == hipSuccess &&
-        hipFuncSetAttribute(reinterpret_cast<const void *>(&q1_gemv_lutp_kernel<false>),
+        hipFuncSetAttribute(reinterpret_cast<const void *>(&q1_gemv_lutp_kernel<false, AFF>),
                             hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024) == hipSuccess;
     if (!attrs_set) return hipErrorInvalidValue;
-    void *args[] = {&wbits, &scales, &x, &y, &N, &K};
+    void *args[] = {&wbits, &scales, &biases, &x, &y, &N, &K};
     return launch_kernel(fn, dim3(grid), dim3(64 * nwaves), args, lds, stream);
 }
 
@@ -547,16 +600,16 @@ hipError_t launch_lutp(const uint32_t *wbits, const uint16_t *scales, const uint
 }  // namespace
 
 // Affine 1-bit weights, one row of x, on the table kernels: the binary routes of
-// launch_q1_gemv up to six rounds of 64-row tiles (the persistent kernel has no affine form).
+// launch_q1_gemv, with the persistent kernel only where K is long (below).
 bool q1a_lut_fits(int N, int K)
 {
     const int G = K / 128;
     const bool fits32 = (G + L4<32, true, 2>::gpw - 1) / L4<32, true, 2>::gpw <= L4<32, true, 2>::max_waves ||
                         (G + L4<32, true>::gpw - 1) / L4<32, true>::gpw <= L4<32, true>::max_waves;
     const bool fits64 = (G + L4<64, true>::gpw - 1) / L4<64, true>::gpw <= L4<64, true>::max_waves;
-    // 64-row tiles at any N: the affine form has no persistent kernel, and the tiles beat the
-    // matrix-core kernel at every N timed (N = 248320: about 2x)
-    return (fits32 && ((int64_t)N + 31) / 32 <= 256) || fits64;
+    // 64-row tiles at any N (they beat the matrix-core kernel at every N timed), and the
+    // persistent kernel, whose tables fit a little further in K
+    return (fits32 && ((int64_t)N + 31) / 32 <= 256) || fits64 || lutp_waves<true>(G) != 0;
 }
 
 hipError_t launch_q1a_lut(const uint32_t *wbits, const uint16_t *scales, const uint16_t *biases, const uint16_t *x,
@@ -572,6 +625,13 @@ hipError_t launch_q1a_lut(const uint32_t *wbits, const uint16_t *scales, const u
     const bool fits32 = (G + L4<32, true>::gpw - 1) / L4<32, true>::gpw <= L4<32, true>::max_waves;
     if (fits32 && one_round32) return launch_lut4<32, true>(wbits, scales, biases, x, y, N, K, stream);
     if (!q1a_lut_fits(N, K)) return hipErrorInvalidValue;
+    // past six rounds of 64-row tiles the persistent kernel, where K is long enough for its table
+    // build to pay (K = 5120: 65 us instead of 90 at N = 248320, 43 instead of 47 at N = 131072;
+    // K = 1152, N = 100003: the tiles, 11.3 us against 12.0)
+    const bool fits64 = (G + L4<64, true>::gpw - 1) / L4<64, true>::gpw <= L4<64, true>::max_waves;
+    if (fits64 && (((int64_t)N + 63) / 64 <= 6 * 256 || G < 32))
+        return launch_lut4<64, true>(wbits, scales, biases, x, y, N, K, stream);
+    if (const int nw = lutp_waves<true>(G)) return launch_lutp<true>(wbits, scales, biases, x, y, N, K, nw, stream);
     return launch_lut4<64, true>(wbits, scales, biases, x, y, N, K, stream);
 }
 
@@ -596,7 +656,7 @@ hipError_t launch_q1_gemv(const uint32_t *wbits, const uint16_t *scales, const u
     const int64_t tiles64 = ((int64_t)N + 63) / 64;
     if (fits32 && ((int64_t)N + 31) / 32 <= 256) return launch_lut4<32, false, 2>(wbits, scales, nullptr, x, y, N, K, stream);
     if (fits64 && tiles64 <= 6 * 256) return launch_lut4<64, false>(wbits, scales, nullptr, x, y, N, K, stream);
-    if (const int nw = lutp_waves(G)) return launch_lutp(wbits, scales, x, y, N, K, nw, stream);
+    if (const int nw = lutp_waves(G)) return launch_lutp(wbits, scales, nullptr, x, y, N, K, nw, stream);
     if (fits64) return launch_lut4<64, false>(wbits, scales, nullptr, x, y, N, K, stream);
     return launch_gemv_mfma(false, wbits, scales, x, y, M, N, K, stream);
 }

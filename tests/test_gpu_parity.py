@@ -432,7 +432,10 @@ def test_affine_matmul_vs_oracle(M, N, K, orc):
 
 @pytest.mark.parametrize("M,N,K", [(1, 5120, 5120), (8, 13824, 5120),
                                    # one row of x past six rounds of 64-row tiles (ragged N, odd G)
-                                   (1, 100003, 1152)])
+                                   (1, 100003, 1152),
+                                   # the persistent table kernel: paired and single scale copies,
+                                   # and K past the 64-row tiles' tables at small N
+                                   (1, 248320, 5120), (1, 110001, 4224), (1, 9000, 6528)])
 def test_affine_matmul_decode_shapes_sampled(M, N, K, orc):
     w, a, b, x = synth.make_q1a(M, N, K, 0, f"aff{N}x{K}")
     y = _affine(w, a, b, x)
@@ -453,7 +456,8 @@ def test_affine_bonsai_packing_matches_binary(M, N, K, orc):
     assert_close(y, yref, 3 * mag, "q1a as binary")
 
 
-@pytest.mark.parametrize("M,N,K", [(1, 300, 640), (1, 9000, 1024), (7, 260, 1024), (20, 129, 384)])
+@pytest.mark.parametrize("M,N,K", [(1, 300, 640), (1, 9000, 1024), (7, 260, 1024), (20, 129, 384),
+                                   (1, 110000, 4352)])
 def test_affine_integer_inputs_bit_exact(M, N, K, orc):
     """Small integer x, scales and biases: every partial sum is exact in float32, so the kernel
     must equal the exact result bit for bit."""
