@@ -625,11 +625,14 @@ hipError_t launch_q1a_lut(const uint32_t *wbits, const uint16_t *scales, const u
     const bool fits32 = (G + L4<32, true>::gpw - 1) / L4<32, true>::gpw <= L4<32, true>::max_waves;
     if (fits32 && one_round32) return launch_lut4<32, true>(wbits, scales, biases, x, y, N, K, stream);
     if (!q1a_lut_fits(N, K)) return hipErrorInvalidValue;
-    // past six rounds of 64-row tiles the persistent kernel, where K is long enough for its table
-    // build to pay (K = 5120: 65 us instead of 90 at N = 248320, 43 instead of 47 at N = 131072;
-    // K = 1152, N = 100003: the tiles, 11.3 us against 12.0)
+    // past six rounds of 64-row tiles the persistent kernel, except for short K at moderate N
+    // (timed: K = 5120, N = 248320: 65 us against 90 for the tiles; K = 2560 and 3072 at
+    // N = 100003 ... 248320: 18-39 us against 24-65; K = 1152 and 2048: the tiles lead by about
+    // 1 us up to N = 160000 and trail by 2.5 us at 248320)
+    const int64_t tiles64 = ((int64_t)N + 63) / 64;
+    const bool persist = tiles64 > 6 * 256 && (G >= 20 || tiles64 > 12 * 256);
     const bool fits64 = (G + L4<64, true>::gpw - 1) / L4<64, true>::gpw <= L4<64, true>::max_waves;
-    if (fits64 && (((int64_t)N + 63) / 64 <= 6 * 256 || G < 32))
+    if (fits64 && !persist)
         return launch_lut4<64, true>(wbits, scales, biases, x, y, N, K, stream);
     if (const int nw = lutp_waves<true>(G)) return launch_lutp<true>(wbits, scales, biases, x, y, N, K, nw, stream);
     return launch_lut4<64, true>(wbits, scales, biases, x, y, N, K, stream);
@@ -646,7 +649,10 @@ hipError_t launch_q1_gemv(const uint32_t *wbits, const uint16_t *scales, const u
     //   4.4 us instead of 5.3);
     // - 64-row tiles (one workgroup per CU, about 5 us a round) up to six rounds;
     // - beyond, the persistent kernel: about 15 us up front for the tables of all of K on every
-    //   CU, then about 0.15 ns a row, so it overtakes near 100k rows;
+    //   CU, then about 0.15 ns a row, so it overtakes near 100k rows.  Shorter K fits two or
+    //   more tiles' workgroups on a CU and builds fewer tables per tile, so there the tiles keep
+    //   the lead further: with K/128 < 28 they won at every N timed up to 200k rows (K = 1152 ...
+    //   3072: by 1 to 3.5 us), and below 16 up to 248320 as well;
     // - K too long for any of their tables in LDS: the matrix-core kernel, which measured 9.6 us
     //   against 15.7 for a table-lookup kernel that stages K in batches (N = 5120, K = 13824).
     const int G = K / 128;
@@ -655,7 +661,8 @@ hipError_t launch_q1_gemv(const uint32_t *wbits, const uint16_t *scales, const u
     const bool fits64 = (G + L4<64>::gpw - 1) / L4<64>::gpw <= L4<64>::max_waves;
     const int64_t tiles64 = ((int64_t)N + 63) / 64;
     if (fits32 && ((int64_t)N + 31) / 32 <= 256) return launch_lut4<32, false, 2>(wbits, scales, nullptr, x, y, N, K, stream);
-    if (fits64 && tiles64 <= 6 * 256) return launch_lut4<64, false>(wbits, scales, nullptr, x, y, N, K, stream);
+    const bool persist = tiles64 > 6 * 256 && (G >= 28 || (G >= 16 && tiles64 > 14 * 256));
+    if (fits64 && !persist) return launch_lut4<64, false>(wbits, scales, nullptr, x, y, N, K, stream);
     if (const int nw = lutp_waves(G)) return launch_lutp(wbits, scales, nullptr, x, y, N, K, nw, stream);
     if (fits64) return launch_lut4<64, false>(wbits, scales, nullptr, x, y, N, K, stream);
     return launch_gemv_mfma(false, wbits, scales, x, y, M, N, K, stream);

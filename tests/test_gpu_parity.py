@@ -154,6 +154,9 @@ EDGE = {
                 (1, 8192, 640), (1, 8193, 640), (1, 16384, 384), (1, 16385, 1152), (1, 20000, 640),
                 (1, 40000, 256), (1, 17000, 6144), (1, 98304, 384), (1, 98305, 384), (1, 100003, 640),
                 (1, 16500, 8192), (1, 5000, 7808),
+                # the persistent kernel past six rounds for long K, past 14 rounds for middling K,
+                # and where K is past the 64-row tiles' tables
+                (1, 100003, 3712), (1, 230001, 2176), (1, 9000, 6784),
                 # 32-row tiles at two groups per lane, up to their 60 groups (G even and odd)
                 (1, 3000, 7680), (1, 2999, 7552)],
     "q2t_gemv": [(1, 1, 128), (1, 63, 256), (2, 65, 384), (8, 1000, 1152), (7, 777, 2048),
@@ -435,7 +438,9 @@ def test_affine_matmul_vs_oracle(M, N, K, orc):
                                    (1, 100003, 1152),
                                    # the persistent table kernel: paired and single scale copies,
                                    # and K past the 64-row tiles' tables at small N
-                                   (1, 248320, 5120), (1, 110001, 4224), (1, 9000, 6528)])
+                                   (1, 248320, 5120), (1, 110001, 4224), (1, 9000, 6528),
+                                   # short K: the persistent kernel only past 12 rounds of tiles
+                                   (1, 200003, 1152)])
 def test_affine_matmul_decode_shapes_sampled(M, N, K, orc):
     w, a, b, x = synth.make_q1a(M, N, K, 0, f"aff{N}x{K}")
     y = _affine(w, a, b, x)
