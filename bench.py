@@ -550,26 +550,29 @@ def main() -> int:
             del cs, ss, c5, s5, x5, y
         extra["ternary_base3_gemv"] = {"shape": "N=5120 K=5120, 1.725 bits per weight", **t5r}
 
-        # Affine 1-bit form (MLX's scale and bias per group): decode at the MLP shape
+        # Affine 1-bit form (MLX's scale and bias per group): decode at the MLP shape, and one row
+        # of x at the LM-head shape
         aff = {}
-        for M7 in (1, 8):
-            w, a7, b7, x = (up(v) for v in synth.make_q1a(M7, N4, K))
-            nb7 = q1_bytes(N4, K) + 2 * N4 * (K // 128)            # + the biases
+        for M7, N7 in ((1, N4), (8, N4), (1, N3)):
+            w, a7, b7, x = (up(v) for v in synth.make_q1a(M7, N7, K))
+            nb7 = q1_bytes(N7, K) + 2 * N7 * (K // 128)            # + the biases
             R7 = max(3, math.ceil(ROTATE_BYTES / nb7))
             ws = [w] + [w.clone() for _ in range(R7 - 1)]
             as_ = [a7] + [a7.clone() for _ in range(R7 - 1)]
             bs = [b7] + [b7.clone() for _ in range(R7 - 1)]
-            y = torch.empty((M7, N4), dtype=torch.float32, device=dev)
+            y = torch.empty((M7, N7), dtype=torch.float32, device=dev)
             bonsai.q1a_matmul(ws[0], as_[0], bs[0], x, out=y)
             kt7 = kernel_times(hip, bonsai, [lambda j=j: bonsai.q1a_matmul(ws[j % R7], as_[j % R7], bs[j % R7], x, out=y)
-                                             for j in range(R7)])
+                                             for j in range(R7 if N7 == N4 else 4 * R7)])
             t7 = float(np.mean(kt7))
             gb7 = nb7 / (t7 / 1e3) / 1e9
-            aff[f"M{M7}"] = {"avg_kernel_us": round(t7 * 1e3, 2), "packed_weight_GBps": round(gb7, 1),
+            aff[(M7, N7)] = {"avg_kernel_us": round(t7 * 1e3, 2), "packed_weight_GBps": round(gb7, 1),
                              "frac_of_8TBps": round(gb7 / PEAK_HBM_GBPS, 4)}
-            log(f"affine M={M7}: {t7 * 1e3:.2f} us, {gb7:.1f} GB/s")
+            log(f"affine M={M7} N={N7}: {t7 * 1e3:.2f} us, {gb7:.1f} GB/s")
             del ws, as_, bs, w, a7, b7, x, y
-        extra["affine_gemv"] = {"shape": "N=13824 K=5120, 1-bit affine (scale + bias per group)", **aff}
+        extra["affine_gemv"] = {"shape": "N=13824 K=5120, 1-bit affine (scale + bias per group)",
+                                "M1": aff[(1, N4)], "M8": aff[(8, N4)]}
+        extra["affine_lm_head_gemv"] = {"shape": "M=1 N=248320 K=5120, 1-bit affine", **aff[(1, N3)]}
 
         # Embedding gather: 512 token ids from the binary vocabulary table (V = 248320, K = 5120)
         w, s, _ = (up(v) for v in synth.make_q1(1, N3, K))
