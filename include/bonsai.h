@@ -166,8 +166,44 @@ const char *bonsai_last_device_error(void);
  * hipExtLaunchKernel, recording start_event when the kernel starts executing and stop_event
  * when it completes, so hipEventElapsedTime(start, stop) is that kernel's device duration.
  * The events are hipEvent_t handles created and owned by the caller (either may be NULL);
- * the hook is consumed by that one call.  Do not arm it around stream capture. */
+ * the hook is consumed by that one call, whatever it returns: a call that fails its argument
+ * checks or enqueues nothing disarms it too.  Do not arm it around stream capture. */
 bonsai_status bonsai_time_next_launch(void *start_event, void *stop_event);
+
+/* Launch plan (diagnostic).  Describes the kernel launch that a GPU entry point would enqueue
+ * for these sizes, without reading or writing device memory and without launching anything:
+ * "<kernel> grid=<x>,<y> block=<threads> lds=<bytes>" (NUL-terminated, truncated to len bytes),
+ * followed by " timed" when the measurement hook below was armed and would time that launch (the
+ * plan consumes the hook like a launch would); "none" when the call would enqueue nothing
+ * (M == 0 or N == 0).  <kernel> is the launcher's name and template arguments.  op selects the entry point:
+ * 0 bonsai_q1_gemv, 1 bonsai_q1_gemm, 2 bonsai_q2t_gemv, 3 bonsai_q2t_gemm, 4 bonsai_t5_matmul,
+ * 5 bonsai_q1a_matmul, 6 bonsai_q1_embed (M = n_ids, N = V).  cus > 0 plans for a device with
+ * that many compute units and makes no HIP call at all (so it runs on a host without a GPU; the
+ * kernels' register counts are then taken as unknown, i.e. 8 waves per SIMD); cus <= 0 plans
+ * for the calling thread's current device.  Returns what the entry point would return (its
+ * argument checks run), or BONSAI_ERR_VALUE for an unknown op.  buf may be NULL. */
+bonsai_status bonsai_plan(int op, int64_t M, int64_t N, int64_t K, int cus, char *buf, int64_t len);
+
+/* Stream probe (diagnostic; the decode GEMVs are bound by memory bandwidth -- model card,
+ * cross-platform throughput -- and this gives the rate a kernel that only moves bytes reaches
+ * on the same device).  Streams `bytes` of device memory at buf once, one workgroup of eight
+ * waves per compute unit:
+ *   mode 0: reads by 16-byte vector loads (non-temporal);
+ *   mode 1: reads by direct global->LDS copies of 16 bytes per lane, three 1 KB copies in
+ *           flight per wave (the load path of the table GEMVs);
+ *   mode 2: writes zeros over the buffer.
+ * bytes: a positive multiple of 1024.  sink: device buffer of at least 64 KiB; modes 0 and 1
+ * store one word per wave there (a digest of the bytes read, so that no load is dead); mode 2
+ * leaves it alone.  buf and sink must be 16-byte aligned. */
+bonsai_status bonsai_probe_stream(void *buf, int64_t bytes, int mode, uint32_t *sink, void *hip_stream);
+
+/* Clock probe (diagnostic).  One wave stores the shader clock counter (s_memtime) and the
+ * 100 MHz real-time counter (s_memrealtime), waits until spin_ns nanoseconds of real time have
+ * passed (0 <= spin_ns <= 1e9), and stores both again: stamps = device uint64 [4] = {memtime0,
+ * realtime0, memtime1, realtime1}.  The shader clock over that interval is
+ * 100 MHz * (memtime1 - memtime0) / (realtime1 - realtime0).  Run beside a workload on another
+ * stream, it reads the clock the workload runs at. */
+bonsai_status bonsai_probe_clock(uint64_t *stamps, int64_t spin_ns, void *hip_stream);
 
 /* Static, NUL-terminated description of a status value. */
 const char *bonsai_status_str(bonsai_status s);

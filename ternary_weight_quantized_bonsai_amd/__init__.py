@@ -53,6 +53,12 @@ _lib.bonsai_q1_from_affine.argtypes = [_vp, _vp, _c_i64, _vp]
 _lib.bonsai_q1_from_affine.restype = ctypes.c_int
 _lib.bonsai_q1_embed.argtypes = [_vp, _vp, _vp, _vp, _c_i64, _c_i64, _c_i64, _vp]
 _lib.bonsai_q1_embed.restype = ctypes.c_int
+_lib.bonsai_plan.argtypes = [ctypes.c_int, _c_i64, _c_i64, _c_i64, ctypes.c_int, ctypes.c_char_p, _c_i64]
+_lib.bonsai_plan.restype = ctypes.c_int
+_lib.bonsai_probe_stream.argtypes = [_vp, _c_i64, ctypes.c_int, _vp, _vp]
+_lib.bonsai_probe_stream.restype = ctypes.c_int
+_lib.bonsai_probe_clock.argtypes = [_vp, _c_i64, _vp]
+_lib.bonsai_probe_clock.restype = ctypes.c_int
 _lib.bonsai_time_next_launch.argtypes = [_vp, _vp]
 _lib.bonsai_time_next_launch.restype = ctypes.c_int
 _lib.bonsai_last_device_error.argtypes = []
@@ -81,6 +87,42 @@ def time_next_launch(start_event: int, stop_event: int) -> None:
     """Arm the measurement hook: the next GPU call on this thread records the two hipEvent_t
     handles around its kernel's execution (bonsai_time_next_launch)."""
     _check("bonsai_time_next_launch", _lib.bonsai_time_next_launch(start_event, stop_event))
+
+
+PLAN_OPS = {"q1_gemv": 0, "q1_gemm": 1, "q2t_gemv": 2, "q2t_gemm": 3, "t5_matmul": 4, "q1a_matmul": 5,
+            "q1_embed": 6}
+
+
+def plan(op: str, M: int, N: int, K: int, cus: int = 0) -> str:
+    """The kernel launch the entry point `op` would enqueue for these sizes (bonsai_plan):
+    "<kernel> grid=x,y block=b lds=l", or "none".  cus > 0 plans for a device with that many
+    compute units without touching any GPU; cus = 0 plans for the current device."""
+    buf = ctypes.create_string_buffer(512)
+    _check("bonsai_plan", _lib.bonsai_plan(PLAN_OPS[op], M, N, K, cus, buf, len(buf)))
+    return buf.value.decode()
+
+
+def probe_stream(buf, nbytes: int, mode: int, sink) -> None:
+    """Stream nbytes of the device tensor buf once (mode 0: vector loads, 1: direct global->LDS
+    copies, 2: write zeros); sink: a device tensor of at least 64 KiB (bonsai_probe_stream)."""
+    import torch
+
+    if buf.numel() * buf.element_size() < nbytes or sink.numel() * sink.element_size() < 65536:
+        raise ValueError("buffer shorter than nbytes, or sink under 64 KiB")
+    stream = torch.cuda.current_stream(buf.device).cuda_stream
+    _check("bonsai_probe_stream", _lib.bonsai_probe_stream(buf.data_ptr(), nbytes, mode, sink.data_ptr(), stream))
+
+
+def probe_clock(stamps, spin_ns: int, stream: int | None = None) -> None:
+    """One wave stamps the shader and real-time clocks, waits spin_ns, stamps again into the
+    int64 device tensor stamps[4] (bonsai_probe_clock); on `stream` (a hipStream_t) if given."""
+    import torch
+
+    if stamps.dtype != torch.int64 or stamps.numel() < 4 or not stamps.is_cuda:
+        raise ValueError("stamps must be an int64 device tensor of 4 elements")
+    if stream is None:
+        stream = torch.cuda.current_stream(stamps.device).cuda_stream
+    _check("bonsai_probe_clock", _lib.bonsai_probe_clock(stamps.data_ptr(), spin_ns, stream))
 
 
 def _check(fn: str, status: int):

@@ -62,8 +62,8 @@ hipError_t launch_q1_embed(const uint32_t *wbits, const uint16_t *scales, const 
     int64_t blocks = (total + 255) / 256;
     if (blocks > 8192) blocks = 8192;
     void *args[] = {&wbits, &scales, &ids, &out, &n_ids, &V, &K};
-    return launch_kernel(reinterpret_cast<const void *>(&q1_embed_kernel), dim3((unsigned)blocks), dim3(256), args,
-                         0, stream);
+    return launch_kernel(reinterpret_cast<const void *>(&q1_embed_kernel), "q1_embed_kernel", dim3((unsigned)blocks),
+                         dim3(256), args, 0, stream);
 }
 
 }  // namespace bonsai

@@ -327,7 +327,6 @@ __global__ __launch_bounds__(sm_max_waves(RT) * 64) void gemv_mfma_kernel(const 
     }
 }
 
-constexpr int kLdsPerCu = 160 * 1024;
 
 // waves of a workgroup: one per slice of K, at most 16 and as many as the LDS holds
 template <bool TERN, bool AFF, int SG>
@@ -353,31 +352,17 @@ hipError_t launch_rt(const uint32_t *codes, const uint16_t *scales, const uint16
     if (blocks > INT_MAX || yblocks > 65535) return hipErrorInvalidValue;
     const void *fn = (K / 128) % 2 == 0 ? reinterpret_cast<const void *>(&gemv_mfma_kernel<TERN, AFF, RT, true, SG>)
                                         : reinterpret_cast<const void *>(&gemv_mfma_kernel<TERN, AFF, RT, false, SG>);
-    static const bool attr =
-        hipFuncSetAttribute(reinterpret_cast<const void *>(&gemv_mfma_kernel<TERN, AFF, RT, true, SG>),
-                            hipFuncAttributeMaxDynamicSharedMemorySize, kLdsPerCu) == hipSuccess &&
-        hipFuncSetAttribute(reinterpret_cast<const void *>(&gemv_mfma_kernel<TERN, AFF, RT, false, SG>),
-                            hipFuncAttributeMaxDynamicSharedMemorySize, kLdsPerCu) == hipSuccess;
-    if (!attr) return hipErrorInvalidValue;
+    if (!set_lds_limit(fn, kLdsPerCu)) return hipErrorInvalidValue;
     void *args[] = {&codes, &scales, &biases, &x, &y, &M, &N, &K};
-    return launch_kernel(fn, dim3((unsigned)blocks, (unsigned)yblocks), dim3(64 * nw), args, lds, stream);
+    return launch_kernel(fn, __PRETTY_FUNCTION__, dim3((unsigned)blocks, (unsigned)yblocks), dim3(64 * nw), args, lds,
+                         stream);
 }
 
-// waves of gemv_mfma_kernel<TERN, AFF, RT, PAIRS, SG> that one CU holds by registers: 512 VGPRs
-// per SIMD lane, in granules of 8, at most 8 waves per SIMD, 4 SIMDs
+// waves of gemv_mfma_kernel<TERN, AFF, RT, PAIRS, SG> that one CU holds by registers
 template <bool TERN, bool AFF, int RT, bool PAIRS, int SG>
 int sm_reg_waves_per_cu()
 {
-    static const int waves = [] {
-        hipFuncAttributes a;
-        if (hipFuncGetAttributes(&a, reinterpret_cast<const void *>(&gemv_mfma_kernel<TERN, AFF, RT, PAIRS, SG>)) !=
-                hipSuccess ||
-            a.numRegs <= 0)
-            return 8;
-        const int per_simd = 512 / ((a.numRegs + 7) / 8 * 8);
-        return 4 * (per_simd < 8 ? per_simd : 8);
-    }();
-    return waves;
+    return reg_waves_per_cu(func_vgprs(reinterpret_cast<const void *>(&gemv_mfma_kernel<TERN, AFF, RT, PAIRS, SG>)));
 }
 
 template <bool TERN, bool AFF, int RT, int SG>
@@ -412,7 +397,7 @@ inline int sm_simd_groups(int nw, int ns, int sg)
 template <bool TERN, bool AFF, int SG>
 SmChoice<TERN, AFF, SG> sm_choose(int M, int N, int K)
 {
-    constexpr int kCus = 256;
+    const int kCus = device_cus();
     const int mb = M < 16 ? M : 16;
     const bool pairs = (K / 128) % 2 == 0;
     using C = SmChoice<TERN, AFF, SG>;

@@ -31,9 +31,35 @@ hipError_t launch_t5_matmul(const uint8_t *codes, const uint16_t *scales, const 
 hipError_t launch_fill_zero(float *y, int64_t count, hipStream_t stream);
 hipError_t launch_q1_embed(const uint32_t *wbits, const uint16_t *scales, const int64_t *ids, uint16_t *out,
                            int64_t n_ids, int64_t V, int K, hipStream_t stream);
+// Measurement probes (probe.hip): a stream over device memory, and a clock stamp.
+hipError_t launch_probe_stream(void *buf, int64_t bytes, int mode, uint32_t *sink, hipStream_t stream);
+hipError_t launch_probe_clock(uint64_t *stamps, int64_t spin_ns, hipStream_t stream);
+
+// LDS bytes of one CU on gfx950.
+constexpr int kLdsPerCu = 160 * 1024;
+
+// Facts of the device the calling thread has current, looked up once per device (the routing
+// reads them on every call).  During a launch plan (bonsai_plan) the compute-unit count is the
+// planned one and no HIP call is made.
+int device_cus();
+// hipFuncSetAttribute(fn, MaxDynamicSharedMemorySize, bytes), once per (device, fn).
+bool set_lds_limit(const void *fn, int bytes);
+// VGPRs per lane of a kernel (hipFuncGetAttributes, once per (device, fn)); 0 if unknown.
+int func_vgprs(const void *fn);
+// Waves of a kernel that one CU holds by its registers: 512 VGPRs per SIMD lane, in granules of
+// 8, at most 8 waves per SIMD, 4 SIMDs (8 per SIMD when the register count is unknown).
+inline int reg_waves_per_cu(int vgprs)
+{
+    if (vgprs <= 0) return 32;
+    const int per_simd = 512 / ((vgprs + 7) / 8 * 8);
+    return 4 * (per_simd < 8 ? per_simd : 8);
+}
 
 // Every kernel launch of the library goes through here: a plain hipLaunchKernel, or, when the
-// caller armed the timing hook on this thread, hipExtLaunchKernel with the caller's events.
-hipError_t launch_kernel(const void *fn, dim3 grid, dim3 block, void **args, size_t lds, hipStream_t stream);
+// caller armed the timing hook for this call, hipExtLaunchKernel with the caller's events.
+// During a launch plan nothing is launched: the launch is recorded instead.  `name` is a
+// static description of the kernel (the launcher's signature with its template arguments).
+hipError_t launch_kernel(const void *fn, const char *name, dim3 grid, dim3 block, void **args, size_t lds,
+                         hipStream_t stream);
 
 }  // namespace bonsai

@@ -398,9 +398,11 @@ hipError_t launch_q1_gemm(const uint32_t *wbits, const uint16_t *scales, const u
     const int64_t tiles = (int64_t)((N + BN - 1) / BN) * ((M + BM - 1) / BM);
     if (tiles > INT_MAX || K % 128 != 0 || K <= 0) return hipErrorInvalidValue;
     void *args[] = {&wbits, &scales, &x, &y, &M, &N, &K};
-    const void *fn = (K % 1024 == 0) ? reinterpret_cast<const void *>(&q1_gemm_kernel<false, 16>)
-                                     : reinterpret_cast<const void *>(&q1_gemm_kernel<false, 2>);
-    return launch_kernel(fn, dim3((unsigned)tiles), dim3(256), args, 0, stream);
+    const bool s16 = K % 1024 == 0;
+    const void *fn = s16 ? reinterpret_cast<const void *>(&q1_gemm_kernel<false, 16>)
+                         : reinterpret_cast<const void *>(&q1_gemm_kernel<false, 2>);
+    return launch_kernel(fn, s16 ? "q1_gemm_kernel<false, 16>" : "q1_gemm_kernel<false, 2>", dim3((unsigned)tiles),
+                         dim3(256), args, 0, stream);
 }
 
 // Ternary prefill ("Ternary Bonsai 27B" article, cross-platform throughput: pp512) on the
@@ -412,9 +414,11 @@ hipError_t launch_q2t_gemm(const uint32_t *wcodes, const uint16_t *scales, const
     const int64_t tiles = (int64_t)((N + BN - 1) / BN) * ((M + BM - 1) / BM);
     if (tiles > INT_MAX || K % 128 != 0 || K <= 0) return hipErrorInvalidValue;
     void *args[] = {&wcodes, &scales, &x, &y, &M, &N, &K};
-    const void *fn = ((K / 128) % 2 == 0) ? reinterpret_cast<const void *>(&q1_gemm_kernel<true, 4>)
-                                          : reinterpret_cast<const void *>(&q1_gemm_kernel<true, 2>);
-    return launch_kernel(fn, dim3((unsigned)tiles), dim3(256), args, 0, stream);
+    const bool s4 = (K / 128) % 2 == 0;
+    const void *fn = s4 ? reinterpret_cast<const void *>(&q1_gemm_kernel<true, 4>)
+                        : reinterpret_cast<const void *>(&q1_gemm_kernel<true, 2>);
+    return launch_kernel(fn, s4 ? "q1_gemm_kernel<true, 4>" : "q1_gemm_kernel<true, 2>", dim3((unsigned)tiles),
+                         dim3(256), args, 0, stream);
 }
 
 }  // namespace bonsai

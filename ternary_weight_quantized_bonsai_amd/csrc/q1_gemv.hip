@@ -331,16 +331,9 @@ hipError_t launch_lut4(const uint32_t *wbits, const uint16_t *scales, const uint
     const bool pairs = (G % 2) == 0;                // a row's scale pairs are then dword aligned
     const void *fn = pairs ? reinterpret_cast<const void *>(&q1_gemv_lut4_kernel<ROWS, true, AFF, GPL>)
                            : reinterpret_cast<const void *>(&q1_gemv_lut4_kernel<ROWS, false, AFF, GPL>);
-    static const bool attrs_set = [] {
-        const int most = L::max_waves * L::wave;
-        return hipFuncSetAttribute(reinterpret_cast<const void *>(&q1_gemv_lut4_kernel<ROWS, true, AFF, GPL>),
-                                   hipFuncAttributeMaxDynamicSharedMemorySize, most) == hipSuccess &&
-               hipFuncSetAttribute(reinterpret_cast<const void *>(&q1_gemv_lut4_kernel<ROWS, false, AFF, GPL>),
-                                   hipFuncAttributeMaxDynamicSharedMemorySize, most) == hipSuccess;
-    }();
-    if (!attrs_set) return hipErrorInvalidValue;
+    if (!set_lds_limit(fn, L::max_waves * L::wave)) return hipErrorInvalidValue;
     void *args[] = {&wbits, &scales, &biases, &x, &y, &N, &K};
-    return launch_kernel(fn, dim3(tiles), dim3(64 * waves), args, lds, stream);
+    return launch_kernel(fn, __PRETTY_FUNCTION__, dim3(tiles), dim3(64 * waves), args, lds, stream);
 }
 
 // ---- M = 1, large N: persistent workgroups, tables built once ------------------------------
@@ -577,22 +570,16 @@ template <bool AFF = false>
 hipError_t launch_lutp(const uint32_t *wbits, const uint16_t *scales, const uint16_t *biases, const uint16_t *x,
                        float *y, int N, int K, int nwaves, hipStream_t stream)
 {
-    constexpr int kCus = 256;
     const int G = K / 128;
     const int tiles = (N + 63) / 64;
-    const int grid = min(kCus, (tiles + nwaves - 1) / nwaves);
+    const int grid = min(device_cus(), (tiles + nwaves - 1) / nwaves);
     const size_t lds = lutp_lds<AFF>(G, nwaves);
     const bool pairs = (G % 2) == 0;
     const void *fn = pairs ? reinterpret_cast<const void *>(&q1_gemv_lutp_kernel<true, AFF>)
                            : reinterpret_cast<const void *>(&q1_gemv_lutp_kernel<false, AFF>);
-    static const bool attrs_set =
-        hipFuncSetAttribute(reinterpret_cast<const void *>(&q1_gemv_lutp_kernel<true, AFF>),
-                            hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024) == hipSuccess &&
-        hipFuncSetAttribute(reinterpret_cast<const void *>(&q1_gemv_lutp_kernel<false, AFF>),
-                            hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024) == hipSuccess;
-    if (!attrs_set) return hipErrorInvalidValue;
+    if (!set_lds_limit(fn, kLdsPerCu)) return hipErrorInvalidValue;
     void *args[] = {&wbits, &scales, &biases, &x, &y, &N, &K};
-    return launch_kernel(fn, dim3(grid), dim3(64 * nwaves), args, lds, stream);
+    return launch_kernel(fn, __PRETTY_FUNCTION__, dim3(grid), dim3(64 * nwaves), args, lds, stream);
 }
 
 #undef BONSAI_L4_XREAD8
@@ -609,7 +596,7 @@ bool q1a_lut_fits(int N, int K)
     const bool fits64 = (G + L4<64, true>::gpw - 1) / L4<64, true>::gpw <= L4<64, true>::max_waves;
     // 64-row tiles at any N (they beat the matrix-core kernel at every N timed), and the
     // persistent kernel, whose tables fit a little further in K
-    return (fits32 && ((int64_t)N + 31) / 32 <= 256) || fits64 || lutp_waves<true>(G) != 0;
+    return (fits32 && ((int64_t)N + 31) / 32 <= device_cus()) || fits64 || lutp_waves<true>(G) != 0;
 }
 
 hipError_t launch_q1a_lut(const uint32_t *wbits, const uint16_t *scales, const uint16_t *biases, const uint16_t *x,
@@ -618,7 +605,8 @@ hipError_t launch_q1a_lut(const uint32_t *wbits, const uint16_t *scales, const u
     // as the binary route: 32-row tiles while one round of 256 CUs holds them, with two groups
     // per lane where their waves fit, then 64-row tiles
     const int G = K / 128;
-    const bool one_round32 = ((int64_t)N + 31) / 32 <= 256;
+    const int cus = device_cus();
+    const bool one_round32 = ((int64_t)N + 31) / 32 <= cus;
     using A2 = L4<32, true, 2>;
     if (one_round32 && (G + A2::gpw - 1) / A2::gpw <= A2::max_waves)
         return launch_lut4<32, true, 2>(wbits, scales, biases, x, y, N, K, stream);
@@ -630,7 +618,7 @@ hipError_t launch_q1a_lut(const uint32_t *wbits, const uint16_t *scales, const u
     // N = 100003 ... 248320: 18-39 us against 24-65; K = 1152 and 2048: the tiles lead by about
     // 1 us up to N = 160000 and trail by 2.5 us at 248320)
     const int64_t tiles64 = ((int64_t)N + 63) / 64;
-    const bool persist = tiles64 > 6 * 256 && (G >= 20 || tiles64 > 12 * 256);
+    const bool persist = tiles64 > 6 * cus && (G >= 20 || tiles64 > 12 * cus);
     const bool fits64 = (G + L4<64, true>::gpw - 1) / L4<64, true>::gpw <= L4<64, true>::max_waves;
     if (fits64 && !persist)
         return launch_lut4<64, true>(wbits, scales, biases, x, y, N, K, stream);
@@ -660,8 +648,9 @@ hipError_t launch_q1_gemv(const uint32_t *wbits, const uint16_t *scales, const u
     const bool fits32 = (G + L32::gpw - 1) / L32::gpw <= L32::max_waves;
     const bool fits64 = (G + L4<64>::gpw - 1) / L4<64>::gpw <= L4<64>::max_waves;
     const int64_t tiles64 = ((int64_t)N + 63) / 64;
-    if (fits32 && ((int64_t)N + 31) / 32 <= 256) return launch_lut4<32, false, 2>(wbits, scales, nullptr, x, y, N, K, stream);
-    const bool persist = tiles64 > 6 * 256 && (G >= 28 || (G >= 16 && tiles64 > 14 * 256));
+    const int cus = device_cus();
+    if (fits32 && ((int64_t)N + 31) / 32 <= cus) return launch_lut4<32, false, 2>(wbits, scales, nullptr, x, y, N, K, stream);
+    const bool persist = tiles64 > 6 * cus && (G >= 28 || (G >= 16 && tiles64 > 14 * cus));
     if (fits64 && !persist) return launch_lut4<64, false>(wbits, scales, nullptr, x, y, N, K, stream);
     if (const int nw = lutp_waves(G)) return launch_lutp(wbits, scales, nullptr, x, y, N, K, nw, stream);
     if (fits64) return launch_lut4<64, false>(wbits, scales, nullptr, x, y, N, K, stream);

@@ -50,7 +50,6 @@ constexpr int kT5LutBytes = 256 * 8;
 // tile takes about 160 VGPRs: the 8-wave build keeps them all, the 16-wave build fits in 128
 // (no spill) and lets a CU hold two 8-wave workgroups by registers.
 constexpr int t5_max_waves(bool wide) { return wide ? 16 : 8; }
-constexpr int kLdsPerCu = 160 * 1024;
 
 constexpr int t5_scale_bytes(int rt) { return (5 * 16 * rt + 63) / 64 * 256; }
 
@@ -263,20 +262,11 @@ size_t t5_lds(int rt, int mb, int nw)
     return (size_t)kT5LutBytes + (size_t)nw * t5_wave_bytes(rt, mb) + (size_t)nw * mb * 16 * rt * 4;
 }
 
-// waves of t5_gemv_kernel<RT> that one CU holds by registers: 512 VGPRs per SIMD lane, in
-// granules of 8, at most 8 waves per SIMD, 4 SIMDs
+// waves of t5_gemv_kernel<RT, WIDE> that one CU holds by registers
 template <int RT, bool WIDE>
 int t5_reg_waves_per_cu()
 {
-    static const int waves = [] {
-        hipFuncAttributes a;
-        if (hipFuncGetAttributes(&a, reinterpret_cast<const void *>(&t5_gemv_kernel<RT, WIDE>)) != hipSuccess ||
-            a.numRegs <= 0)
-            return 8;
-        const int per_simd = 512 / ((a.numRegs + 7) / 8 * 8);
-        return 4 * (per_simd < 8 ? per_simd : 8);
-    }();
-    return waves;
+    return reg_waves_per_cu(func_vgprs(reinterpret_cast<const void *>(&t5_gemv_kernel<RT, WIDE>)));
 }
 
 template <int RT, bool WIDE>
@@ -290,13 +280,11 @@ hipError_t t5_launch_rt(const uint8_t *codes, const uint16_t *scales, const uint
     const int64_t yblocks = ((int64_t)M + 15) / 16;
     if (blocks > INT_MAX || yblocks > 65535) return hipErrorInvalidValue;
     // dynamic LDS: everything but the static 2 KB byte table
-    static const bool attr = hipFuncSetAttribute(reinterpret_cast<const void *>(&t5_gemv_kernel<RT, WIDE>),
-                                                 hipFuncAttributeMaxDynamicSharedMemorySize,
-                                                 kLdsPerCu - kT5LutBytes) == hipSuccess;
-    if (!attr) return hipErrorInvalidValue;
+    const void *fn = reinterpret_cast<const void *>(&t5_gemv_kernel<RT, WIDE>);
+    if (!set_lds_limit(fn, kLdsPerCu - kT5LutBytes)) return hipErrorInvalidValue;
     void *args[] = {&codes, &scales, &x, &y, &M, &N, &K};
-    return launch_kernel(reinterpret_cast<const void *>(&t5_gemv_kernel<RT, WIDE>), dim3((unsigned)blocks, (unsigned)yblocks),
-                         dim3(64 * nw), args, t5_lds(RT, mb, nw) - kT5LutBytes, stream);
+    return launch_kernel(fn, __PRETTY_FUNCTION__, dim3((unsigned)blocks, (unsigned)yblocks), dim3(64 * nw), args,
+                         t5_lds(RT, mb, nw) - kT5LutBytes, stream);
 }
 
 }  // namespace
@@ -311,7 +299,7 @@ hipError_t launch_t5_matmul(const uint8_t *codes, const uint16_t *scales, const 
                             int M, int N, int K, hipStream_t stream)
 {
     if (M < 1) return hipErrorInvalidValue;
-    constexpr int kCus = 256;
+    const int kCus = device_cus();
     const int mb = M < 16 ? M : 16;
     auto rounds = [&](int rt, bool wide, int reg_waves) -> int64_t {
         const int nw = t5_waves(rt, wide, mb, K);

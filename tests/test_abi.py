@@ -282,3 +282,91 @@ def test_embed_validation():
     assert f(p, p, p, p, 4, -1, 128, None) == bonsai.ERR_SHAPE
     assert f(p, p, p + 8, p, 4, 10, 128, None) == bonsai.ERR_ALIGN
     assert f(p, p, p, p + 2, 4, 10, 128, None) == bonsai.ERR_ALIGN
+
+
+# ---- launch plans: the routing, on any compute-unit count, with no GPU ------------------
+def _plan_kernel(op, M, N, K, cus):
+    return bonsai.plan(op, M, N, K, cus).split(" grid=")[0]
+
+
+def _plan_grid(op, M, N, K, cus):
+    return int(bonsai.plan(op, M, N, K, cus).split(" grid=")[1].split(",")[0])
+
+
+def test_plan_names_each_route_of_the_decode_gemv():
+    # one row of x: 32-row table tiles while one round of the CUs holds them, 64-row tiles up
+    # to six rounds, then the persistent kernel; more rows of x go to the matrix cores
+    assert _plan_kernel("q1_gemv", 1, 5120, 5120, 256) == "launch_lut4[ROWS = 32, AFF = false, GPL = 2]"
+    assert _plan_kernel("q1_gemv", 1, 13824, 5120, 256) == "launch_lut4[ROWS = 64, AFF = false, GPL = 4]"
+    assert _plan_kernel("q1_gemv", 1, 248320, 5120, 256).startswith("launch_lut")
+    assert _plan_kernel("q1_gemv", 8, 5120, 5120, 256).startswith("launch_rt[TERN = false")
+    assert _plan_kernel("q1_gemm", 512, 13824, 5120, 256) == "q1_gemm_kernel<false, 16>"
+    assert _plan_kernel("q1_gemm", 512, 13824, 5248, 256) == "q1_gemm_kernel<false, 2>"
+    assert _plan_kernel("q2t_gemm", 512, 13824, 5120, 256) == "q1_gemm_kernel<true, 4>"
+    assert _plan_kernel("q2t_gemv", 1, 5120, 5120, 256).startswith("launch_rt[TERN = true")
+    assert _plan_kernel("t5_matmul", 1, 5120, 5120, 256).startswith("t5_launch_rt")
+    assert _plan_kernel("q1_embed", 512, 248320, 5120, 256) == "q1_embed_kernel"
+    assert bonsai.plan("q1_gemv", 0, 64, 128, 256) == "none"
+    assert bonsai.plan("q1_gemv", 1, 64, 0, 256).startswith("fill_zero_kernel")
+
+
+def test_plan_routing_follows_the_compute_unit_count():
+    # 32-row tiles run while one round of the device's CUs holds them: 5120 rows make 160 tiles
+    # of 32, so a device of 128 CUs takes 64-row tiles instead
+    assert _plan_kernel("q1_gemv", 1, 5120, 5120, 256).startswith("launch_lut4[ROWS = 32")
+    assert _plan_kernel("q1_gemv", 1, 5120, 5120, 160).startswith("launch_lut4[ROWS = 32")
+    assert _plan_kernel("q1_gemv", 1, 5120, 5120, 128).startswith("launch_lut4[ROWS = 64")
+    # the persistent LM-head kernel takes one workgroup per CU
+    for cus in (80, 256, 304):
+        plan = bonsai.plan("q1_gemv", 1, 248320, 5120, cus)
+        if plan.startswith("launch_lutp"):
+            assert _plan_grid("q1_gemv", 1, 248320, 5120, cus) == cus
+    # the small-M kernel's tiles always cover every row, whatever tile the CU count selects
+    for cus in (32, 64, 256, 304):
+        plan = bonsai.plan("q2t_gemv", 8, 5120, 5120, cus)
+        rows = int(plan.split("RT = ")[1].split(",")[0]) * 16
+        assert _plan_grid("q2t_gemv", 8, 5120, 5120, cus) * rows >= 5120
+
+
+def test_plan_runs_the_entry_points_argument_checks():
+    with pytest.raises(bonsai.BonsaiError) as e:
+        bonsai.plan("q1_gemv", 9, 64, 128, 256)
+    assert e.value.status == bonsai.ERR_SHAPE
+    with pytest.raises(bonsai.BonsaiError) as e:
+        bonsai.plan("q1_gemm", 4, 64, 100, 256)
+    assert e.value.status == bonsai.ERR_SHAPE
+    assert bonsai.raw().bonsai_plan(99, 1, 64, 128, 256, None, 0) == bonsai.ERR_VALUE
+
+
+def test_timing_hook_is_consumed_by_a_call_that_fails_or_enqueues_nothing():
+    lib = bonsai.raw()
+    ev = 0x7F0000001000            # stand-in event handles: planned launches never touch them
+    # armed: the next planned launch would be timed, and consumes the hook
+    assert lib.bonsai_time_next_launch(ev, ev) == bonsai.OK
+    assert bonsai.plan("q1_gemv", 1, 256, 512, 256).endswith(" timed")
+    assert not bonsai.plan("q1_gemv", 1, 256, 512, 256).endswith(" timed")
+    # a call that fails its argument checks consumes it too
+    for call, status in ((lambda: lib.bonsai_q1_gemv(FAKE, FAKE, FAKE, FAKE, 1, 64, 100, None), bonsai.ERR_SHAPE),
+                         (lambda: lib.bonsai_q1_gemm(None, FAKE, FAKE, FAKE, 1, 64, 128, None), bonsai.ERR_NULL),
+                         (lambda: lib.bonsai_q1_gemv(FAKE, FAKE, FAKE, FAKE, 0, 64, 128, None), bonsai.OK),
+                         (lambda: lib.bonsai_q1a_matmul(FAKE, FAKE, None, FAKE, FAKE, 1, 64, 128, None),
+                          bonsai.ERR_NULL),
+                         (lambda: lib.bonsai_q1_embed(FAKE, FAKE, FAKE, FAKE, 0, 10, 128, None), bonsai.OK),
+                         (lambda: lib.bonsai_probe_stream(FAKE, 1000, 0, FAKE, None), bonsai.ERR_SHAPE),
+                         (lambda: lib.bonsai_probe_clock(None, 10, None), bonsai.ERR_NULL)):
+        assert lib.bonsai_time_next_launch(ev, ev) == bonsai.OK
+        assert call() == status
+        assert not bonsai.plan("q1_gemv", 1, 256, 512, 256).endswith(" timed")
+
+
+def test_probe_validation():
+    lib = bonsai.raw()
+    assert lib.bonsai_probe_stream(FAKE, 1000, 0, FAKE, None) == bonsai.ERR_SHAPE     # not a multiple of 1 KiB
+    assert lib.bonsai_probe_stream(FAKE, 0, 0, FAKE, None) == bonsai.ERR_SHAPE
+    assert lib.bonsai_probe_stream(FAKE, 1024, 3, FAKE, None) == bonsai.ERR_SHAPE
+    assert lib.bonsai_probe_stream(None, 1024, 0, FAKE, None) == bonsai.ERR_NULL
+    assert lib.bonsai_probe_stream(FAKE, 1024, 0, None, None) == bonsai.ERR_NULL
+    assert lib.bonsai_probe_stream(FAKE + 4, 1024, 1, FAKE, None) == bonsai.ERR_ALIGN
+    assert lib.bonsai_probe_clock(None, 10, None) == bonsai.ERR_NULL
+    assert lib.bonsai_probe_clock(FAKE, -1, None) == bonsai.ERR_SHAPE
+    assert lib.bonsai_probe_clock(FAKE, 2_000_000_000, None) == bonsai.ERR_SHAPE
