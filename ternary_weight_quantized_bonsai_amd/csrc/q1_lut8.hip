@@ -1,0 +1,297 @@
+// q1_lut8.hip -- binary g128 GEMV for one row of x over many weight rows (the LM head):
+// y[n] = sum_k W[n][k] x[k] straight from the packed sign words ("1-bit Bonsai 27B" model card,
+// "Weight representation: Binary g128": bit 1 -> +s, bit 0 -> -s, one FP16 scale per 128
+// consecutive weights; its highlights count the LM head among the binary weights).
+//
+// Decode streams the weights once and is bound by memory bandwidth (model card, cross-platform
+// throughput), so what matters is that the arithmetic per weight stays well under what HBM
+// delivers.  Here a byte of sign bits, 8 weights, indexes a 256-entry table of the signed sums
+// of their 8 x values: one LDS read and one add per 8 weights, and one v_perm_b32 that forms the
+// table address from the byte.  With nibble tables (the tile kernels of q1_gemv.hip) it is one
+// read, one add and one address operation per 4 weights.
+//
+// Byte tables are 1 KB each, so one CU holds those of 1024 k (one "slice", 128 tables, 128 KB):
+// every CU walks all the slices of its rows, rebuilding the tables between slices, and keeps
+// each lane's partial sums in registers across the slices, so no partial sum leaves the CU and
+// the result does not depend on how rows are spread over CUs.
+//
+// LDS banks.  The 32 lanes of a half-wave read in one pass only if they fall on 32 distinct
+// banks (or share an address).  The lanes hold different rows, so a table shared by them would
+// be read at 32 random entries.  Instead the 32 lanes always read 32 different tables, and each
+// table lives in one bank.  Lane l holds row l / 8 of an 8-row unit and group p = l % 8 of the
+// slice: the 16-byte cell of four sign words of that (row, group), loaded straight into its
+// registers.  At step j it looks up the four bytes of word j, and lookup m of the step takes byte
+// i = (m + l / 8) % 4.  The table of byte i of word d = 4 p + j of the slice (its 8 weights) holds
+// entry e at byte offset
+//     (i >> 1) * 64 KB + e * 256 + (i & 1) * 128 + 4 (4 p + (j + i) % 4),
+// i.e. in bank 4 p + (j + m + l / 8) % 4: over a half-wave (p = 0..7, (l / 8) % 4 = 0..3) the 32
+// banks of a lookup are distinct.  The address is one v_perm_b32 of the word with a per-lane
+// source holding the bank's offset and the 64 KB half, under a per-lane byte selector.
+#include <algorithm>
+
+#include "device.h"
+#include "launch.h"
+
+namespace bonsai {
+namespace {
+
+typedef __attribute__((address_space(3))) float lds_f32_t;
+typedef __attribute__((address_space(3))) u32x4 lds_u32x4_t;
+
+constexpr int kL8SliceK = 1024;             // k per slice: 128 B of sign bits per row, 8 groups
+constexpr int kL8Tables = 128 * 1024;       // 128 tables of 256 fp32 entries
+constexpr int kL8MaxK = (160 * 1024 - kL8Tables) / 2;   // x (binary16) is staged after the tables
+
+// LDS float at byte address a (the kernel's dynamic LDS starts at 0: it has no static LDS).
+__device__ __forceinline__ float lds_f32(uint32_t a)
+{
+    return *reinterpret_cast<const lds_f32_t *>(static_cast<uintptr_t>(a));
+}
+
+// Entries I .. END - 1 of this wave's share of a table: entry base + I is lo[I % 16] + hi[I / 16],
+// at byte address tb + 256 I.
+template <int I, int END>
+__device__ __forceinline__ void store_entries(uint32_t tb, const float (&lo)[16], const float *hi)
+{
+    if constexpr (I < END) {
+        *reinterpret_cast<lds_f32_t *>(static_cast<uintptr_t>(tb + 256 * I)) = lo[I % 16] + hi[I / 16];
+        store_entries<I + 1, END>(tb, lo, hi);
+    }
+}
+
+// Compile-time loop: f(IC<I>{}) for I = BEGIN .. END - 1.
+template <int I>
+struct IC {
+    static constexpr int value = I;
+};
+template <int I, int END, typename F>
+__device__ __forceinline__ void static_for(F &&f)
+{
+    if constexpr (I < END) {
+        f(IC<I>{});
+        static_for<I + 1, END>(f);
+    }
+}
+
+// Sum over the 8 lanes 8 r .. 8 r + 7 (every lane gets it): swaps within pairs and within quads,
+// then each lane of a half-row of 8 adds the lane at its mirror position -- data-parallel
+// moves between lanes (DPP), in a fixed order.
+__device__ __forceinline__ float sum8(float v)
+{
+    v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0xB1, 0xF, 0xF, false));
+    v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x4E, 0xF, 0xF, false));
+    v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x141, 0xF, 0xF, false));
+    return v;
+}
+
+// W waves; PD units in flight per wave (their cells and scales in registers); at most UMAX units
+// per wave (a multiple of PD, so a unit's registers are fixed at compile time; the launch gives
+// every workgroup at most W UMAX units).
+template <int W, int PD, int UMAX>
+__global__ __launch_bounds__(W * 64) void q1_gemv_lut8_kernel(const uint32_t *__restrict__ wbits,
+                                                              const uint16_t *__restrict__ scales,
+                                                              const uint16_t *__restrict__ x,
+                                                              float *__restrict__ y, int N, int K)
+{
+    static_assert(UMAX % PD == 0, "a unit's registers are fixed at compile time");
+    static_assert(W == 4 || W == 8 || W == 16, "every wave builds the same share of each table");
+    constexpr int EPW = 256 / W;                        // table entries each wave builds
+    constexpr int NH = EPW / 16;                        // their high nibbles
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int G = K >> 7;
+    const int S = (K + kL8SliceK - 1) / kL8SliceK;      // slices
+
+    // this workgroup's units (8 rows each) and this wave's share: units ub0 + wave + W t
+    const int U = (N + 7) / 8;
+    const int ub0 = (int)((int64_t)U * blockIdx.x / gridDim.x);
+    const int ub1 = (int)((int64_t)U * (blockIdx.x + 1) / gridDim.x);
+    const int nw = ub1 - ub0 > wave ? (ub1 - ub0 - wave + W - 1) / W : 0;     // units of this wave
+
+    const int r = lane >> 3, p = lane & 7;              // row of the unit, group of the slice
+    const int rq = r & 3;
+
+    // Unit (s, t) -- slice s, t-th unit of the wave: the lane's cell and scale, at a wave-uniform
+    // base plus the lane's offset.  The last unit of the matrix starts at row N - 8 when N is not
+    // a multiple of 8 (its first rows repeat the unit before, and are written twice with the same
+    // value).  A unit past the wave's own loads the wave's first unit instead (every iteration
+    // issues the same two loads, so the waits the compiler places stay exact).  voff, soff: the
+    // lane's offsets (groups clamped inside a short last slice).
+    auto load = [&](int s, int t, uint32_t voff, uint32_t soff, u32x4 &cell, uint32_t &sc) {
+        const int row0 = min(8 * (ub0 + wave + W * (t < nw ? t : 0)), N - 8);
+        const size_t at = (size_t)row0 * G + 8 * s;
+        const char *cb = reinterpret_cast<const char *>(wbits) + 16 * at;
+        const char *sb = reinterpret_cast<const char *>(scales) + 2 * at;
+        cell = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(cb + voff));
+        sc = *reinterpret_cast<const uint16_t *>(sb + soff);
+    };
+    auto lane_offsets = [&](int s, uint32_t &voff, uint32_t &soff) {
+        const int g = min(p, G - 8 * s - 1);
+        voff = 16u * (uint32_t)(r * G + g);
+        soff = 2u * (uint32_t)(r * G + g);
+    };
+
+    // Tables of slice s: wave w writes entries EPW w .. EPW w + EPW - 1 of every table, two
+    // 256-byte rows of table columns per entry (the 64 KB halves h = 0, 1).  Lane c holds column
+    // c of a row: byte i = 2 h + c / 32 of word d = 4 (b / 4) + ((b % 4) - i) % 4, b = c % 32, whose
+    // 8 weights are k = 1024 s + 8 (4 d + i) ..; x read clamped inside x past K (such tables
+    // belong to groups past K, which count with weight 0).
+    auto load_x = [&](int s, u32x4 xv[2]) {
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const int i = 2 * h + (lane >> 5), b = lane & 31;
+            const int d = 4 * (b >> 2) + (((b & 3) - i) & 3);
+            xv[h] = *reinterpret_cast<const lds_u32x4_t *>(static_cast<uintptr_t>(kL8Tables + 16 * min(128 * s + 4 * d + i, K / 8 - 1)));
+        }
+    };
+    auto build = [&](const u32x4 xv[2]) {
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            float xs[8];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const half2_t pr = as_half2(xv[h][j]);
+                xs[2 * j] = (float)pr[0];
+                xs[2 * j + 1] = (float)pr[1];
+            }
+            // lo[v] = sum_{j<4} (bit j of v ? +x_j : -x_j); hi likewise over x_4..x_7 for the
+            // NH high nibbles NH w .. NH w + NH - 1 of this wave's entries
+            float lo[16];
+            lo[0] = -((xs[0] + xs[1]) + (xs[2] + xs[3]));
+#pragma unroll
+            for (int b = 0; b < 4; ++b) {
+                const float tx = 2.f * xs[b];
+#pragma unroll
+                for (int v = 0; v < (1 << b); ++v) lo[v | (1 << b)] = lo[v] + tx;
+            }
+            float hi[NH];
+#pragma unroll
+            for (int hb = 0; hb < NH; ++hb) {
+                const int v = NH * wave + hb;
+                const float s4 = (v & 1) ? xs[4] : -xs[4], s5 = (v & 2) ? xs[5] : -xs[5];
+                const float s6 = (v & 4) ? xs[6] : -xs[6], s7 = (v & 8) ? xs[7] : -xs[7];
+                hi[hb] = (s4 + s5) + (s6 + s7);
+            }
+            store_entries<0, EPW>(h * 65536 + 256 * (EPW * wave) + 4 * lane, lo, hi);
+        }
+    };
+
+    // Per-lane lookup constants.  Lookup m takes byte i = (m + rq) % 4 of the word: its selector
+    // puts byte 0 of the source (the column offset), byte i of the word (the entry), byte 2 of
+    // the source (the 64 KB half) and a zero byte; the source of (step j, lookup m) holds
+    // 4 (4 p + (j + i) % 4) + 128 (i & 1) in byte 0 and i >> 1 in byte 2.  (v_perm_b32 selector
+    // bytes 0..3 pick bytes of the second operand, 4..7 of the first, 12 gives 0.)
+    uint32_t sel[4], src[16];
+    u32x4 cell[PD];
+    uint32_t scw[PD];
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+        const int i = (m + rq) & 3;
+        sel[m] = 0x0C020000u | ((uint32_t)(4 + i) << 8);
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            src[4 * j + m] = (uint32_t)(4 * (4 * p + ((j + i) & 3)) + 128 * (i & 1)) | ((uint32_t)(i >> 1) << 16);
+    }
+
+    // x to LDS (after the tables; its loads go out before the first units'), the first PD units
+    // in flight, then the first slice's tables
+    {
+        constexpr int XR = (kL8MaxK / 8 + W * 64 - 1) / (W * 64);     // 16-byte pieces of x per thread
+        const u32x4 *xg = reinterpret_cast<const u32x4 *>(x);
+        u32x4 xr[XR];
+#pragma unroll
+        for (int it = 0; it < XR; ++it) {
+            const int c = threadIdx.x + it * W * 64;
+            if (c < K / 8) xr[it] = xg[c];
+        }
+        uint32_t voff, soff;
+        lane_offsets(0, voff, soff);
+        static_for<0, PD>([&](auto ic) {
+            constexpr int tt = decltype(ic)::value;
+            load(0, tt, voff, soff, cell[tt], scw[tt]);
+        });
+#pragma unroll
+        for (int it = 0; it < XR; ++it) {
+            const int c = threadIdx.x + it * W * 64;
+            if (c < K / 8) *reinterpret_cast<lds_u32x4_t *>(static_cast<uintptr_t>(kL8Tables + 16 * c)) = xr[it];
+        }
+    }
+    __syncthreads();
+    {
+        u32x4 xv[2];
+        load_x(0, xv);
+        build(xv);
+    }
+    __syncthreads();
+
+    float acc[UMAX];
+#pragma unroll
+    for (int tt = 0; tt < UMAX; ++tt) acc[tt] = 0.f;
+    for (int s = 0; s < S; ++s) {
+        const bool last = s == S - 1;
+        const bool live_group = 8 * s + p < G;          // groups past K (a short last slice) count 0
+        uint32_t voff, soff, voffn, soffn;              // this slice's and the next's lane offsets
+        lane_offsets(s, voff, soff);
+        lane_offsets(last ? s : s + 1, voffn, soffn);
+        static_for<0, UMAX>([&](auto ic) {
+            constexpr int tt = decltype(ic)::value, b = tt % PD;
+            if (tt < nw) {
+                float tv[16];
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+#pragma unroll
+                    for (int m = 0; m < 4; ++m)
+                        tv[4 * j + m] = lds_f32(__builtin_amdgcn_perm(cell[b][j], src[4 * j + m], sel[m]));
+                const float part = (((tv[0] + tv[1]) + (tv[2] + tv[3])) + ((tv[4] + tv[5]) + (tv[6] + tv[7]))) +
+                                   (((tv[8] + tv[9]) + (tv[10] + tv[11])) + ((tv[12] + tv[13]) + (tv[14] + tv[15])));
+                if (live_group) acc[tt] = fmaf(f16_bits_to_f32((uint16_t)scw[b]), part, acc[tt]);
+            }
+            // the unit PD ahead into the registers just used (past the last slice: nothing)
+            constexpr int ta = tt + PD;
+            if constexpr (ta < UMAX) load(s, ta, voff, soff, cell[b], scw[b]);
+            else if (!last) load(s + 1, ta - UMAX, voffn, soffn, cell[b], scw[b]);
+        });
+        if (!last) {
+            __syncthreads();                            // every wave is done with these tables
+            u32x4 xv[2];
+            load_x(s + 1, xv);
+            build(xv);
+            __syncthreads();
+        }
+    }
+    // add each row's 8 group partials (lanes 8 r .. 8 r + 7) in a fixed order and store
+#pragma unroll
+    for (int tt = 0; tt < UMAX; ++tt) {
+        if (tt < nw) {
+            const float v = sum8(acc[tt]);
+            const int row = min(8 * (ub0 + wave + W * tt), N - 8) + r;
+            if (p == 0) y[row] = v;
+        }
+    }
+}
+
+template <int W, int PD, int UMAX>
+hipError_t launch_lut8_t(const uint32_t *wbits, const uint16_t *scales, const uint16_t *x, float *y, int N, int K,
+                         hipStream_t stream)
+{
+    if (N < 8 || K > kL8MaxK) return hipErrorInvalidValue;
+    // one workgroup per CU, or more where a CU's share would exceed W UMAX units
+    const int64_t U = ((int64_t)N + 7) / 8;
+    const int64_t cus = device_cus();
+    const int64_t grid = std::max(std::min(U, cus), (U + W * UMAX - 1) / (W * UMAX));
+    const void *fn = reinterpret_cast<const void *>(&q1_gemv_lut8_kernel<W, PD, UMAX>);
+    const size_t lds = (size_t)kL8Tables + 2 * (size_t)K;
+    if (!set_lds_limit(fn, kLdsPerCu)) return hipErrorInvalidValue;
+    void *args[] = {&wbits, &scales, &x, &y, &N, &K};
+    return launch_kernel(fn, __PRETTY_FUNCTION__, dim3((unsigned)grid), dim3(64 * W), args, lds, stream);
+}
+
+}  // namespace
+
+hipError_t launch_lut8(const uint32_t *wbits, const uint16_t *scales, const uint16_t *x, float *y, int N, int K,
+                       hipStream_t stream)
+{
+    return launch_lut8_t<8, 8, 16>(wbits, scales, x, y, N, K, stream);
+}
+
+}  // namespace bonsai
