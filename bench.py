@@ -50,7 +50,7 @@ PROBE_BYTES = LM_N * LM_K // 8 + 2 * LM_N * (LM_K // 128)
 
 # The kernel that runs the headline shape, and the source each profiled kernel is built from
 # (the counter summaries are keyed to it).
-HEADLINE_KERNEL = "q1_gemv_lutp_kernel"
+HEADLINE_KERNEL = "q1_gemv_lut8_kernel"
 KERNEL_SRC = {
     "q1_gemv_lut4_kernel": "ternary_weight_quantized_bonsai_amd/csrc/q1_gemv.hip",
     "q1_gemv_lutp_kernel": "ternary_weight_quantized_bonsai_amd/csrc/q1_gemv.hip",
@@ -62,7 +62,7 @@ KERNEL_SRC = {
 KERNEL_OF_LAUNCHER = {
     "launch_lut4": "q1_gemv_lut4_kernel",
     "launch_lutp": "q1_gemv_lutp_kernel",
-    "launch_lut8": "q1_gemv_lut8_kernel",
+    "launch_lut8_t": "q1_gemv_lut8_kernel",
     "launch_rt": "gemv_mfma_kernel",
     "t5_launch_rt": "t5_gemv_kernel",
 }

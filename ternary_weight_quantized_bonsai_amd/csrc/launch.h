@@ -18,7 +18,9 @@ hipError_t launch_q2t_gemm(const uint32_t *wcodes, const uint16_t *scales, const
 // entry points use it for ternary M = 1..8 and binary M = 2..8, the GEMMs for small M).
 hipError_t launch_gemv_mfma(bool ternary, const uint32_t *codes, const uint16_t *scales, const uint16_t *x,
                             float *y, int M, int N, int K, hipStream_t stream);
-// Binary weights, one row of x, many rows: byte lookup tables, a slice of K at a time (q1_lut8.hip).
+// Binary weights, one row of x, many rows: byte lookup tables, a slice of K at a time (q1_lut8.hip);
+// it takes N >= 8 and K up to what its LDS holds beside the tables (lut8_fits).
+bool lut8_fits(int N, int K);
 hipError_t launch_lut8(const uint32_t *wbits, const uint16_t *scales, const uint16_t *x, float *y, int N, int K,
                        hipStream_t stream);
 // Affine 1-bit weights at M = 1 on the table kernels, where their tables fit (q1a_lut_fits).

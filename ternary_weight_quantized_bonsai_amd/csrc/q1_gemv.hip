@@ -649,6 +649,10 @@ hipError_t launch_q1_gemv(const uint32_t *wbits, const uint16_t *scales, const u
     const bool fits64 = (G + L4<64>::gpw - 1) / L4<64>::gpw <= L4<64>::max_waves;
     const int64_t tiles64 = ((int64_t)N + 63) / 64;
     const int cus = device_cus();
+    // - many rows (the LM head): byte tables, rebuilt per 1024 k on every CU, which halve the
+    //   lookups of the nibble tables (K = 5120: 248320 rows in 36 us against 51 us; they tie
+    //   near 131072 rows, below which the rebuilds cost more than the lookups they save)
+    if ((int64_t)N >= 600LL * cus && G >= 16 && lut8_fits(N, K)) return launch_lut8(wbits, scales, x, y, N, K, stream);
     if (fits32 && ((int64_t)N + 31) / 32 <= cus) return launch_lut4<32, false, 2>(wbits, scales, nullptr, x, y, N, K, stream);
     const bool persist = tiles64 > 6 * cus && (G >= 28 || (G >= 16 && tiles64 > 14 * cus));
     if (fits64 && !persist) return launch_lut4<64, false>(wbits, scales, nullptr, x, y, N, K, stream);

@@ -288,10 +288,12 @@ hipError_t launch_lut8_t(const uint32_t *wbits, const uint16_t *scales, const ui
 
 }  // namespace
 
+bool lut8_fits(int N, int K) { return N >= 8 && K <= kL8MaxK; }
+
 hipError_t launch_lut8(const uint32_t *wbits, const uint16_t *scales, const uint16_t *x, float *y, int N, int K,
                        hipStream_t stream)
 {
-    return launch_lut8_t<8, 8, 16>(wbits, scales, x, y, N, K, stream);
+    return launch_lut8_t<16, 4, 8>(wbits, scales, x, y, N, K, stream);
 }
 
 }  // namespace bonsai

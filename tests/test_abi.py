@@ -298,7 +298,8 @@ def test_plan_names_each_route_of_the_decode_gemv():
     # to six rounds, then the persistent kernel; more rows of x go to the matrix cores
     assert _plan_kernel("q1_gemv", 1, 5120, 5120, 256) == "launch_lut4[ROWS = 32, AFF = false, GPL = 2]"
     assert _plan_kernel("q1_gemv", 1, 13824, 5120, 256) == "launch_lut4[ROWS = 64, AFF = false, GPL = 4]"
-    assert _plan_kernel("q1_gemv", 1, 248320, 5120, 256).startswith("launch_lut")
+    assert _plan_kernel("q1_gemv", 1, 248320, 5120, 256).startswith("launch_lut8")
+    assert _plan_kernel("q1_gemv", 1, 100003, 5120, 256) == "launch_lutp[AFF = false]"
     assert _plan_kernel("q1_gemv", 8, 5120, 5120, 256).startswith("launch_rt[TERN = false")
     assert _plan_kernel("q1_gemm", 512, 13824, 5120, 256) == "q1_gemm_kernel<false, 16>"
     assert _plan_kernel("q1_gemm", 512, 13824, 5248, 256) == "q1_gemm_kernel<false, 2>"
@@ -316,11 +317,16 @@ def test_plan_routing_follows_the_compute_unit_count():
     assert _plan_kernel("q1_gemv", 1, 5120, 5120, 256).startswith("launch_lut4[ROWS = 32")
     assert _plan_kernel("q1_gemv", 1, 5120, 5120, 160).startswith("launch_lut4[ROWS = 32")
     assert _plan_kernel("q1_gemv", 1, 5120, 5120, 128).startswith("launch_lut4[ROWS = 64")
-    # the persistent LM-head kernel takes one workgroup per CU
+    # the persistent LM-head kernels take one workgroup per CU (the byte-table kernel more when a
+    # CU's share of rows would exceed what its waves hold); the byte tables take over at 600 rows
+    # per CU
     for cus in (80, 256, 304):
         plan = bonsai.plan("q1_gemv", 1, 248320, 5120, cus)
-        if plan.startswith("launch_lutp"):
-            assert _plan_grid("q1_gemv", 1, 248320, 5120, cus) == cus
+        assert plan.startswith("launch_lut8") or plan.startswith("launch_lutp"), plan
+        grid = _plan_grid("q1_gemv", 1, 248320, 5120, cus)
+        assert grid == cus or (plan.startswith("launch_lut8") and grid > cus and grid * 16 * 8 * 8 >= 248320)
+    assert _plan_kernel("q1_gemv", 1, 600 * 200, 5120, 200).startswith("launch_lut8")
+    assert not _plan_kernel("q1_gemv", 1, 600 * 200 - 1, 5120, 200).startswith("launch_lut8")
     # the small-M kernel's tiles always cover every row, whatever tile the CU count selects
     for cus in (32, 64, 256, 304):
         plan = bonsai.plan("q2t_gemv", 8, 5120, 5120, cus)

@@ -94,6 +94,8 @@ def test_launch_distribution_and_kernel_names():
     assert d["mean_us"] == pytest.approx(5.5) and d["median_us"] == pytest.approx(5.5)
     assert d["p10_us"] == pytest.approx(1.9) and d["p90_us"] == pytest.approx(9.1) and d["launches"] == 10
     assert bench.kernel_of("launch_lutp[AFF = false] grid=256,1 block=512 lds=163840") == "q1_gemv_lutp_kernel"
+    assert bench.kernel_of("launch_lut8_t[W = 16, PD = 4, UMAX = 8] grid=256,1 block=1024 lds=141312") == \
+        "q1_gemv_lut8_kernel"
     assert bench.kernel_of("q1_gemm_kernel<false, 16> grid=216,1 block=256 lds=0") == "q1_gemm_kernel"
     assert bench.KERNEL_SRC[bench.HEADLINE_KERNEL].endswith(".hip")
 
