@@ -84,18 +84,18 @@ __device__ __forceinline__ float sum8(float v)
     return v;
 }
 
-// W waves; PD units in flight per wave (their cells and scales in registers); at most UMAX units
-// per wave (a multiple of PD, so a unit's registers are fixed at compile time; the launch gives
-// every workgroup at most W UMAX units).
-template <int W, int PD, int UMAX>
+// W waves; PD units in flight per wave (their cells in registers); at most UMAX units per wave (a
+// multiple of PD, so a unit's registers are fixed at compile time; the launch gives every
+// workgroup at most W UMAX units); the scales of SQ slices of every unit in registers at a time.
+template <int W, int PD, int UMAX, int SQ>
 __global__ __launch_bounds__(W * 64) void q1_gemv_lut8_kernel(const uint32_t *__restrict__ wbits,
                                                               const uint16_t *__restrict__ scales,
                                                               const uint16_t *__restrict__ x,
                                                               float *__restrict__ y, int N, int K)
 {
     static_assert(UMAX % PD == 0, "a unit's registers are fixed at compile time");
-    static_assert(W == 4 || W == 8 || W == 16, "every wave builds the same share of each table");
-    constexpr int EPW = 256 / W;                        // table entries each wave builds
+    static_assert(W == 4 || W == 8 || W == 16, "every wave builds an equal share of one half's tables");
+    constexpr int EPW = 512 / W;                        // entries of its half's tables each wave builds
     constexpr int NH = EPW / 16;                        // their high nibbles
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -111,69 +111,88 @@ __global__ __launch_bounds__(W * 64) void q1_gemv_lut8_kernel(const uint32_t *__
     const int r = lane >> 3, p = lane & 7;              // row of the unit, group of the slice
     const int rq = r & 3;
 
-    // Unit (s, t) -- slice s, t-th unit of the wave: the lane's cell and scale, at a wave-uniform
-    // base plus the lane's offset.  The last unit of the matrix starts at row N - 8 when N is not
-    // a multiple of 8 (its first rows repeat the unit before, and are written twice with the same
-    // value).  A unit past the wave's own loads the wave's first unit instead (every iteration
-    // issues the same two loads, so the waits the compiler places stay exact).  voff, soff: the
-    // lane's offsets (groups clamped inside a short last slice).
-    auto load = [&](int s, int t, uint32_t voff, uint32_t soff, u32x4 &cell, uint32_t &sc) {
-        const int row0 = min(8 * (ub0 + wave + W * (t < nw ? t : 0)), N - 8);
-        const size_t at = (size_t)row0 * G + 8 * s;
-        const char *cb = reinterpret_cast<const char *>(wbits) + 16 * at;
-        const char *sb = reinterpret_cast<const char *>(scales) + 2 * at;
-        cell = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(cb + voff));
-        sc = *reinterpret_cast<const uint16_t *>(sb + soff);
+    // First row of the wave's t-th unit.  The last unit of the matrix starts at row N - 8 when N
+    // is not a multiple of 8 (its first rows repeat the unit before, and are written twice with
+    // the same value).  A unit past the wave's own stands for the wave's first unit (every
+    // iteration issues the same loads, so the waits the compiler places stay exact).
+    auto unit_row0 = [&](int t) { return min(8 * (ub0 + wave + W * (t < nw ? t : 0)), N - 8); };
+
+    // Unit (s, t) -- slice s, t-th unit: the lane's cell, at the unit's wave-uniform base plus the
+    // lane's offset voff of the slice (the group clamped inside a short last slice).
+    const char *ubase[UMAX];
+#pragma unroll
+    for (int t = 0; t < UMAX; ++t) ubase[t] = reinterpret_cast<const char *>(wbits) + 16 * (size_t)unit_row0(t) * G;
+    auto load_cell = [&](int t, uint32_t voff, u32x4 &cell) {
+        cell = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(ubase[t] + voff));
     };
-    auto lane_offsets = [&](int s, uint32_t &voff, uint32_t &soff) {
-        const int g = min(p, G - 8 * s - 1);
-        voff = 16u * (uint32_t)(r * G + g);
-        soff = 2u * (uint32_t)(r * G + g);
+    auto lane_voff = [&](int s) { return 16u * (uint32_t)(r * G + 8 * s + min(p, G - 8 * s - 1)); };
+    const char *xb = reinterpret_cast<const char *>(x);
+    const uint32_t xoff = 16u * (uint32_t)(lane % (K / 8));
+
+    // Scales of slices s0 .. s0 + SQ - 1 of every unit of the wave: lane (r, p) takes that of
+    // group 8 s + p of row r (clamped to the row's last group past K), two slices to a register.
+    // A row's 80 bytes of scales (K = 5120) are read together rather than 16 bytes per slice, one
+    // slice's worth of the weights apart: between slices the cache would have to hold them while
+    // the weights stream.  load_scales issues the loads of units t0 .. t1 - 1, pack_scales pairs
+    // them once they are in.
+    constexpr int SQ2 = (SQ + 1) / 2;
+    auto load_scales = [&](int s0, int t0, int t1, uint32_t (&raw)[UMAX][SQ]) {
+        uint32_t so[SQ];
+#pragma unroll
+        for (int q = 0; q < SQ; ++q) so[q] = 2u * (uint32_t)(r * G + min(8 * (s0 + q) + p, G - 1));
+#pragma unroll
+        for (int t = t0; t < t1; ++t) {
+            const char *sb = reinterpret_cast<const char *>(scales) + 2 * (size_t)unit_row0(t) * G;
+#pragma unroll
+            for (int q = 0; q < SQ; ++q) raw[t][q] = *reinterpret_cast<const uint16_t *>(sb + so[q]);
+        }
+    };
+    auto pack_scales = [&](int t0, int t1, const uint32_t (&raw)[UMAX][SQ], uint32_t (&sc)[UMAX][SQ2]) {
+#pragma unroll
+        for (int t = t0; t < t1; ++t)
+#pragma unroll
+            for (int q2 = 0; q2 < SQ2; ++q2)
+                sc[t][q2] = 2 * q2 + 1 < SQ ? raw[t][2 * q2] | (raw[t][2 * q2 + 1] << 16) : raw[t][2 * q2];
     };
 
-    // Tables of slice s: wave w writes entries EPW w .. EPW w + EPW - 1 of every table, two
-    // 256-byte rows of table columns per entry (the 64 KB halves h = 0, 1).  Lane c holds column
-    // c of a row: byte i = 2 h + c / 32 of word d = 4 (b / 4) + ((b % 4) - i) % 4, b = c % 32, whose
-    // 8 weights are k = 1024 s + 8 (4 d + i) ..; x read clamped inside x past K (such tables
-    // belong to groups past K, which count with weight 0).
-    auto load_x = [&](int s, u32x4 xv[2]) {
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-            const int i = 2 * h + (lane >> 5), b = lane & 31;
-            const int d = 4 * (b >> 2) + (((b & 3) - i) & 3);
-            xv[h] = *reinterpret_cast<const lds_u32x4_t *>(static_cast<uintptr_t>(kL8Tables + 16 * min(128 * s + 4 * d + i, K / 8 - 1)));
-        }
+    // Tables of slice s: wave w writes entries EPW (w / 2) .. EPW (w / 2) + EPW - 1 of the 64
+    // tables of the 64 KB half h = w % 2, one 256-byte row of table columns per entry.  Lane c
+    // holds column c of the row: byte i = 2 h + c / 32 of word d = 4 (b / 4) + ((b % 4) - i) % 4,
+    // b = c % 32, whose 8 weights are k = 1024 s + 8 (4 d + i) ..; x read clamped inside x past K
+    // (such tables belong to groups past K, which count with weight 0).
+    const int bh = wave & 1, bq = wave >> 1;
+    auto load_x = [&](int s) -> u32x4 {
+        const int i = 2 * bh + (lane >> 5), b = lane & 31;
+        const int d = 4 * (b >> 2) + (((b & 3) - i) & 3);
+        return *reinterpret_cast<const lds_u32x4_t *>(static_cast<uintptr_t>(kL8Tables + 16 * min(128 * s + 4 * d + i, K / 8 - 1)));
     };
-    auto build = [&](const u32x4 xv[2]) {
+    auto build = [&](const u32x4 xv) {
+        float xs[8];
 #pragma unroll
-        for (int h = 0; h < 2; ++h) {
-            float xs[8];
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const half2_t pr = as_half2(xv[h][j]);
-                xs[2 * j] = (float)pr[0];
-                xs[2 * j + 1] = (float)pr[1];
-            }
-            // lo[v] = sum_{j<4} (bit j of v ? +x_j : -x_j); hi likewise over x_4..x_7 for the
-            // NH high nibbles NH w .. NH w + NH - 1 of this wave's entries
-            float lo[16];
-            lo[0] = -((xs[0] + xs[1]) + (xs[2] + xs[3]));
-#pragma unroll
-            for (int b = 0; b < 4; ++b) {
-                const float tx = 2.f * xs[b];
-#pragma unroll
-                for (int v = 0; v < (1 << b); ++v) lo[v | (1 << b)] = lo[v] + tx;
-            }
-            float hi[NH];
-#pragma unroll
-            for (int hb = 0; hb < NH; ++hb) {
-                const int v = NH * wave + hb;
-                const float s4 = (v & 1) ? xs[4] : -xs[4], s5 = (v & 2) ? xs[5] : -xs[5];
-                const float s6 = (v & 4) ? xs[6] : -xs[6], s7 = (v & 8) ? xs[7] : -xs[7];
-                hi[hb] = (s4 + s5) + (s6 + s7);
-            }
-            store_entries<0, EPW>(h * 65536 + 256 * (EPW * wave) + 4 * lane, lo, hi);
+        for (int j = 0; j < 4; ++j) {
+            const half2_t pr = as_half2(xv[j]);
+            xs[2 * j] = (float)pr[0];
+            xs[2 * j + 1] = (float)pr[1];
         }
+        // lo[v] = sum_{j<4} (bit j of v ? +x_j : -x_j); hi likewise over x_4..x_7 for the NH high
+        // nibbles NH (w / 2) .. NH (w / 2) + NH - 1 of this wave's entries
+        float lo[16];
+        lo[0] = -((xs[0] + xs[1]) + (xs[2] + xs[3]));
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+            const float tx = 2.f * xs[b];
+#pragma unroll
+            for (int v = 0; v < (1 << b); ++v) lo[v | (1 << b)] = lo[v] + tx;
+        }
+        float hi[NH];
+#pragma unroll
+        for (int hb = 0; hb < NH; ++hb) {
+            const int v = NH * bq + hb;
+            const float s4 = (v & 1) ? xs[4] : -xs[4], s5 = (v & 2) ? xs[5] : -xs[5];
+            const float s6 = (v & 4) ? xs[6] : -xs[6], s7 = (v & 8) ? xs[7] : -xs[7];
+            hi[hb] = (s4 + s5) + (s6 + s7);
+        }
+        store_entries<0, EPW>(bh * 65536 + 256 * (EPW * bq) + 4 * lane, lo, hi);
     };
 
     // Per-lane lookup constants.  Lookup m takes byte i = (m + rq) % 4 of the word: its selector
@@ -183,7 +202,7 @@ __global__ __launch_bounds__(W * 64) void q1_gemv_lut8_kernel(const uint32_t *__
     // bytes 0..3 pick bytes of the second operand, 4..7 of the first, 12 gives 0.)
     uint32_t sel[4], src[16];
     u32x4 cell[PD];
-    uint32_t scw[PD];
+    uint32_t raw[UMAX][SQ], sc[UMAX][SQ2];
 #pragma unroll
     for (int m = 0; m < 4; ++m) {
         const int i = (m + rq) & 3;
@@ -193,8 +212,8 @@ __global__ __launch_bounds__(W * 64) void q1_gemv_lut8_kernel(const uint32_t *__
             src[4 * j + m] = (uint32_t)(4 * (4 * p + ((j + i) & 3)) + 128 * (i & 1)) | ((uint32_t)(i >> 1) << 16);
     }
 
-    // x to LDS (after the tables; its loads go out before the first units'), the first PD units
-    // in flight, then the first slice's tables
+    // x to LDS (after the tables), the first SQ slices' scales paired, with the first PD units
+    // in flight, then the first slice's tables.  The loads go out in that order: x, scales, cells.
     {
         constexpr int XR = (kL8MaxK / 8 + W * 64 - 1) / (W * 64);     // 16-byte pieces of x per thread
         const u32x4 *xg = reinterpret_cast<const u32x4 *>(x);
@@ -204,73 +223,87 @@ __global__ __launch_bounds__(W * 64) void q1_gemv_lut8_kernel(const uint32_t *__
             const int c = threadIdx.x + it * W * 64;
             if (c < K / 8) xr[it] = xg[c];
         }
-        uint32_t voff, soff;
-        lane_offsets(0, voff, soff);
-        static_for<0, PD>([&](auto ic) {
-            constexpr int tt = decltype(ic)::value;
-            load(0, tt, voff, soff, cell[tt], scw[tt]);
-        });
+        load_scales(0, 0, UMAX, raw);
+        const uint32_t voff = lane_voff(0);
+#pragma unroll
+        for (int t = 0; t < PD; ++t) load_cell(t, voff, cell[t]);
 #pragma unroll
         for (int it = 0; it < XR; ++it) {
             const int c = threadIdx.x + it * W * 64;
             if (c < K / 8) *reinterpret_cast<lds_u32x4_t *>(static_cast<uintptr_t>(kL8Tables + 16 * c)) = xr[it];
         }
+        pack_scales(0, UMAX, raw, sc);
     }
     __syncthreads();
-    {
-        u32x4 xv[2];
-        load_x(0, xv);
-        build(xv);
-    }
+    build(load_x(0));
     __syncthreads();
 
     float acc[UMAX];
 #pragma unroll
     for (int tt = 0; tt < UMAX; ++tt) acc[tt] = 0.f;
-    for (int s = 0; s < S; ++s) {
-        const bool last = s == S - 1;
-        const bool live_group = 8 * s + p < G;          // groups past K (a short last slice) count 0
-        uint32_t voff, soff, voffn, soffn;              // this slice's and the next's lane offsets
-        lane_offsets(s, voff, soff);
-        lane_offsets(last ? s : s + 1, voffn, soffn);
-        static_for<0, UMAX>([&](auto ic) {
-            constexpr int tt = decltype(ic)::value, b = tt % PD;
-            if (tt < nw) {
-                float tv[16];
-#pragma unroll
-                for (int j = 0; j < 4; ++j)
-#pragma unroll
-                    for (int m = 0; m < 4; ++m)
-                        tv[4 * j + m] = lds_f32(__builtin_amdgcn_perm(cell[b][j], src[4 * j + m], sel[m]));
-                const float part = (((tv[0] + tv[1]) + (tv[2] + tv[3])) + ((tv[4] + tv[5]) + (tv[6] + tv[7]))) +
-                                   (((tv[8] + tv[9]) + (tv[10] + tv[11])) + ((tv[12] + tv[13]) + (tv[14] + tv[15])));
-                if (live_group) acc[tt] = fmaf(f16_bits_to_f32((uint16_t)scw[b]), part, acc[tt]);
-            }
-            // the unit PD ahead into the registers just used (past the last slice: nothing)
-            constexpr int ta = tt + PD;
-            if constexpr (ta < UMAX) load(s, ta, voff, soff, cell[b], scw[b]);
-            else if (!last) load(s + 1, ta - UMAX, voffn, soffn, cell[b], scw[b]);
-        });
-        if (!last) {
-            __syncthreads();                            // every wave is done with these tables
-            u32x4 xv[2];
-            load_x(s + 1, xv);
-            build(xv);
-            __syncthreads();
+    for (int s0 = 0; s0 < S; s0 += SQ) {
+        if (s0 > 0) {                                   // K > 1024 SQ: the next SQ slices' scales,
+            load_scales(s0, 0, UMAX / 2, raw);          // half the units at a time
+            pack_scales(0, UMAX / 2, raw, sc);
+            load_scales(s0, UMAX / 2, UMAX, raw);
+            pack_scales(UMAX / 2, UMAX, raw, sc);
         }
+        static_for<0, SQ>([&](auto qc) {
+            constexpr int q = decltype(qc)::value;
+            const int s = s0 + q;
+            if (s < S) {
+                const bool last = s == S - 1;
+                const bool live_group = 8 * s + p < G;  // groups past K (a short last slice) count 0
+                const uint32_t voff = lane_voff(s), voffn = lane_voff(last ? s : s + 1);
+                static_for<0, UMAX>([&](auto ic) {
+                    // Every unit slot is computed (a slot past the wave's units repeats its first
+                    // unit and is not stored), and every slot issues one load: with no branches
+                    // the compiler's waits count exactly PD - 1 loads still in flight.
+                    constexpr int tt = decltype(ic)::value, b = tt % PD;
+                    float tv[16];
+#pragma unroll
+                    for (int j = 0; j < 4; ++j)
+#pragma unroll
+                        for (int m = 0; m < 4; ++m)
+                            tv[4 * j + m] = lds_f32(__builtin_amdgcn_perm(cell[b][j], src[4 * j + m], sel[m]));
+                    const float part =
+                        (((tv[0] + tv[1]) + (tv[2] + tv[3])) + ((tv[4] + tv[5]) + (tv[6] + tv[7]))) +
+                        (((tv[8] + tv[9]) + (tv[10] + tv[11])) + ((tv[12] + tv[13]) + (tv[14] + tv[15])));
+                    const uint16_t sbits = (uint16_t)(sc[tt][q / 2] >> (16 * (q % 2)));
+                    acc[tt] = live_group ? fmaf(f16_bits_to_f32(sbits), part, acc[tt]) : acc[tt];
+                    // the unit PD ahead into the registers just used; past the last slice a
+                    // re-read of x, which the cache holds
+                    constexpr int ta = tt + PD;
+                    if constexpr (ta < UMAX) {
+                        load_cell(ta, voff, cell[b]);
+                    } else {
+                        const char *bp = last ? xb : ubase[ta - UMAX];
+                        cell[b] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(bp + (last ? xoff : voffn)));
+                    }
+                });
+                if (!last) {
+                    __syncthreads();                    // every wave is done with these tables
+                    build(load_x(s + 1));
+                    __syncthreads();
+                }
+            }
+        });
     }
-    // add each row's 8 group partials (lanes 8 r .. 8 r + 7) in a fixed order and store
+    // add each row's 8 group partials (lanes 8 r .. 8 r + 7) in a fixed order and store; the
+    // lane's row is taken afresh from the lane count (mbcnt), which the compiler recomputes here
+    // instead of keeping r live through the slices
+    const int lane_end = (int)__builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
 #pragma unroll
     for (int tt = 0; tt < UMAX; ++tt) {
         if (tt < nw) {
             const float v = sum8(acc[tt]);
-            const int row = min(8 * (ub0 + wave + W * tt), N - 8) + r;
-            if (p == 0) y[row] = v;
+            const int row = min(8 * (ub0 + wave + W * tt), N - 8) + (lane_end >> 3);
+            if ((lane_end & 7) == 0) y[row] = v;
         }
     }
 }
 
-template <int W, int PD, int UMAX>
+template <int W, int PD, int UMAX, int SQ>
 hipError_t launch_lut8_t(const uint32_t *wbits, const uint16_t *scales, const uint16_t *x, float *y, int N, int K,
                          hipStream_t stream)
 {
@@ -279,7 +312,7 @@ hipError_t launch_lut8_t(const uint32_t *wbits, const uint16_t *scales, const ui
     const int64_t U = ((int64_t)N + 7) / 8;
     const int64_t cus = device_cus();
     const int64_t grid = std::max(std::min(U, cus), (U + W * UMAX - 1) / (W * UMAX));
-    const void *fn = reinterpret_cast<const void *>(&q1_gemv_lut8_kernel<W, PD, UMAX>);
+    const void *fn = reinterpret_cast<const void *>(&q1_gemv_lut8_kernel<W, PD, UMAX, SQ>);
     const size_t lds = (size_t)kL8Tables + 2 * (size_t)K;
     if (!set_lds_limit(fn, kLdsPerCu)) return hipErrorInvalidValue;
     void *args[] = {&wbits, &scales, &x, &y, &N, &K};
@@ -293,7 +326,7 @@ bool lut8_fits(int N, int K) { return N >= 8 && K <= kL8MaxK; }
 hipError_t launch_lut8(const uint32_t *wbits, const uint16_t *scales, const uint16_t *x, float *y, int N, int K,
                        hipStream_t stream)
 {
-    return launch_lut8_t<16, 4, 8>(wbits, scales, x, y, N, K, stream);
+    return launch_lut8_t<16, 4, 8, 5>(wbits, scales, x, y, N, K, stream);
 }
 
 }  // namespace bonsai
