@@ -113,21 +113,24 @@ __global__ __launch_bounds__(W * 64) void q1_gemv_lut8_kernel(const uint32_t *__
 
     // First row of the wave's t-th unit.  The last unit of the matrix starts at row N - 8 when N
     // is not a multiple of 8 (its first rows repeat the unit before, and are written twice with
-    // the same value).  A unit past the wave's own stands for the wave's first unit (every
-    // iteration issues the same loads, so the waits the compiler places stay exact).
+    // the same value).  A unit slot past the wave's own units still issues every load (so the
+    // waits the compiler places stay exact) and is computed but not stored: its scales are the
+    // wave's first unit's, and its cells are read from x, which the cache holds (a lane offset
+    // is below K bytes, x spans 2K).
     auto unit_row0 = [&](int t) { return min(8 * (ub0 + wave + W * (t < nw ? t : 0)), N - 8); };
 
     // Unit (s, t) -- slice s, t-th unit: the lane's cell, at the unit's wave-uniform base plus the
     // lane's offset voff of the slice (the group clamped inside a short last slice).
     const char *ubase[UMAX];
 #pragma unroll
-    for (int t = 0; t < UMAX; ++t) ubase[t] = reinterpret_cast<const char *>(wbits) + 16 * (size_t)unit_row0(t) * G;
+    for (int t = 0; t < UMAX; ++t)
+        ubase[t] = t < nw ? reinterpret_cast<const char *>(wbits) + 16 * (size_t)unit_row0(t) * G
+                          : reinterpret_cast<const char *>(x);
     auto load_cell = [&](int t, uint32_t voff, u32x4 &cell) {
         cell = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(ubase[t] + voff));
     };
     auto lane_voff = [&](int s) { return 16u * (uint32_t)(r * G + 8 * s + min(p, G - 8 * s - 1)); };
     const char *xb = reinterpret_cast<const char *>(x);
-    const uint32_t xoff = 16u * (uint32_t)(lane % (K / 8));
 
     // Scales of slices s0 .. s0 + SQ - 1 of every unit of the wave: lane (r, p) takes that of
     // group 8 s + p of row r (clamped to the row's last group past K), two slices to a register.
@@ -212,8 +215,9 @@ __global__ __launch_bounds__(W * 64) void q1_gemv_lut8_kernel(const uint32_t *__
             src[4 * j + m] = (uint32_t)(4 * (4 * p + ((j + i) & 3)) + 128 * (i & 1)) | ((uint32_t)(i >> 1) << 16);
     }
 
-    // x to LDS (after the tables), the first SQ slices' scales paired, with the first PD units
-    // in flight, then the first slice's tables.  The loads go out in that order: x, scales, cells.
+    // x to LDS (after the tables) and the first slice's tables, with the first PD units and the
+    // first SQ slices' scales in flight (the loads go out in that order: x, cells, scales); the
+    // scales are paired once the tables are built.
     {
         constexpr int XR = (kL8MaxK / 8 + W * 64 - 1) / (W * 64);     // 16-byte pieces of x per thread
         const u32x4 *xg = reinterpret_cast<const u32x4 *>(x);
@@ -223,20 +227,20 @@ __global__ __launch_bounds__(W * 64) void q1_gemv_lut8_kernel(const uint32_t *__
             const int c = threadIdx.x + it * W * 64;
             if (c < K / 8) xr[it] = xg[c];
         }
-        load_scales(0, 0, UMAX, raw);
         const uint32_t voff = lane_voff(0);
 #pragma unroll
         for (int t = 0; t < PD; ++t) load_cell(t, voff, cell[t]);
+        load_scales(0, 0, UMAX, raw);
 #pragma unroll
         for (int it = 0; it < XR; ++it) {
             const int c = threadIdx.x + it * W * 64;
             if (c < K / 8) *reinterpret_cast<lds_u32x4_t *>(static_cast<uintptr_t>(kL8Tables + 16 * c)) = xr[it];
         }
-        pack_scales(0, UMAX, raw, sc);
     }
     __syncthreads();
     build(load_x(0));
     __syncthreads();
+    pack_scales(0, UMAX, raw, sc);
 
     float acc[UMAX];
 #pragma unroll
@@ -278,7 +282,7 @@ __global__ __launch_bounds__(W * 64) void q1_gemv_lut8_kernel(const uint32_t *__
                         load_cell(ta, voff, cell[b]);
                     } else {
                         const char *bp = last ? xb : ubase[ta - UMAX];
-                        cell[b] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(bp + (last ? xoff : voffn)));
+                        cell[b] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(bp + voffn));
                     }
                 });
                 if (!last) {
@@ -326,7 +330,7 @@ bool lut8_fits(int N, int K) { return N >= 8 && K <= kL8MaxK; }
 hipError_t launch_lut8(const uint32_t *wbits, const uint16_t *scales, const uint16_t *x, float *y, int N, int K,
                        hipStream_t stream)
 {
-    return launch_lut8_t<16, 4, 8, 5>(wbits, scales, x, y, N, K, stream);
+    return launch_lut8_t<16, 8, 8, 5>(wbits, scales, x, y, N, K, stream);
 }
 
 }  // namespace bonsai
