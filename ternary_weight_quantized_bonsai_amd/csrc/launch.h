@@ -23,6 +23,10 @@ hipError_t launch_gemv_mfma(bool ternary, const uint32_t *codes, const uint16_t 
 bool lut8_fits(int N, int K);
 hipError_t launch_lut8(const uint32_t *wbits, const uint16_t *scales, const uint16_t *x, float *y, int N, int K,
                        hipStream_t stream);
+// The same for affine 1-bit weights (scale and bias per group), K up to lut8a_fits.
+bool lut8a_fits(int N, int K);
+hipError_t launch_lut8a(const uint32_t *wbits, const uint16_t *scales, const uint16_t *biases, const uint16_t *x,
+                        float *y, int N, int K, hipStream_t stream);
 // Affine 1-bit weights at M = 1 on the table kernels, where their tables fit (q1a_lut_fits).
 bool q1a_lut_fits(int N, int K);
 hipError_t launch_q1a_lut(const uint32_t *wbits, const uint16_t *scales, const uint16_t *biases, const uint16_t *x,

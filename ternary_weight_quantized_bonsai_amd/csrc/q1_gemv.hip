@@ -602,10 +602,12 @@ bool q1a_lut_fits(int N, int K)
 hipError_t launch_q1a_lut(const uint32_t *wbits, const uint16_t *scales, const uint16_t *biases, const uint16_t *x,
                           float *y, int N, int K, hipStream_t stream)
 {
-    // as the binary route: 32-row tiles while one round of 256 CUs holds them, with two groups
-    // per lane where their waves fit, then 64-row tiles
+    // as the binary route: byte tables for many rows, 32-row tiles while one round of 256 CUs
+    // holds them, with two groups per lane where their waves fit, then 64-row tiles
     const int G = K / 128;
     const int cus = device_cus();
+    if ((int64_t)N >= 600LL * cus && G >= 16 && lut8a_fits(N, K))
+        return launch_lut8a(wbits, scales, biases, x, y, N, K, stream);
     const bool one_round32 = ((int64_t)N + 31) / 32 <= cus;
     using A2 = L4<32, true, 2>;
     if (one_round32 && (G + A2::gpw - 1) / A2::gpw <= A2::max_waves)

@@ -41,6 +41,7 @@ typedef __attribute__((address_space(3))) u32x4 lds_u32x4_t;
 constexpr int kL8SliceK = 1024;             // k per slice: 128 B of sign bits per row, 8 groups
 constexpr int kL8Tables = 128 * 1024;       // 128 tables of 256 fp32 entries
 constexpr int kL8MaxK = (160 * 1024 - kL8Tables) / 2;   // x (binary16) is staged after the tables
+constexpr int kL8MaxKAff = 16128;           // affine: and X of every group after x (2K + K/32 bytes)
 
 // LDS float at byte address a (the kernel's dynamic LDS starts at 0: it has no static LDS).
 __device__ __forceinline__ float lds_f32(uint32_t a)
@@ -87,9 +88,17 @@ __device__ __forceinline__ float sum8(float v)
 // W waves; PD units in flight per wave (their cells in registers); at most UMAX units per wave (a
 // multiple of PD, so a unit's registers are fixed at compile time; the launch gives every
 // workgroup at most W UMAX units); the scales of SQ slices of every unit in registers at a time.
-template <int W, int PD, int UMAX, int SQ>
+//
+// AFF: MLX's affine form ("prism-ml/Bonsai-27B-mlx-1bit", MLX packaging): weight a q + b for
+// the bit q, a scale a and a bias b (binary16, [N][K/128] each) per group.  With D the table sum
+// of +-x over a group and X its plain sum of x, the group adds (a/2) D + (a/2 + b) X.  X of every
+// group is summed once per workgroup into LDS after x; the second term does not depend on the
+// bits, so each round's biases are read like the scales and folded into the partial sums at
+// once, and only the scales stay in registers.
+template <int W, int PD, int UMAX, int SQ, bool AFF>
 __global__ __launch_bounds__(W * 64) void q1_gemv_lut8_kernel(const uint32_t *__restrict__ wbits,
                                                               const uint16_t *__restrict__ scales,
+                                                              const uint16_t *__restrict__ biases,
                                                               const uint16_t *__restrict__ x,
                                                               float *__restrict__ y, int N, int K)
 {
@@ -132,20 +141,20 @@ __global__ __launch_bounds__(W * 64) void q1_gemv_lut8_kernel(const uint32_t *__
     auto lane_voff = [&](int s) { return 16u * (uint32_t)(r * G + 8 * s + min(p, G - 8 * s - 1)); };
     const char *xb = reinterpret_cast<const char *>(x);
 
-    // Scales of slices s0 .. s0 + SQ - 1 of every unit of the wave: lane (r, p) takes that of
-    // group 8 s + p of row r (clamped to the row's last group past K), two slices to a register.
-    // A row's 80 bytes of scales (K = 5120) are read together rather than 16 bytes per slice, one
-    // slice's worth of the weights apart: between slices the cache would have to hold them while
-    // the weights stream.  load_scales issues the loads of units t0 .. t1 - 1, pack_scales pairs
-    // them once they are in.
+    // Scales (or biases: arr) of slices s0 .. s0 + SQ - 1 of every unit of the wave: lane (r, p)
+    // takes that of group 8 s + p of row r (clamped to the row's last group past K), two slices to
+    // a register.  A row's 80 bytes of scales (K = 5120) are read together rather than 16 bytes
+    // per slice, one slice's worth of the weights apart: between slices the cache would have to
+    // hold them while the weights stream.  load_scales issues the loads of units t0 .. t1 - 1,
+    // pack_scales pairs them once they are in.
     constexpr int SQ2 = (SQ + 1) / 2;
-    auto load_scales = [&](int s0, int t0, int t1, uint32_t (&raw)[UMAX][SQ]) {
+    auto load_scales = [&](const uint16_t *arr, int s0, int t0, int t1, uint32_t (&raw)[UMAX][SQ]) {
         uint32_t so[SQ];
 #pragma unroll
         for (int q = 0; q < SQ; ++q) so[q] = 2u * (uint32_t)(r * G + min(8 * (s0 + q) + p, G - 1));
 #pragma unroll
         for (int t = t0; t < t1; ++t) {
-            const char *sb = reinterpret_cast<const char *>(scales) + 2 * (size_t)unit_row0(t) * G;
+            const char *sb = reinterpret_cast<const char *>(arr) + 2 * (size_t)unit_row0(t) * G;
 #pragma unroll
             for (int q = 0; q < SQ; ++q) raw[t][q] = *reinterpret_cast<const uint16_t *>(sb + so[q]);
         }
@@ -155,7 +164,8 @@ __global__ __launch_bounds__(W * 64) void q1_gemv_lut8_kernel(const uint32_t *__
         for (int t = t0; t < t1; ++t)
 #pragma unroll
             for (int q2 = 0; q2 < SQ2; ++q2)
-                sc[t][q2] = 2 * q2 + 1 < SQ ? raw[t][2 * q2] | (raw[t][2 * q2 + 1] << 16) : raw[t][2 * q2];
+                sc[t][q2] = 2 * q2 + 1 < SQ ? __builtin_amdgcn_perm(raw[t][2 * q2 + 1], raw[t][2 * q2], 0x05040100u)
+                                            : raw[t][2 * q2];
     };
 
     // Tables of slice s: wave w writes entries EPW (w / 2) .. EPW (w / 2) + EPW - 1 of the 64
@@ -206,6 +216,28 @@ __global__ __launch_bounds__(W * 64) void q1_gemv_lut8_kernel(const uint32_t *__
     uint32_t sel[4], src[16];
     u32x4 cell[PD];
     uint32_t raw[UMAX][SQ], sc[UMAX][SQ2];
+    float acc[UMAX];
+#pragma unroll
+    for (int tt = 0; tt < UMAX; ++tt) acc[tt] = 0.f;
+    constexpr uint32_t kXsum = kL8Tables;                // + 2K: X of group g at + 4 g (AFF)
+    // AFF: add (a/2 + b) X of the lane's groups in slices s0 .. s0 + SQ - 1 (those inside K) to
+    // the partial sums of units t0 .. t1 - 1, from the paired scales and the biases in raw
+    auto add_bias_terms = [&](int s0, int t0, int t1, const uint32_t (&raw)[UMAX][SQ]) {
+#pragma unroll
+        for (int q = 0; q < SQ; ++q) {
+            const int g = 8 * (s0 + q) + p;             // past K: X = 0 (adds zeros)
+            const float xl = lds_f32(kXsum + 2 * K + 4 * min(g, G - 1));
+            const float xg = g < G ? xl : 0.f;
+#pragma unroll
+            for (int t = t0; t < t1; ++t) {
+                // a/2 + b as one mixed-precision FMA on the two halves (no fp32 copy of a
+                // that the compiler could keep for the slices)
+                const float c2 = fmaf(f16_bits_to_f32((uint16_t)(sc[t][q / 2] >> (16 * (q % 2)))), 0.5f,
+                                      f16_bits_to_f32((uint16_t)raw[t][q]));
+                acc[t] = fmaf(c2, xg, acc[t]);
+            }
+        }
+    };
 #pragma unroll
     for (int m = 0; m < 4; ++m) {
         const int i = (m + rq) & 3;
@@ -230,7 +262,7 @@ __global__ __launch_bounds__(W * 64) void q1_gemv_lut8_kernel(const uint32_t *__
         const uint32_t voff = lane_voff(0);
 #pragma unroll
         for (int t = 0; t < PD; ++t) load_cell(t, voff, cell[t]);
-        load_scales(0, 0, UMAX, raw);
+        load_scales(scales, 0, 0, UMAX, raw);
 #pragma unroll
         for (int it = 0; it < XR; ++it) {
             const int c = threadIdx.x + it * W * 64;
@@ -238,19 +270,39 @@ __global__ __launch_bounds__(W * 64) void q1_gemv_lut8_kernel(const uint32_t *__
         }
     }
     __syncthreads();
+    if constexpr (AFF) {
+        // X of group g: wave g mod W adds the group's 128 x, two per lane, then across the wave
+        // in a fixed butterfly; lane 0 writes it after x (read once the tables are built)
+        for (int g = wave; g < G; g += W) {
+            const half2_t pr = as_half2(*reinterpret_cast<const __attribute__((address_space(3))) uint32_t *>(
+                static_cast<uintptr_t>(kL8Tables + 256 * g + 4 * lane)));
+            float v = (float)pr[0] + (float)pr[1];
+#pragma unroll
+            for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off);
+            if (lane == 0) *reinterpret_cast<lds_f32_t *>(static_cast<uintptr_t>(kXsum + 2 * K + 4 * g)) = v;
+        }
+    }
     build(load_x(0));
     __syncthreads();
     pack_scales(0, UMAX, raw, sc);
-
-    float acc[UMAX];
-#pragma unroll
-    for (int tt = 0; tt < UMAX; ++tt) acc[tt] = 0.f;
+    if constexpr (AFF) {                                // the biases, once the scales are paired,
+        load_scales(biases, 0, 0, UMAX / 2, raw);       // half the units at a time
+        add_bias_terms(0, 0, UMAX / 2, raw);
+        load_scales(biases, 0, UMAX / 2, UMAX, raw);
+        add_bias_terms(0, UMAX / 2, UMAX, raw);
+    }
     for (int s0 = 0; s0 < S; s0 += SQ) {
-        if (s0 > 0) {                                   // K > 1024 SQ: the next SQ slices' scales,
-            load_scales(s0, 0, UMAX / 2, raw);          // half the units at a time
+        if (s0 > 0) {                                   // K > 1024 SQ: the next SQ slices' scales
+            load_scales(scales, s0, 0, UMAX / 2, raw);  // (and biases), half the units at a time
             pack_scales(0, UMAX / 2, raw, sc);
-            load_scales(s0, UMAX / 2, UMAX, raw);
+            load_scales(scales, s0, UMAX / 2, UMAX, raw);
             pack_scales(UMAX / 2, UMAX, raw, sc);
+            if constexpr (AFF) {
+                load_scales(biases, s0, 0, UMAX / 2, raw);
+                add_bias_terms(s0, 0, UMAX / 2, raw);
+                load_scales(biases, s0, UMAX / 2, UMAX, raw);
+                add_bias_terms(s0, UMAX / 2, UMAX, raw);
+            }
         }
         static_for<0, SQ>([&](auto qc) {
             constexpr int q = decltype(qc)::value;
@@ -260,9 +312,9 @@ __global__ __launch_bounds__(W * 64) void q1_gemv_lut8_kernel(const uint32_t *__
                 const bool live_group = 8 * s + p < G;  // groups past K (a short last slice) count 0
                 const uint32_t voff = lane_voff(s), voffn = lane_voff(last ? s : s + 1);
                 static_for<0, UMAX>([&](auto ic) {
-                    // Every unit slot is computed (a slot past the wave's units repeats its first
-                    // unit and is not stored), and every slot issues one load: with no branches
-                    // the compiler's waits count exactly PD - 1 loads still in flight.
+                    // Every unit slot is computed (a slot past the wave's units is not stored),
+                    // and every slot issues one load: with no branches the compiler's waits count
+                    // exactly PD - 1 loads still in flight.
                     constexpr int tt = decltype(ic)::value, b = tt % PD;
                     float tv[16];
 #pragma unroll
@@ -274,7 +326,10 @@ __global__ __launch_bounds__(W * 64) void q1_gemv_lut8_kernel(const uint32_t *__
                         (((tv[0] + tv[1]) + (tv[2] + tv[3])) + ((tv[4] + tv[5]) + (tv[6] + tv[7]))) +
                         (((tv[8] + tv[9]) + (tv[10] + tv[11])) + ((tv[12] + tv[13]) + (tv[14] + tv[15])));
                     const uint16_t sbits = (uint16_t)(sc[tt][q / 2] >> (16 * (q % 2)));
-                    acc[tt] = live_group ? fmaf(f16_bits_to_f32(sbits), part, acc[tt]) : acc[tt];
+                    // AFF: (a/2) D as a (D/2), halving being exact, so the fp16 scale still
+                    // feeds the mixed-precision FMA straight from its half of the register
+                    const float pv = AFF ? 0.5f * part : part;
+                    acc[tt] = live_group ? fmaf(f16_bits_to_f32(sbits), pv, acc[tt]) : acc[tt];
                     // the unit PD ahead into the registers just used; past the last slice a
                     // re-read of x, which the cache holds
                     constexpr int ta = tt + PD;
@@ -307,30 +362,37 @@ __global__ __launch_bounds__(W * 64) void q1_gemv_lut8_kernel(const uint32_t *__
     }
 }
 
-template <int W, int PD, int UMAX, int SQ>
-hipError_t launch_lut8_t(const uint32_t *wbits, const uint16_t *scales, const uint16_t *x, float *y, int N, int K,
-                         hipStream_t stream)
+template <int W, int PD, int UMAX, int SQ, bool AFF>
+hipError_t launch_lut8_t(const uint32_t *wbits, const uint16_t *scales, const uint16_t *biases, const uint16_t *x,
+                         float *y, int N, int K, hipStream_t stream)
 {
-    if (N < 8 || K > kL8MaxK) return hipErrorInvalidValue;
+    if (N < 8 || K > (AFF ? kL8MaxKAff : kL8MaxK)) return hipErrorInvalidValue;
     // one workgroup per CU, or more where a CU's share would exceed W UMAX units
     const int64_t U = ((int64_t)N + 7) / 8;
     const int64_t cus = device_cus();
     const int64_t grid = std::max(std::min(U, cus), (U + W * UMAX - 1) / (W * UMAX));
-    const void *fn = reinterpret_cast<const void *>(&q1_gemv_lut8_kernel<W, PD, UMAX, SQ>);
-    const size_t lds = (size_t)kL8Tables + 2 * (size_t)K;
+    const void *fn = reinterpret_cast<const void *>(&q1_gemv_lut8_kernel<W, PD, UMAX, SQ, AFF>);
+    const size_t lds = (size_t)kL8Tables + 2 * (size_t)K + (AFF ? 4 * (size_t)(K / 128) : 0);
     if (!set_lds_limit(fn, kLdsPerCu)) return hipErrorInvalidValue;
-    void *args[] = {&wbits, &scales, &x, &y, &N, &K};
+    void *args[] = {&wbits, &scales, &biases, &x, &y, &N, &K};
     return launch_kernel(fn, __PRETTY_FUNCTION__, dim3((unsigned)grid), dim3(64 * W), args, lds, stream);
 }
 
 }  // namespace
 
 bool lut8_fits(int N, int K) { return N >= 8 && K <= kL8MaxK; }
+bool lut8a_fits(int N, int K) { return N >= 8 && K <= kL8MaxKAff; }
 
 hipError_t launch_lut8(const uint32_t *wbits, const uint16_t *scales, const uint16_t *x, float *y, int N, int K,
                        hipStream_t stream)
 {
-    return launch_lut8_t<16, 8, 8, 5>(wbits, scales, x, y, N, K, stream);
+    return launch_lut8_t<16, 8, 8, 5, false>(wbits, scales, nullptr, x, y, N, K, stream);
+}
+
+hipError_t launch_lut8a(const uint32_t *wbits, const uint16_t *scales, const uint16_t *biases, const uint16_t *x,
+                        float *y, int N, int K, hipStream_t stream)
+{
+    return launch_lut8_t<16, 4, 8, 5, true>(wbits, scales, biases, x, y, N, K, stream);
 }
 
 }  // namespace bonsai

@@ -300,6 +300,11 @@ def test_plan_names_each_route_of_the_decode_gemv():
     assert _plan_kernel("q1_gemv", 1, 13824, 5120, 256) == "launch_lut4[ROWS = 64, AFF = false, GPL = 4]"
     assert _plan_kernel("q1_gemv", 1, 248320, 5120, 256).startswith("launch_lut8")
     assert _plan_kernel("q1_gemv", 1, 100003, 5120, 256) == "launch_lutp[AFF = false]"
+    # the affine form follows the same routes, on its own instances
+    assert _plan_kernel("q1a_matmul", 1, 248320, 5120, 256).startswith("launch_lut8_t")
+    assert "AFF = true" in _plan_kernel("q1a_matmul", 1, 248320, 5120, 256)
+    assert "AFF = false" in _plan_kernel("q1_gemv", 1, 248320, 5120, 256)
+    assert _plan_kernel("q1a_matmul", 1, 100003, 4992, 256) == "launch_lutp[AFF = true]"
     assert _plan_kernel("q1_gemv", 8, 5120, 5120, 256).startswith("launch_rt[TERN = false")
     assert _plan_kernel("q1_gemm", 512, 13824, 5120, 256) == "q1_gemm_kernel<false, 16>"
     assert _plan_kernel("q1_gemm", 512, 13824, 5248, 256) == "q1_gemm_kernel<false, 2>"

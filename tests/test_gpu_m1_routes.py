@@ -48,6 +48,8 @@ AFFINE_ROUTES = [
     ("launch_lut4[ROWS = 32", 5000, 5120),
     ("launch_lut4[ROWS = 64", 20000, 640),
     ("launch_lutp", 100003, 4992),
+    ("launch_lut8", 160001, 5120),
+    ("launch_lut8", 160003, 6272),
 ]
 
 
