@@ -59,6 +59,7 @@ KERNEL_SRC = {
     "q1_gemv_lut8_kernel": "ternary_weight_quantized_bonsai_amd/csrc/q1_lut8.hip",
     "q1_gemm_kernel": "ternary_weight_quantized_bonsai_amd/csrc/q1_gemm.hip",
     "gemv_mfma_kernel": "ternary_weight_quantized_bonsai_amd/csrc/gemv_mfma.hip",
+    "skinny_gemm_kernel": "ternary_weight_quantized_bonsai_amd/csrc/gemm_skinny.hip",
 }
 # rocprofv3 names of the kernels behind the launchers the library's plan names.
 KERNEL_OF_LAUNCHER = {
@@ -67,6 +68,7 @@ KERNEL_OF_LAUNCHER = {
     "launch_lut8_t": "q1_gemv_lut8_kernel",
     "launch_rt": "gemv_mfma_kernel",
     "t5_launch_rt": "t5_gemv_kernel",
+    "launch_skinny_t": "skinny_gemm_kernel",
 }
 
 
@@ -657,7 +659,7 @@ def main() -> int:
         w, s, _ = (up(a) for a in synth.make_q1(1, N4, K))
         R6 = max(3, math.ceil(ROTATE_BYTES / q1_bytes(N4, K)))
         ws, ss = copies(w, R6), copies(s, R6)
-        for M6 in (16, 64):
+        for M6 in (16, 32, 64, 128):
             x = up(synth.make_q1(M6, N4, K)[2])
             y = torch.empty((M6, N4), dtype=torch.float32, device=dev)
             bonsai.q1_gemm(ws[0], ss[0], x, out=y)

@@ -34,6 +34,11 @@ hipError_t launch_q1a_lut(const uint32_t *wbits, const uint16_t *scales, const u
 // Affine 1-bit weights (binary words with a binary16 scale and bias per group), any M >= 1.
 hipError_t launch_q1a_matmul(const uint32_t *wbits, const uint16_t *scales, const uint16_t *biases,
                              const uint16_t *x, float *y, int M, int N, int K, hipStream_t stream);
+// Binary (tern = false) or 2-bit ternary weights, 1 <= M <= skinny_max_m() rows of x: each weight
+// expanded once for all rows of x (gemm_skinny.hip).
+int skinny_max_m();
+hipError_t launch_skinny(bool tern, const uint32_t *codes, const uint16_t *scales, const uint16_t *x, float *y,
+                         int M, int N, int K, hipStream_t stream);
 // Base-3 ternary weights (five trits per byte, 32-byte superblocks of 160 k), any M >= 1.
 hipError_t launch_t5_matmul(const uint8_t *codes, const uint16_t *scales, const uint16_t *x, float *y,
                             int M, int N, int K, hipStream_t stream);

@@ -45,6 +45,7 @@
 #include <utility>
 
 #include "device.h"
+#include "expand.h"
 #include "launch.h"
 
 namespace bonsai {
@@ -73,38 +74,6 @@ __device__ __forceinline__ void wait_vmcnt()
 
 // sched_group_barrier masks
 constexpr int SG_MFMA = 0x008, SG_VALU = 0x002, SG_DS_READ = 0x100;
-
-// 8 halves (+-s) of the k16 slice s of one 64-k step: w is the word holding it, q selects
-// k 0..7 or 8..15 of the slice, cs = (-s, -s)
-__device__ __forceinline__ half8_t expand8(uint32_t w, int s, int q, uint32_t cs)
-{
-    const uint32_t hi = 0xFFFF0000u;
-    const uint32_t v = (s & 1) ? (((w >> 1) & hi) | (((w >> 16) | (w << 16)) & ~hi))
-                               : (((w << 15) & hi) | (w & ~hi));
-    const int p = 8 * q;
-    u32x4 e;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) e[i] = ((v << (15 - (p + 2 * i))) & 0x80008000u) ^ cs;
-    return __builtin_bit_cast(half8_t, e);
-}
-
-// Ternary: 8 halves of the k16 slice held by word w (16 codes, code j of k = j), k 8q .. 8q + 7,
-// times the scale.  Merging the word's half q with the same half shifted by one code puts codes
-// k and k + 1 16 bits apart, so one shift and one mask read a pair as binary16 (0 or +-2: code
-// 01 sets the top exponent bit, 11 also the sign); cs2 = (s, s) scales the pair exactly (2s is
-// finite for |s| < 32752), and the factor 2 comes off the fp32 sums.
-__device__ __forceinline__ half8_t expand8_tern(uint32_t w, int q, uint32_t cs2)
-{
-    const uint32_t lo = w >> (16 * q), hi = w >> (16 * q + 2);
-    const uint32_t v = (lo & 0xFFFFu) | (hi << 16);
-    u32x4 e;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const half2_t t = as_half2((v << (14 - 4 * i)) & 0xC000C000u);
-        e[i] = __builtin_bit_cast(uint32_t, t * as_half2(cs2));
-    }
-    return __builtin_bit_cast(half8_t, e);
-}
 
 // Scale copies of one chunk per column: binary SMODE 16, one 16-byte copy of the chunk's 8
 // scales (K % 1024 == 0), or SMODE 2, one 2-byte copy per group (low half of a dword); ternary
@@ -384,17 +353,19 @@ __global__ __launch_bounds__(256) void q1_gemm_kernel(const uint32_t *__restrict
 
 }  // namespace
 
-// Up to this many rows of x the small-M kernel (16 rows of x per pass over the weights) beats
-// the 128 x 256 tiles, which leave most CUs idle there (N = 13824 makes 54 tiles per 128 rows
-// of x).  Measured at N = 13824, K = 5120: 10 us against 51 us at M = 16, 35 against 51 at
-// M = 64; the two meet near M = 96 (binary) and 72 (ternary).
-constexpr int kSmallM = 80;
+// Up to 16 rows of x the small-M kernel (one pass of 16 rows of x over the weights) is the
+// fastest; from 17 to 128 rows the skinny GEMM (every weight expanded once for all rows of x,
+// gemm_skinny.hip), then the 128 x 256 tiles.  Measured at N = 13824, K = 5120 (binary;
+// ternary alike): M = 16: 10.6 us small-M, 11.9 skinny; M = 32: 18.6 / 12.2; M = 64: 33.9 /
+// 17.2; M = 128: 51.3 on the tiles (54 of them, most CUs idle), 28.0 skinny.
+constexpr int kSmallM = 16;
 
 hipError_t launch_q1_gemm(const uint32_t *wbits, const uint16_t *scales, const uint16_t *x, float *y,
                           int M, int N, int K, hipStream_t stream)
 {
     if (M == 1) return launch_q1_gemv(wbits, scales, x, y, M, N, K, stream);
     if (M <= kSmallM) return launch_gemv_mfma(false, wbits, scales, x, y, M, N, K, stream);
+    if (M <= skinny_max_m()) return launch_skinny(false, wbits, scales, x, y, M, N, K, stream);
     const int64_t tiles = (int64_t)((N + BN - 1) / BN) * ((M + BM - 1) / BM);
     if (tiles > INT_MAX || K % 128 != 0 || K <= 0) return hipErrorInvalidValue;
     void *args[] = {&wbits, &scales, &x, &y, &M, &N, &K};
@@ -411,6 +382,7 @@ hipError_t launch_q2t_gemm(const uint32_t *wcodes, const uint16_t *scales, const
                            int M, int N, int K, hipStream_t stream)
 {
     if (M <= kSmallM) return launch_gemv_mfma(true, wcodes, scales, x, y, M, N, K, stream);
+    if (M <= skinny_max_m()) return launch_skinny(true, wcodes, scales, x, y, M, N, K, stream);
     const int64_t tiles = (int64_t)((N + BN - 1) / BN) * ((M + BM - 1) / BM);
     if (tiles > INT_MAX || K % 128 != 0 || K <= 0) return hipErrorInvalidValue;
     void *args[] = {&wcodes, &scales, &x, &y, &M, &N, &K};

@@ -200,12 +200,15 @@ def test_affine_m1_route_poison_metamorphic_onehot(route, N, K, orc):
 
 
 # ---- the prefill tiles against the one-row kernels on the same weights and x ------------------
-@pytest.mark.parametrize("M,N,K", [(96, 1000, 2048), (512, 1000, 2048), (96, 1000, 1152), (200, 9000, 5120)])
-def test_prefill_tiles_match_one_row_kernels(M, N, K, orc):
-    """q1_gemm at M > 80 (the 128 x 256 matrix-core tiles) against q1_gemv at M = 1 (the table
-    kernels) on rows of the same x, each against the oracle and both against each other."""
+@pytest.mark.parametrize("M,N,K,gemm", [(96, 1000, 2048, "launch_skinny_t"), (512, 1000, 2048, "q1_gemm_kernel"),
+                                        (130, 1000, 1152, "q1_gemm_kernel"), (200, 9000, 5120, "q1_gemm_kernel"),
+                                        (33, 9000, 5120, "launch_skinny_t")])
+def test_prefill_tiles_match_one_row_kernels(M, N, K, gemm, orc):
+    """q1_gemm on the matrix cores (the 128 x 256 tiles past 128 rows of x, the skinny GEMM from 17
+    to 128) against q1_gemv at M = 1 (the table kernels) on rows of the same x, each against the
+    oracle and both against each other."""
     gemm_plan, gemv_plan = _plan("q1_gemm", M, N, K), _plan("q1_gemv", 1, N, K)
-    assert gemm_plan.startswith("q1_gemm_kernel") and gemv_plan.startswith("launch_lut"), (gemm_plan, gemv_plan)
+    assert gemm_plan.startswith(gemm) and gemv_plan.startswith("launch_lut"), (gemm_plan, gemv_plan)
     w, s, x = synth.make_q1(M, N, K, 61, f"cross/{N}x{K}")
     yg = call("q1_gemm", w, s, x)
     ms = [0, 1, M // 2, M - 1]

@@ -161,7 +161,8 @@ EDGE = {
                 (1, 3000, 7680), (1, 2999, 7552)],
     "q2t_gemv": [(1, 1, 128), (1, 63, 256), (2, 65, 384), (8, 1000, 1152), (7, 777, 2048),
                  (1, 130, 131072), (4, 4097, 640)],
-    # M <= 80 runs the small-M kernel in 16-row blocks of x (ragged last block), above it the tiles
+    # M <= 16 runs the small-M kernel (one 16-row block of x), 17 .. 128 the skinny GEMM (ragged
+    # blocks of 32 rows of x), above it the tiles
     "q1_gemm": [(1, 1, 128), (17, 100, 256), (130, 257, 384), (128, 128, 512), (256, 384, 1024),
                 (5, 3000, 640), (300, 70, 2048), (16, 40, 131072), (64, 300, 1152), (200, 520, 3200),
                 (33, 2000, 1024), (80, 777, 640), (81, 777, 640)],
@@ -185,7 +186,8 @@ def test_edge_shapes(kind, M, N, K, orc):
 # width that does not divide K / 128 leaves a partial last slice.  These shapes were chosen so that
 # the launcher's choices, as they stand, reach every such combination of each weight form (no
 # 64-row tile for the affine form).  Whatever the launcher picks, each case is checked against the
-# oracle on sampled rows.
+# oracle on sampled rows.  (From 17 rows of x the binary and ternary GEMM entry points take the
+# skinny GEMM instead, tested below; the affine form keeps the small-M kernel there.)
 SMALL_M_VARIANTS = sorted({(2, 33, 128), (2, 33, 256), (2, 5000, 128), (2, 5000, 256), (2, 13824, 128),
                            (2, 13824, 256), (2, 33, 1152), (16, 33, 5120), (2, 33, 1280), (2, 5000, 1152),
                            (2, 5000, 1280), (2, 13824, 1152), (2, 13824, 1280), (33, 1500, 5120),
@@ -214,6 +216,32 @@ def test_small_m_kernel_variants(form, M, N, K, orc):
     y = call(kind, w, s, x)
     yref, a = ref(kind, orc, w, s, x, n_idx=rows)
     assert_close(y[:, rows], yref, a, f"{kind} M={M} N={N} K={K}")
+
+
+# The skinny GEMM (17 to 128 rows of x through the GEMM entry points): one, two and four blocks of
+# 32 rows of x, ragged M and N, and K split over its four waves unevenly (K / 128 = 11: 2, 3, 3, 3
+# groups, which leave one or two groups after whole triples), with waves left idle (K / 128 = 1
+# and 3) and with a long K.  Random inputs against the oracle's tolerance, integer-valued inputs
+# bit for bit (every partial sum is exact in float32).
+SKINNY_SHAPES = [(17, 100, 128), (32, 64, 384), (33, 1000, 1408), (48, 777, 1152), (64, 2000, 5120),
+                 (65, 300, 640), (96, 129, 2560), (128, 128, 16384), (100, 65, 1280)]
+
+
+@pytest.mark.parametrize("kind", ["q1_gemm", "q2t_gemm"])
+@pytest.mark.parametrize("M,N,K", SKINNY_SHAPES)
+def test_skinny_gemm_shapes(kind, M, N, K, orc):
+    import ternary_weight_quantized_bonsai_amd as bonsai
+    assert bonsai.plan(kind, M, N, K).startswith("launch_skinny_t")
+    note(f"skinny {kind} M={M} N={N} K={K}")
+    rows = _sampled_rows(N, 94)
+    w, s, x = make(kind, M, N, K, 93, f"sk/{N}x{K}")
+    y = call(kind, w, s, x)
+    yref, a = ref(kind, orc, w, s, x, n_idx=rows)
+    assert_close(y[:, rows], yref, a, f"skinny {kind} {M}x{N}x{K}")
+    wi, si, xi = integer_inputs(kind, M, N, K, 95)
+    yi = call(kind, wi, si, xi)
+    ye = exact(kind, orc, wi, si, xi, n_idx=rows).astype(np.float32)
+    assert np.array_equal(yi[:, rows], ye), f"skinny {kind} {M}x{N}x{K} integer inputs"
 
 
 @pytest.mark.parametrize("kind", KINDS)
