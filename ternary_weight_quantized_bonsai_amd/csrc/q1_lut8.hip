@@ -247,9 +247,10 @@ __global__ __launch_bounds__(W * 64) void q1_gemv_lut8_kernel(const uint32_t *__
             src[4 * j + m] = (uint32_t)(4 * (4 * p + ((j + i) & 3)) + 128 * (i & 1)) | ((uint32_t)(i >> 1) << 16);
     }
 
-    // x to LDS (after the tables) and the first slice's tables, with the first PD units and the
-    // first SQ slices' scales in flight (the loads go out in that order: x, cells, scales); the
-    // scales are paired once the tables are built.
+    // x to LDS (after the tables) and the first slice's tables, with the first SQ slices' scales
+    // and the first PD units in flight (the loads go out in that order: x, scales, cells, so the
+    // first lookups need not wait for every cell of the first slice; 0.3 us less than cells
+    // first); the scales are paired once the tables are built.
     {
         constexpr int XR = (kL8MaxK / 8 + W * 64 - 1) / (W * 64);     // 16-byte pieces of x per thread
         const u32x4 *xg = reinterpret_cast<const u32x4 *>(x);
@@ -259,10 +260,10 @@ __global__ __launch_bounds__(W * 64) void q1_gemv_lut8_kernel(const uint32_t *__
             const int c = threadIdx.x + it * W * 64;
             if (c < K / 8) xr[it] = xg[c];
         }
+        load_scales(scales, 0, 0, UMAX, raw);
         const uint32_t voff = lane_voff(0);
 #pragma unroll
         for (int t = 0; t < PD; ++t) load_cell(t, voff, cell[t]);
-        load_scales(scales, 0, 0, UMAX, raw);
 #pragma unroll
         for (int it = 0; it < XR; ++it) {
             const int c = threadIdx.x + it * W * 64;
