@@ -596,6 +596,11 @@ def test_graph_capture_and_replay_of_every_entry_point(orc):
     calls.append(("q1_gemv M=5", bonsai.q1_gemv, (to_dev(w), to_dev(s), to_dev(x)), orc.q1_matmul(w, s, x, 1024)))
     w, s, x = synth.make_q1(130, 300, 768, 83, "graph/gemm")
     calls.append(("q1_gemm M=130", bonsai.q1_gemm, (to_dev(w), to_dev(s), to_dev(x)), orc.q1_matmul(w, s, x, 768)))
+    w, s, x = synth.make_q1(40, 700, 1408, 88, "graph/skinny")             # the skinny GEMM
+    calls.append(("q1_gemm M=40", bonsai.q1_gemm, (to_dev(w), to_dev(s), to_dev(x)), orc.q1_matmul(w, s, x, 1408)))
+    w, s, x = synth.make_q1(1, 160001, 2048, 89, "graph/lut8")             # the byte tables
+    calls.append(("q1_gemv M=1 N=160001", bonsai.q1_gemv, (to_dev(w), to_dev(s), to_dev(x)),
+                  orc.q1_matmul(w, s, x, 2048)))
     w, s, x = synth.make_q2t(3, 500, 640, 84, "graph/q2t")
     calls.append(("q2t_gemv M=3", bonsai.q2t_gemv, (to_dev(w), to_dev(s), to_dev(x)), orc.q2t_matmul(w, s, x, 640)))
     w, s, x = synth.make_q2t(100, 300, 640, 85, "graph/q2tg")
@@ -606,6 +611,9 @@ def test_graph_capture_and_replay_of_every_entry_point(orc):
     w, a, b, x = synth.make_q1a(4, 300, 640, 87, "graph/q1a")
     calls.append(("q1a_matmul M=4", bonsai.q1a_matmul, (to_dev(w), to_dev(a), to_dev(b), to_dev(x)),
                   (orc.q1a_matmul(w, a, b, x, 640)[0], _affine_magnitude(orc, w, a, b, x))))
+    w, a, b, x = synth.make_q1a(1, 160001, 2048, 90, "graph/lut8a")       # the affine byte tables
+    calls.append(("q1a_matmul M=1 N=160001", bonsai.q1a_matmul, (to_dev(w), to_dev(a), to_dev(b), to_dev(x)),
+                  (orc.q1a_matmul(w, a, b, x, 2048)[0], _affine_magnitude(orc, w, a, b, x))))
     outs = [torch.empty((args[-1].shape[0], args[0].shape[0]), dtype=torch.float32, device=dev)
             for _, _, args, _ in calls]
     note("graph: eager reference run")
@@ -714,6 +722,11 @@ def test_concurrent_calls_from_threads_on_their_own_streams():
     w, a, b, x = synth.make_q1a(1, 9000, 1024, 3, "thr6")
     cases.append(("q1a_matmul M=1", lambda o, w=d(w), a=d(a), b=d(b), x=d(x):
                   bonsai.q1a_matmul(w, a, b, x, out=o), (1, 9000)))
+    w, s, x = synth.make_q2t(48, 3000, 2048, 3, "thr7")                    # the skinny GEMM
+    cases.append(("q2t_gemm M=48", lambda o, w=d(w), s=d(s), x=d(x): bonsai.q2t_gemm(w, s, x, out=o), (48, 3000)))
+    w, s, x = synth.make_q1(1, 160001, 2048, 3, "thr8")                     # the byte tables
+    cases.append(("q1_gemv M=1 N=160001", lambda o, w=d(w), s=d(s), x=d(x): bonsai.q1_gemv(w, s, x, out=o),
+                  (1, 160001)))
     torch.cuda.synchronize()
 
     expected = []
