@@ -23,6 +23,11 @@
 // there.  The copies are ordered against those reads by waits on the copies themselves, with
 // exact counts, since each wave reads only what it copied.
 //
+// Pipeline.  The A fragments of the next k16 slice are read from LDS and its B fragments
+// expanded while the current slice's MFMAs run (one wave per SIMD: nothing else would hide the
+// LDS latency); the last slice of a stage waits for the next stage's copies and fetches its
+// first operands.
+//
 // Bound.  The MFMA work is 2 M N K flops; each workgroup also reads all of x (2 M K bytes) from
 // the cache.  At M = 64, N = 13824, K = 5120: 9.1 GFLOP and 216 workgroups of 640 KB of x.
 #include <algorithm>
@@ -43,6 +48,8 @@ struct IC {
 
 constexpr int kSkRows = 64;                 // weight rows per workgroup
 constexpr int kSkWaves = 4;
+// sched_group_barrier masks
+constexpr int SG_MFMA = 0x008, SG_VALU = 0x002, SG_DS_READ = 0x100;
 
 // MB: blocks of 32 rows of x (M <= 32 MB).  NB: stages of x (64 k each) in a wave's ring.
 template <bool TERN, int MB, int NB>
@@ -129,54 +136,94 @@ __global__ __launch_bounds__(kSkWaves * 64) void skinny_gemm_kernel(const uint32
             copy_group(g0 + (NB == 2 ? 2 : hh + 1), NB == 2 ? 2 : hh + 1);
         }
 
-        // Group g of the wave in group slot r: the arithmetic of its two stages, the copies of
-        // the stages NB ahead, and the group three ahead into the slot.  Every group issues the
-        // same copies in the same order (past the wave's range they are clamped repeats), so one
-        // wait count holds for every stage: a stage's copies have landed once at most the
-        // copies issued after them are outstanding (NB - 1 stages and NB / 2 groups).  The
-        // group's own codes and scales were copied before the first stage's.
+        // Operands of one k16 slice: buffer c holds the current slice's, c ^ 1 the next one's,
+        // fetched and expanded under the current slice's MFMAs.
+        half8_t af[2][MB], bf[2][2];
+        u32x4 cw[2][CW / 4];                            // code words of the group being expanded
+        uint32_t cs[2];                                 // its scale pairs
+        auto read_codes = [&](int r) {
+            const uint32_t gslot = gring + (uint32_t)(r * GSLOT);
+            const uint32_t flip = TERN ? 0u : 0x80008000u;     // binary (-s, -s), ternary (s, s)
+#pragma unroll
+            for (int t = 0; t < 2; ++t) {
+                const int row = 32 * t + l32;
+#pragma unroll
+                for (int hh = 0; hh < CW / 4; ++hh)
+                    cw[t][hh] = *reinterpret_cast<const lds_u32x4_t *>((uintptr_t)(gslot + 1024 * hh + 16 * row));
+                const uint32_t sv = *reinterpret_cast<const lds_u16_t *>((uintptr_t)(gslot + GCODES + 4 * row));
+                cs[t] = (sv | (sv << 16)) ^ flip;
+            }
+        };
+        // A of slice jj (0..3) of stage st, B of slice j (0..7) of the group whose codes are in cw
+        auto read_a = [&](int buf, int st, int jj) {
+            const uint32_t slot = ring + (uint32_t)((st % NB) * STAGE);
+#pragma unroll
+            for (int mb = 0; mb < MB; ++mb) {
+                const int m = 32 * mb + l32;
+                af[buf][mb] = *reinterpret_cast<const lds_half8_t *>(
+                    (uintptr_t)(slot + 128 * m + 16 * ((2 * jj + q) ^ (m & 7))));
+            }
+        };
+        auto make_b = [&](int buf, int j) {
+#pragma unroll
+            for (int t = 0; t < 2; ++t) {
+                if constexpr (TERN) bf[buf][t] = expand8_tern(cw[t][j >> 2][j & 3], q, cs[t]);
+                else bf[buf][t] = expand8(cw[t][0][j >> 1], j, q, cs[t]);
+            }
+        };
+        auto mfma = [&](int buf) {
+#pragma unroll
+            for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+                for (int t = 0; t < 2; ++t)
+                    acc[mb][t] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[buf][mb], bf[buf][t], acc[mb][t], 0, 0, 0);
+        };
+
+        // Every group issues the same copies in the same order (past the wave's range they are
+        // clamped repeats): after stage s's copies come those of the later stages, and a group's
+        // copies after each odd stage (a group's second).  Stage 0 has landed once at most the
+        // copies issued after it in the prologue are outstanding.
+        vm_wait<(NB - 1) * 4 * MB + (NB / 2) * GC>();
+        read_codes(0);
+        read_a(0, 0, 0);
+        make_b(0, 0);
+
+        // Group g of the wave in group slot r.  The last slice of stage st fetches the first
+        // operands of stage st + 1 (and, at the group's end, the next group's codes, which were
+        // copied before that stage): it waits until at most the copies issued after stage st + 1
+        // are outstanding -- the stages up to st + NB - 1 and a group's copies after each odd one
+        // of them -- then issues the copies of stage st + NB into the slot stage st used.
         auto do_group = [&](auto rc, int g) {
             constexpr int r = decltype(rc)::value;
-            const uint32_t gslot = gring + (uint32_t)(r * GSLOT);
-            u32x4 cw[2][CW / 4];
-            uint32_t cs[2];
 #pragma unroll
             for (int h = 0; h < 2; ++h) {
                 const int st = 2 * (g - g0) + h;
-                vm_wait<(NB - 1) * 4 * MB + (NB / 2) * GC>();
-                if (h == 0) {
-                    const uint32_t flip = TERN ? 0u : 0x80008000u;     // binary (-s, -s), ternary (s, s)
-#pragma unroll
-                    for (int t = 0; t < 2; ++t) {
-                        const int row = 32 * t + l32;
-#pragma unroll
-                        for (int hh = 0; hh < CW / 4; ++hh)
-                            cw[t][hh] = *reinterpret_cast<const lds_u32x4_t *>((uintptr_t)(gslot + 1024 * hh + 16 * row));
-                        const uint32_t sv = *reinterpret_cast<const lds_u16_t *>((uintptr_t)(gslot + GCODES + 4 * row));
-                        cs[t] = (sv | (sv << 16)) ^ flip;
-                    }
-                }
-                const uint32_t slot = ring + (uint32_t)((st % NB) * STAGE);
 #pragma unroll
                 for (int jj = 0; jj < 4; ++jj) {
-                    const int j = 4 * h + jj;                   // slice of the group
-                    half8_t bf[2], af[MB];
-#pragma unroll
-                    for (int t = 0; t < 2; ++t) {
-                        if constexpr (TERN) bf[t] = expand8_tern(cw[t][j >> 2][j & 3], q, cs[t]);
-                        else bf[t] = expand8(cw[t][0][j >> 1], j, q, cs[t]);
+                    const int cur = jj & 1, nxt = cur ^ 1;
+                    if (jj < 3) {
+                        read_a(nxt, st, jj + 1);
+                        make_b(nxt, 4 * h + jj + 1);
+                    } else {
+                        // st has the parity of h: NB / 2 - h odd stages among st + 1 .. st + NB - 1
+                        if (h == 0) vm_wait<(NB - 2) * 4 * MB + (NB / 2) * GC>();
+                        else vm_wait<(NB - 2) * 4 * MB + (NB / 2 - 1) * GC>();
+                        read_a(nxt, st + 1, 0);
+                        if (h == 0) {
+                            make_b(nxt, 4);
+                        } else {
+                            read_codes((r + 1) % 3);
+                            make_b(nxt, 0);
+                        }
                     }
+                    mfma(cur);
 #pragma unroll
-                    for (int mb = 0; mb < MB; ++mb) {
-                        const int m = 32 * mb + l32;
-                        af[mb] = *reinterpret_cast<const lds_half8_t *>(
-                            (uintptr_t)(slot + 128 * m + 16 * ((2 * jj + q) ^ (m & 7))));
+                    for (int i = 0; i < 2 * MB; ++i) {
+                        __builtin_amdgcn_sched_group_barrier(SG_MFMA, 1, 0);
+                        if (i < MB) __builtin_amdgcn_sched_group_barrier(SG_DS_READ, 1, 0);
+                        __builtin_amdgcn_sched_group_barrier(SG_VALU, 24 / (2 * MB), 0);
                     }
-#pragma unroll
-                    for (int mb = 0; mb < MB; ++mb)
-#pragma unroll
-                        for (int t = 0; t < 2; ++t)
-                            acc[mb][t] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[mb], bf[t], acc[mb][t], 0, 0, 0);
+                    __builtin_amdgcn_sched_barrier(0);
                 }
                 copy_stage(st + NB);
             }
