@@ -391,9 +391,9 @@ inline int sm_simd_groups(int nw, int ns, int sg)
 }
 
 // The row tile (16, 32 or 64 rows) for slices of SG groups: the one whose grid needs the fewest
-// rounds of the chip's 256 CUs, given what the LDS and the registers of a CU hold; among those,
-// the one that leaves the busiest CU the fewest weight rows (workgroups per CU, rounded up,
-// times the tile), then the larger tile (its x copies and reduction serve more rows).
+// rounds of the device's CUs (256 on MI355X), given what the LDS and the registers of a CU hold;
+// among those, the one that leaves the busiest CU the fewest weight rows (workgroups per CU,
+// rounded up, times the tile), then the larger tile (its x copies and reduction serve more rows).
 template <bool TERN, bool AFF, int SG>
 SmChoice<TERN, AFF, SG> sm_choose(int M, int N, int K)
 {

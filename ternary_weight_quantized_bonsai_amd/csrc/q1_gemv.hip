@@ -602,7 +602,7 @@ bool q1a_lut_fits(int N, int K)
 hipError_t launch_q1a_lut(const uint32_t *wbits, const uint16_t *scales, const uint16_t *biases, const uint16_t *x,
                           float *y, int N, int K, hipStream_t stream)
 {
-    // as the binary route: byte tables for many rows, 32-row tiles while one round of 256 CUs
+    // as the binary route: byte tables for many rows, 32-row tiles while one round of the CUs
     // holds them, with two groups per lane where their waves fit, then 64-row tiles
     const int G = K / 128;
     const int cus = device_cus();
@@ -634,7 +634,7 @@ hipError_t launch_q1_gemv(const uint32_t *wbits, const uint16_t *scales, const u
     if (M >= 2 && M <= 8) return launch_gemv_mfma(false, wbits, scales, x, y, M, N, K, stream);
     if (M != 1) return hipErrorInvalidValue;
     // The route follows measurements at K = 5120 (N = 1024 ... 248320) and K = 13824:
-    // - 32-row tiles while one round of 256 CUs holds them (twice the CUs of 64-row tiles), with
+    // - 32-row tiles while one round of the CUs holds them (twice the CUs of 64-row tiles), with
     //   two groups per lane where the waves fit (10 waves instead of 5 at K = 5120, 5120 x 5120:
     //   4.4 us instead of 5.3);
     // - 64-row tiles (one workgroup per CU, about 5 us a round) up to six rounds;

@@ -289,12 +289,12 @@ hipError_t t5_launch_rt(const uint8_t *codes, const uint16_t *scales, const uint
 
 }  // namespace
 
-// Any M >= 1 (16 rows of x per column block).  Three builds: 16-row tiles (up to 16 waves),
-// 32-row tiles with up to 8 waves (163 VGPRs), 32-row tiles with up to 16 waves (held to 128
-// VGPRs, two workgroups per CU).  The launch takes the build whose grid needs the fewest rounds
-// of the chip's 256 CUs, given what the LDS and the registers of a CU hold; on a tie, in the
-// order that measured fastest: for one row of x the 16-row tile first (more workgroups in
-// flight), for more rows the 8-wave 32-row build first (x, held once per wave, fills the LDS).
+// Any M >= 1 (16 rows of x per column block).  Three builds: 16-row tiles (up to 16 waves), 32-row
+// tiles with up to 8 waves (163 VGPRs), 32-row tiles with up to 16 waves (held to 128 VGPRs, two
+// workgroups per CU).  The launch takes the build whose grid needs the fewest rounds of the
+// device's CUs (256 on MI355X), given what the LDS and the registers of a CU hold; on a tie, in the
+// order that measured fastest: for one row of x the 16-row tile first (more workgroups in flight),
+// for more rows the 8-wave 32-row build first (x, held once per wave, fills the LDS).
 hipError_t launch_t5_matmul(const uint8_t *codes, const uint16_t *scales, const uint16_t *x, float *y,
                             int M, int N, int K, hipStream_t stream)
 {
