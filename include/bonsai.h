@@ -78,7 +78,10 @@ bonsai_status bonsai_q1_gemv(const uint32_t *wbits, const uint16_t *scales, cons
 bonsai_status bonsai_q1_gemm(const uint32_t *wbits, const uint16_t *scales, const uint16_t *x,
                              float *y, int64_t M, int64_t N, int64_t K, void *hip_stream);
 
-/* Ternary decode GEMV on 2-bit codes: y[M][N] = x[M][K] * W^T for 1 <= M <= 8. */
+/* Ternary decode GEMV on 2-bit codes: y[M][N] = x[M][K] * W^T for 1 <= M <= 8 (M == 0: no-op).
+ * The weights are {-1, 0, +1} times the FP16 group scale, stored in 2 bits each in the current
+ * release ("Ternary Bonsai 27B" article, ternary format and limitations sections); decode
+ * streams them once, as for the binary weights.  Otherwise as bonsai_q1_gemv. */
 bonsai_status bonsai_q2t_gemv(const uint32_t *wcodes, const uint16_t *scales, const uint16_t *x,
                               float *y, int64_t M, int64_t N, int64_t K, void *hip_stream);
 
@@ -148,6 +151,9 @@ bonsai_status bonsai_q1_from_affine(const uint16_t *mlx_scales, const uint16_t *
                                     uint16_t *scales);
 
 /* Host-side executable layout spec: pure functions on host memory, no device, no allocation.
+ * They fix the bit order and code values given above: one sign bit per weight, bit 1 -> +s
+ * (model card, "Weight representation: Binary g128"), and the ternary weights in two bits
+ * ("Ternary Bonsai 27B" article, ternary format).
  * signs/trits are int8 [N][K] row-major; K must be a multiple of 32 (binary) or 16 (ternary).
  * pack rejects values outside the alphabet with BONSAI_ERR_VALUE (output then unspecified);
  * unpack of ternary rejects field value 2 with BONSAI_ERR_CODE. */
